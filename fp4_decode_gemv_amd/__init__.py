@@ -1,0 +1,274 @@
+"""Python binding of the gfx950 NVFP4 small-M decode-projection library.
+
+A thin ctypes layer over ``lib/libnvfp4.so`` (the C ABI in
+``include/nvfp4.h``).  It only marshals arguments: torch tensors supply
+device memory (``data_ptr()``) and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or fails to load, every call raises.
+
+Functions keep the C names:
+
+* ``nvfp4_pack_weights(w)`` -> ``(codes, scales, gscale)``
+* ``nvfp4_quantize_act(x_bf16, gscale=None)`` -> ``(codes, scales, gscale)``
+* ``nvfp4_gemv_smallm(a, w, ...)`` -> ``y`` (optionally with the LM-head
+  epilogue)
+* ``nvfp4_workspace_size``, ``nvfp4_workspace_init``,
+  ``nvfp4_reset_state_size``, ``nvfp4_reset_state_init``,
+  ``nvfp4_status_str``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libnvfp4.so")
+
+NVFP4_OK = 0
+NVFP4_ERR_NULL = -1
+NVFP4_ERR_SHAPE = -2
+NVFP4_ERR_ALIGN = -3
+NVFP4_ERR_WORKSPACE = -4
+NVFP4_ERR_DEVICE = -5
+NVFP4_ERR_HIP = -6
+NVFP4_ERR_ARG = -7
+
+NVFP4_GS_DYNAMIC = 0
+NVFP4_GS_STATIC = 1
+
+NVFP4_OP_PACK = 0
+NVFP4_OP_QUANT = 1
+NVFP4_OP_GEMV = 2
+NVFP4_OP_GEMV_LMHEAD = 3
+
+EXPORTED = (
+    "nvfp4_status_str",
+    "nvfp4_workspace_size",
+    "nvfp4_workspace_init",
+    "nvfp4_pack_weights",
+    "nvfp4_quantize_act",
+    "nvfp4_reset_state_size",
+    "nvfp4_reset_state_init",
+    "nvfp4_gemv_smallm",
+)
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+class LmheadEpilogue(ctypes.Structure):
+    """Mirror of ``nvfp4_lmhead_epilogue_t``."""
+
+    _fields_ = [
+        ("tau0", ctypes.c_float),
+        ("t_low", ctypes.c_float),
+        ("t_high", ctypes.c_float),
+        ("t_base", ctypes.c_float),
+        ("window", ctypes.c_int),
+        ("mode", ctypes.c_int),
+        ("step_start", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("entropy", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"HIP library not built ({LIB_PATH} missing); run `python -c 'import __graft_entry__ as g; g.build()'`"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    c_int = ctypes.c_int
+    L.nvfp4_status_str.restype = ctypes.c_char_p
+    L.nvfp4_status_str.argtypes = [c_int]
+    L.nvfp4_workspace_size.restype = sz
+    L.nvfp4_workspace_size.argtypes = [c_int, c_int, i64, i64]
+    L.nvfp4_workspace_init.restype = c_int
+    L.nvfp4_workspace_init.argtypes = [vp, sz, vp]
+    L.nvfp4_pack_weights.restype = c_int
+    L.nvfp4_pack_weights.argtypes = [vp, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.nvfp4_quantize_act.restype = c_int
+    L.nvfp4_quantize_act.argtypes = [vp, c_int, i64, vp, vp, vp, c_int, vp, sz, vp]
+    L.nvfp4_reset_state_size.restype = sz
+    L.nvfp4_reset_state_size.argtypes = [c_int]
+    L.nvfp4_reset_state_init.restype = c_int
+    L.nvfp4_reset_state_init.argtypes = [vp, c_int, c_int, vp]
+    L.nvfp4_gemv_smallm.restype = c_int
+    L.nvfp4_gemv_smallm.argtypes = [c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.POINTER(LmheadEpilogue), vp, sz, vp]
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().nvfp4_status_str(int(status)).decode()
+
+
+nvfp4_status_str = status_str
+
+
+def _check(status: int, where: str) -> None:
+    if status != NVFP4_OK:
+        raise Nvfp4Error(status, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int | None:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) or None
+
+
+@dataclass
+class NvFp4Tensor:
+    """An NVFP4 matrix on the device: codes [rows][K/2], E4M3 scales
+    [rows][K/16], global scale [1] (all torch tensors)."""
+
+    codes: "object"
+    scales: "object"
+    gscale: "object"
+
+    @property
+    def rows(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def K(self) -> int:
+        return int(self.codes.shape[1]) * 2
+
+
+def nvfp4_workspace_size(op: int, M: int, N: int, K: int) -> int:
+    return int(lib().nvfp4_workspace_size(op, M, N, K))
+
+
+def nvfp4_workspace_init(ws, stream=None) -> None:
+    _check(lib().nvfp4_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "nvfp4_workspace_init")
+
+
+def new_workspace(nbytes: int, device="cuda", stream=None):
+    """A zero-filled workspace tensor of at least nbytes (16-byte multiple)."""
+    import torch
+
+    n = max(16, (int(nbytes) + 15) // 16 * 16)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    nvfp4_workspace_init(ws, stream)
+    return ws
+
+
+def nvfp4_pack_weights(w, ws=None, out: NvFp4Tensor | None = None, stream=None) -> NvFp4Tensor:
+    """Pack W fp32 [N][K] (device, contiguous) into NVFP4."""
+    import torch
+
+    N, K = int(w.shape[0]), int(w.shape[1])
+    if out is None:
+        out = NvFp4Tensor(torch.empty((N, K // 2), dtype=torch.uint8, device=w.device),
+                          torch.empty((N, K // 16), dtype=torch.uint8, device=w.device),
+                          torch.empty(1, dtype=torch.float32, device=w.device))
+    need = nvfp4_workspace_size(NVFP4_OP_PACK, 0, N, K)
+    if ws is None:
+        ws = new_workspace(need, w.device, stream)
+    _check(lib().nvfp4_pack_weights(_ptr(w), N, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "nvfp4_pack_weights")
+    return out
+
+
+def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, stream=None) -> NvFp4Tensor:
+    """Quantize x bf16 [M][K] (device, contiguous).  ``gscale=None``: dynamic
+    global scale (written into out.gscale); else a device fp32 [1] tensor
+    holding a static scale (used as out.gscale)."""
+    import torch
+
+    M, K = int(x.shape[0]), int(x.shape[1])
+    flags = NVFP4_GS_DYNAMIC if gscale is None else NVFP4_GS_STATIC
+    if out is None:
+        out = NvFp4Tensor(torch.empty((M, K // 2), dtype=torch.uint8, device=x.device),
+                          torch.empty((M, K // 16), dtype=torch.uint8, device=x.device),
+                          gscale if gscale is not None else torch.empty(1, dtype=torch.float32, device=x.device))
+    need = nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K)
+    if need and ws is None:
+        ws = new_workspace(need, x.device, stream)
+    _check(lib().nvfp4_quantize_act(_ptr(x), M, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
+                                    flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
+           "nvfp4_quantize_act")
+    return out
+
+
+def nvfp4_reset_state_size(window: int) -> int:
+    return int(lib().nvfp4_reset_state_size(window))
+
+
+def nvfp4_reset_state_init(state, M: int, window: int, stream=None) -> None:
+    _check(lib().nvfp4_reset_state_init(_ptr(state), M, window, _stream(stream)), "nvfp4_reset_state_init")
+
+
+def new_reset_state(M: int, window: int, device="cuda", stream=None):
+    import torch
+
+    st = torch.empty(M * nvfp4_reset_state_size(window), dtype=torch.uint8, device=device)
+    nvfp4_reset_state_init(st, M, window, stream)
+    return st
+
+
+@dataclass
+class Epilogue:
+    """Host description of the LM-head epilogue (device tensors inside)."""
+
+    step_start: "object"     # uint8 [M]
+    state: "object"          # uint8 [M * state_size]
+    entropy: "object"        # fp32 [M]
+    temperature: "object"    # fp32 [M]
+    tau0: float = 0.6
+    t_low: float = 0.4
+    t_high: float = 1.0
+    t_base: float = 0.6
+    window: int = 8
+    mode: int = 0
+
+    def as_c(self) -> LmheadEpilogue:
+        return LmheadEpilogue(self.tau0, self.t_low, self.t_high, self.t_base, self.window, self.mode,
+                              _ptr(self.step_start), _ptr(self.state), _ptr(self.entropy),
+                              _ptr(self.temperature))
+
+
+def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | None = None, ws=None,
+                      M: int | None = None, stream=None):
+    """y [M][N] fp32 = dequant(a) . dequant(w)^T."""
+    import torch
+
+    M = a.rows if M is None else M
+    N, K = w.rows, w.K
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=w.codes.device)
+    ce = None
+    ws_bytes = 0
+    if epi is not None:
+        ce = epi.as_c()
+        need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD, M, N, K)
+        if ws is None:
+            ws = new_workspace(need, w.codes.device, stream)
+        ws_bytes = ws.numel()
+    _check(lib().nvfp4_gemv_smallm(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale),
+                                   _ptr(w.codes), _ptr(w.scales), _ptr(w.gscale), _ptr(y),
+                                   None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,
+                                   _stream(stream)), "nvfp4_gemv_smallm")
+    return y

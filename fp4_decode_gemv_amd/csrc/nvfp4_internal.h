@@ -1,0 +1,73 @@
+// Host-side declarations shared by the C-ABI layer and the kernel translation
+// units.  No device code and no torch types here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------- quantize --
+
+// How the global scale of a quantization is obtained.
+enum GsMode : int {
+  GS_FROM_PARTIALS = 0,  // reduce per-workgroup amax partials written by amax_partials
+  GS_STATIC = 1,         // read *gscale
+  GS_SELF = 2            // every workgroup reduces the whole (small) tensor itself
+};
+
+// Number of amax partials the two-launch path uses for `elems` elements.
+int amax_partial_count(int64_t elems);
+
+// Activation quantization is done in one launch (GS_SELF) up to this many
+// elements, in two launches (amax partials, then quantize) above it.
+constexpr int64_t kActSelfAmaxMaxElems = 32768;
+
+// Launchers (no validation: the C-ABI layer has done it).
+hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                                uint8_t* scales, float* gscale, GsMode mode, float* partials,
+                                int n_parts, hipStream_t stream);
+hipError_t launch_quantize_f32(const float* x, int64_t rows, int64_t K, uint8_t* codes,
+                               uint8_t* scales, float* gscale, float* partials, int n_parts,
+                               hipStream_t stream);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
+// -------------------------------------------------------------------- gemv --
+
+struct EpilogueArgs {
+  float tau0, t_low, t_high, t_base;
+  int window, mode;
+  const uint8_t* step_start;
+  void* state;
+  float* entropy;
+  float* temperature;
+};
+
+// Launch configuration of the small-M GEMV, chosen per (M, N, K) on the
+// host and fixed for the life of a captured graph.
+struct GemvConfig {
+  int mt;          // compiled token count (1, 2, 4 or 8) >= M
+  int g;           // lanes per weight row
+  int r;           // rows per lane
+  int waves;       // waves per workgroup
+  int kp;          // K elements per LDS phase
+  int64_t rows_per_wg;
+  int64_t grid;
+};
+
+GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi);
+
+// Workspace bytes the LM-head epilogue needs for this shape.
+size_t lmhead_workspace_bytes(int M, int64_t N, int64_t K);
+size_t reset_state_bytes(int window);
+constexpr int kResetMaxWindow = 1024;
+
+hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const uint8_t* a_scales, const float* a_gscale, const uint8_t* w_codes,
+                       const uint8_t* w_scales, const float* w_gscale, float* y,
+                       const EpilogueArgs* epi, void* ws, hipStream_t stream);
+
+hipError_t launch_reset_state_init(void* state, int M, int window, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,261 @@
+// NVFP4 quantization kernels for gfx950: the per-layer activation "Q" step
+// (ReSET reading notes, section 5.3) and the offline weight pack.
+//
+// Format (reading notes, sections 2.1 and 6.1): E2M1 elements, one E4M3
+// scale per 16-element block, one FP32 global scale per tensor.  Recipe:
+//   s_g = amax / 2688                      (2688 = 6 * 448)
+//   t_b = amax_b / (6 * s_g)               (0 when s_g == 0)
+//   s_b = E4M3 round-to-nearest-even of t_b, saturated at 448
+//   e_b = E4M3(s_b) * s_g
+//   q   = E2M1 round-to-nearest-even of |x| / e_b, saturated at 6 (0 when
+//         e_b == 0), sign bit copied from x
+// every step one IEEE float32 operation, so the result is bit-reproducible.
+// This file is compiled with FP contraction off; float division is the
+// correctly rounded sequence and float32 denormals are kept (IEEE mode).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Nearest E4M3 code of a finite t >= 0, ties to the even code, saturated at
+// 448 (code 0x7E).  Below 2^-6 the grid is the subnormal one, step 2^-9;
+// above, a grid of 8 steps per binade.  t * 2^k is exact, rintf rounds half
+// to even, and the code of a grid point has the parity of its step count, so
+// "ties to even step" is "ties to even code".
+__device__ __forceinline__ uint32_t e4m3_code(float t) {
+  if (!(t < 448.0f)) return 0x7Eu;
+  if (t < 0.015625f) return (uint32_t)rintf(t * 512.0f);            // 0 .. 8
+  const int e = (int)((__float_as_uint(t) >> 23) & 0xFFu) - 127;      // -6 .. 8
+  const float to_steps = __uint_as_float((uint32_t)(127 + 3 - e) << 23);  // 2^(3-e)
+  const uint32_t q = (uint32_t)rintf(t * to_steps);                   // 8 .. 16
+  return ((uint32_t)(e + 7) << 3) + (q - 8u);                          // 16 carries into e+1
+}
+
+// Value of a non-negative E4M3 code (<= 0x7E) as float32 (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;                          // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));              // 2^(e-7) * (1 + m/8)
+}
+
+// E2M1 magnitude code of a >= 0: nearest of {0,.5,1,1.5,2,3,4,6}, ties to
+// the even code, saturated at 6.  Each comparison is one grid midpoint; a
+// midpoint that ties toward the upper (even) code uses >=, toward the lower
+// (even) code uses >.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+// Quantize one 16-element block.  Returns the block-scale code; writes the
+// 16 codes packed two per byte (element 2j in the low nibble) into c0/c1.
+__device__ __forceinline__ uint32_t quant_block(const float (&x)[16], float s_g, uint32_t& c0,
+                                                uint32_t& c1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  float t = 0.0f;
+  if (s_g != 0.0f) {
+    const float denom = 6.0f * s_g;
+    t = amax / denom;
+  }
+  const uint32_t sb = e4m3_code(t);
+  const float e = e4m3_value(sb) * s_g;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float v = (e != 0.0f) ? fabsf(x[i]) / e : 0.0f;
+    const uint32_t q = e2m1_mag_code(v) | ((__float_as_uint(x[i]) >> 31) << 3);
+    if (i < 8) lo |= q << (4 * i);
+    else hi |= q << (4 * (i - 8));
+  }
+  c0 = lo;
+  c1 = hi;
+  return sb;
+}
+
+template <typename T>
+struct Loader;
+
+template <>
+struct Loader<uint16_t> {  // bf16 bit patterns
+  static __device__ __forceinline__ void block(const uint16_t* p, float (&x)[16]) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+  // max |x| over 8 consecutive elements
+  static __device__ __forceinline__ float amax8(const uint16_t* p) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    // |bf16| as the top half of a float: clear the sign bits
+    const uint32_t w[4] = {a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(bf16_to_f32(w[i] & 0xFFFFu), bf16_to_f32(w[i] >> 16)));
+    return m;
+  }
+};
+
+template <>
+struct Loader<float> {
+  static __device__ __forceinline__ void block(const float* p, float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = reinterpret_cast<const float4*>(p)[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  }
+  static __device__ __forceinline__ float amax8(const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                 fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+  }
+};
+
+// Max over a workgroup of kThreads threads; result valid in every thread.
+__device__ __forceinline__ float wg_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+// amax of elements [lo, hi) of x (hi - lo a multiple of 8), by this workgroup.
+template <typename T>
+__device__ __forceinline__ float wg_amax_range(const T* x, int64_t lo, int64_t hi, float* red) {
+  float m = 0.0f;
+  for (int64_t i = lo + (int64_t)threadIdx.x * 8; i < hi; i += (int64_t)kThreads * 8)
+    m = fmaxf(m, Loader<T>::amax8(x + i));
+  return wg_max(m, red);
+}
+
+// Pass 1 of the two-launch path: partials[b] = max |x| over chunk b.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_partials_kernel(const T* __restrict__ x, int64_t n,
+                                                                 float* __restrict__ partials) {
+  __shared__ float red[kThreads / 64];
+  const int64_t per = ((n / 8 + gridDim.x - 1) / gridDim.x) * 8;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
+  const float m = wg_amax_range(x, lo < n ? lo : n, hi, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Quantize rows x [rows][K]; one thread per 16-element block, grid-stride.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t K, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode,
+    const float* __restrict__ partials, int n_parts) {
+  __shared__ float red[kThreads / 64];
+  float s_g;
+  if (mode == GS_STATIC) {
+    s_g = *gscale;
+  } else {
+    float amax;
+    if (mode == GS_SELF) {
+      amax = wg_amax_range(x, 0, rows * K, red);
+    } else {
+      float m = 0.0f;
+      for (int i = threadIdx.x; i < n_parts; i += kThreads) m = fmaxf(m, partials[i]);
+      amax = wg_max(m, red);
+    }
+    s_g = amax / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
+  }
+  const int64_t bpr = K / 16;
+  const int64_t nblocks = rows * bpr;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * kThreads) {
+    const int64_t row = b / bpr, j = b - row * bpr;
+    float v[16];
+    Loader<T>::block(x + row * K + j * 16, v);
+    uint32_t c0, c1;
+    const uint32_t sb = quant_block(v, s_g, c0, c1);
+    *reinterpret_cast<uint2*>(codes + row * (K / 2) + j * 8) = make_uint2(c0, c1);
+    scales[row * bpr + j] = (uint8_t)sb;
+  }
+}
+
+__global__ void fill_zero_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+int64_t quant_grid(int64_t nblocks) {
+  int64_t g = (nblocks + kThreads - 1) / kThreads;
+  if (g > 4096) g = 4096;
+  return g < 1 ? 1 : g;
+}
+
+}  // namespace
+
+int amax_partial_count(int64_t elems) {
+  int64_t p = (elems + 65535) / 65536;
+  if (p > 2048) p = 2048;
+  return (int)(p < 1 ? 1 : p);
+}
+
+hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                                uint8_t* scales, float* gscale, GsMode mode, float* partials,
+                                int n_parts, hipStream_t stream) {
+  const int64_t nblocks = rows * (K / 16);
+  if (mode == GS_FROM_PARTIALS) {
+    hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x,
+                       rows * K, partials);
+  }
+  hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((unsigned)quant_grid(nblocks)), dim3(kThreads),
+                     0, stream, x, rows, K, codes, scales, gscale, (int)mode, partials, n_parts);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_f32(const float* x, int64_t rows, int64_t K, uint8_t* codes,
+                               uint8_t* scales, float* gscale, float* partials, int n_parts,
+                               hipStream_t stream) {
+  const int64_t nblocks = rows * (K / 16);
+  hipLaunchKernelGGL(amax_partials_kernel<float>, dim3(n_parts), dim3(kThreads), 0, stream, x,
+                     rows * K, partials);
+  hipLaunchKernelGGL(quantize_kernel<float>, dim3((unsigned)quant_grid(nblocks)), dim3(kThreads), 0,
+                     stream, x, rows, K, codes, scales, gscale, (int)GS_FROM_PARTIALS, partials,
+                     n_parts);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  int64_t g = (n16 + 255) / 256;
+  if (g > 1024) g = 1024;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)g), dim3(256), 0, stream,
+                     reinterpret_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

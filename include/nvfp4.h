@@ -1,0 +1,165 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 small-M decode projection.
+ *
+ * The operation (ReSET project page, "Core contribution -- the nvfp4r
+ * CUDA-core kernel"): y = A . W^T for a small number M (1..8) of active
+ * decode tokens, where both the activation A [M][K] and the weight W [N][K]
+ * are NVFP4 tensors (ReSET reading notes, section 2.1 and section 6.1):
+ *
+ *   - every element is a 4-bit E2M1 float, two per byte, element 2j in the
+ *     low nibble of byte j;
+ *   - each run of 16 consecutive elements of a row shares one FP8 E4M3
+ *     block scale; scales are stored row-major [rows][K/16], not interleaved
+ *     (reading notes, section 5.3 and its Table 3);
+ *   - the tensor carries one FP32 global scale;
+ *   - value = E2M1(code) * E4M3(block scale) * global scale.
+ *
+ * The activation is quantized on the fly, once per layer, by its own call
+ * (the "Q" step, reading notes section 5.3); weights are packed once,
+ * offline.  The quantization recipe (global scale amax / (6*448), block
+ * scale RNE to E4M3 with saturation at 448, element RNE to E2M1 with
+ * saturation at 6, ties to the even code) is fixed and bit-reproducible.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates and frees nothing.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream).  No call synchronizes, so every call
+ *     can be captured into a hipGraph.
+ *   - Arguments are validated on the host BEFORE any HIP call.  A negative
+ *     status means nothing was launched and no output was touched.
+ *   - Device pointers must be 16-byte aligned (NVFP4_ERR_ALIGN otherwise),
+ *     except scalars (global scales, entropy/temperature outputs, flags).
+ *   - Shapes: 1 <= M <= 8, N >= 1, K >= 32, K % 32 == 0.
+ *   - Outputs must not overlap inputs (NVFP4_ERR_ARG).
+ *   - Non-finite inputs give undefined (but memory-safe) results.
+ *   - Workspace `ws` is caller-owned device scratch of at least
+ *     nvfp4_workspace_size(op, M, N, K) bytes; it must be zero-filled once
+ *     after allocation (nvfp4_workspace_init does that with a kernel).
+ *     Kernels that use counters in it reset them before they finish, so
+ *     graph replays are safe.  Calls that share one workspace must be
+ *     ordered on one stream.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = -1,      /* a required pointer is NULL                     */
+  NVFP4_ERR_SHAPE = -2,     /* M not in [1,8], N < 1, K < 32 or K % 32 != 0    */
+  NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned        */
+  NVFP4_ERR_WORKSPACE = -4, /* ws is NULL or ws_bytes is too small             */
+  NVFP4_ERR_DEVICE = -5,    /* the current HIP device is not a gfx950         */
+  NVFP4_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed     */
+  NVFP4_ERR_ARG = -7        /* other bad argument: flags, epilogue parameters,
+                               overlapping input/output buffers               */
+} nvfp4_status_t;
+
+/* nvfp4_quantize_act flags */
+enum { NVFP4_GS_DYNAMIC = 0, NVFP4_GS_STATIC = 1 };
+
+/* ops for nvfp4_workspace_size */
+enum { NVFP4_OP_PACK = 0, NVFP4_OP_QUANT = 1, NVFP4_OP_GEMV = 2, NVFP4_OP_GEMV_LMHEAD = 3 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nvfp4_status_str(int status);
+
+/* Bytes of workspace the op needs for this shape (0 = none; M is ignored
+ * for NVFP4_OP_PACK, where N x K is the weight).  Pure host function. */
+size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K);
+
+/* Zero-fill a workspace with a kernel on `stream` (graph-capturable; no
+ * hipMemset).  ws must be 16-byte aligned; ws_bytes % 16 == 0. */
+int nvfp4_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Offline weight packing: W fp32 [N][K] -> codes u8 [N][K/2], E4M3 block
+ * scales u8 [N][K/16], global scale fp32 [1] (= amax(|W|) / 2688).
+ * The packed bytes are bit-identical to the reference recipe.  Needs
+ * nvfp4_workspace_size(NVFP4_OP_PACK, 0, N, K) bytes of ws.  1 <= N,
+ * K >= 32, K % 32 == 0 (M limits do not apply).
+ */
+int nvfp4_pack_weights(const float* w, int64_t N, int64_t K,
+                       uint8_t* codes, uint8_t* scales, float* gscale,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * On-the-fly activation quantization, the per-layer "Q" step (reading
+ * notes, section 5.3): x bf16 [M][K] (raw bit patterns) -> codes u8
+ * [M][K/2], scales u8 [M][K/16] and the global scale.
+ *   flags = NVFP4_GS_DYNAMIC: *gscale (device) is WRITTEN with
+ *           amax over all M x K elements / 2688 (one scale per tensor, so a
+ *           row's codes depend on the other rows);
+ *   flags = NVFP4_GS_STATIC:  *gscale (device) is READ (a calibrated
+ *           scale); rows are then independent.
+ * Codes, scales and gscale are bit-identical to the reference recipe.
+ * Workspace: nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K) bytes (may be 0;
+ * ws may then be NULL).
+ */
+int nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K,
+                       uint8_t* codes, uint8_t* scales, float* gscale,
+                       int flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ReSET per-sequence state, device resident (ReSET reading notes, sections
+ * 4.1 and 4.2): running sum and count of all entropies so far, running sum
+ * and length of the current reasoning step, and a ring of the last `window`
+ * entropies.  Opaque; nvfp4_reset_state_size(window) bytes per sequence
+ * (a multiple of 16), M sequences stored back to back.  1 <= window <= 1024.
+ */
+size_t nvfp4_reset_state_size(int window);
+int nvfp4_reset_state_init(void* state, int M, int window, void* stream);
+
+/*
+ * Optional fused LM-head epilogue (ReSET project page, "Step-aware
+ * temperature scaling"; reading notes sections 3.1, 4.1-4.3): after the
+ * GEMV produced the logits y [M][N], compute per token the softmax entropy
+ * H_t (natural log, temperature 1, all N logits) and the ReSET temperature:
+ *   update the sequence state with H_t (a position flagged step_start[m]=1
+ *   begins a new step; the first call after init always does);
+ *   Hbar = mean of all entropies so far;
+ *   Hstep = mean of the last min(window, count) entropies while the current
+ *           step is at most `window` positions long, else the step's mean;
+ *   tau   = Hstep if Hstep > Hbar (uncertain step) else tau0;
+ *   T     = t_low if H_t < tau else t_high      (mode 0, ReSET)
+ *   T     = t_base                              (mode 1, ReSET off).
+ */
+typedef struct {
+  float tau0, t_low, t_high, t_base;
+  int window;                 /* must equal the window the states were initialised with */
+  int mode;                   /* 0 = ReSET, 1 = BASE                                     */
+  const uint8_t* step_start;  /* [M] device: 1 = this position starts a new step          */
+  void* state;                /* [M] device states (nvfp4_reset_state_size(window) each) */
+  float* entropy;             /* [M] device out, nats                                    */
+  float* temperature;         /* [M] device out                                          */
+} nvfp4_lmhead_epilogue_t;
+
+/*
+ * y [M][N] fp32 = dequant(A) . dequant(W)^T, the small-M decode projection.
+ * A is (a_codes [M][K/2], a_scales [M][K/16], *a_gscale), W is (w_codes
+ * [N][K/2], w_scales [N][K/16], *w_gscale); both global scales are device
+ * pointers.  Each weight byte is read from HBM once for all M tokens.
+ * Result: within |y - y_exact| <= 1e-5 * sum_k |a_k w_k| of the exact real
+ * dot product of the dequantized rows.
+ * epi == NULL: plain projection, no workspace needed.
+ * epi != NULL: LM-head epilogue as above; needs
+ *   nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD, M, N, K) bytes of zeroed ws.
+ */
+int nvfp4_gemv_smallm(int M, int64_t N, int64_t K,
+                      const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                      float* y, const nvfp4_lmhead_epilogue_t* epi,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

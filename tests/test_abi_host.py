@@ -1,0 +1,138 @@
+"""The C-ABI library loads, exports every function include/nvfp4.h declares,
+and rejects bad arguments with the documented status before any HIP call
+(so these run without a GPU; fake device addresses are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+F = pytest.importorskip("fp4_decode_gemv_amd")
+
+HDR = os.path.join(ROOT, "include", "nvfp4.h")
+A = 0x7F0000000000          # a 16-byte-aligned fake device address
+BIG = 1 << 30               # spacing so fake buffers never overlap
+
+
+def _declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(nvfp4_[a-z_0-9]+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(F.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return F.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == set(F.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(0, -8, -1):
+        txt = F.status_str(s)
+        assert txt.startswith("NVFP4_"), txt
+    assert "unknown" in F.status_str(-99)
+
+
+def _gemv(L, M=1, N=64, K=64, a=A, asc=A + BIG, ag=A + 2 * BIG, w=A + 3 * BIG, wsc=A + 4 * BIG,
+          wg=A + 5 * BIG, y=A + 6 * BIG, epi=None, ws=None, wsb=0):
+    return L.nvfp4_gemv_smallm(M, N, K, a, asc, ag, w, wsc, wg, y, epi, ws, wsb, None)
+
+
+def test_gemv_shape_errors(L):
+    for M, N, K in [(0, 64, 64), (9, 64, 64), (1, 0, 64), (1, 64, 16), (1, 64, 48), (1, 64, 0), (-1, 64, 64)]:
+        assert _gemv(L, M, N, K) == F.NVFP4_ERR_SHAPE, (M, N, K)
+
+
+def test_gemv_null_align_overlap_errors(L):
+    assert _gemv(L, a=None) == F.NVFP4_ERR_NULL
+    assert _gemv(L, wg=None) == F.NVFP4_ERR_NULL
+    assert _gemv(L, y=None) == F.NVFP4_ERR_NULL
+    assert _gemv(L, w=A + 3 * BIG + 8) == F.NVFP4_ERR_ALIGN
+    assert _gemv(L, y=A + 6 * BIG + 4) == F.NVFP4_ERR_ALIGN
+    # y overlapping the weight codes
+    assert _gemv(L, y=A + 3 * BIG + 16) == F.NVFP4_ERR_ARG
+
+
+def test_gemv_epilogue_errors(L):
+    st, ent, tmp, flags = A + 7 * BIG, A + 8 * BIG, A + 9 * BIG, A + 10 * BIG
+    def epi(window=8, mode=0, state=st):
+        return ctypes.byref(F.LmheadEpilogue(0.6, 0.4, 1.0, 0.6, window, mode, flags, state, ent, tmp))
+    need = L.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, 1, 64, 64)
+    assert need > 0
+    ws = A + 11 * BIG
+    assert _gemv(L, epi=epi(window=0), ws=ws, wsb=need) == F.NVFP4_ERR_ARG
+    assert _gemv(L, epi=epi(window=2000), ws=ws, wsb=need) == F.NVFP4_ERR_ARG
+    assert _gemv(L, epi=epi(mode=3), ws=ws, wsb=need) == F.NVFP4_ERR_ARG
+    assert _gemv(L, epi=epi(state=None), ws=ws, wsb=need) == F.NVFP4_ERR_NULL
+    assert _gemv(L, epi=epi(state=st + 4), ws=ws, wsb=need) == F.NVFP4_ERR_ALIGN
+    assert _gemv(L, epi=epi(), ws=ws, wsb=need - 1) == F.NVFP4_ERR_WORKSPACE
+    assert _gemv(L, epi=epi(), ws=None, wsb=need) == F.NVFP4_ERR_WORKSPACE
+    # workspace overlapping the logits
+    assert _gemv(L, epi=epi(), ws=A + 6 * BIG, wsb=need) == F.NVFP4_ERR_ARG
+
+
+def test_quantize_act_errors(L):
+    q = L.nvfp4_quantize_act
+    x, c, s, g = A, A + BIG, A + 2 * BIG, A + 3 * BIG
+    assert q(x, 0, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
+    assert q(x, 9, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
+    assert q(x, 1, 40, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
+    assert q(None, 1, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_NULL
+    assert q(x, 1, 64, c, s, None, 0, None, 0, None) == F.NVFP4_ERR_NULL
+    assert q(x, 1, 64, c, s, g, 7, None, 0, None) == F.NVFP4_ERR_ARG
+    assert q(x + 2, 1, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_ALIGN
+    assert q(x, 1, 64, x + 16, s, g, 0, None, 0, None) == F.NVFP4_ERR_ARG   # codes inside x
+    # large dynamic tensors need the amax workspace
+    need = L.nvfp4_workspace_size(F.NVFP4_OP_QUANT, 8, 0, 25600)
+    assert need > 0
+    assert q(x, 8, 25600, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_WORKSPACE
+    assert q(x, 8, 25600, c, s, g, 0, A + 5 * BIG, need - 4, None) == F.NVFP4_ERR_WORKSPACE
+    # static scale needs no workspace: passes validation, then fails only at the device check
+    assert L.nvfp4_workspace_size(F.NVFP4_OP_QUANT, 1, 0, 4096) == 0
+
+
+def test_pack_errors(L):
+    p = L.nvfp4_pack_weights
+    w, c, s, g, ws = A, A + BIG, A + 2 * BIG, A + 3 * BIG, A + 4 * BIG
+    need = L.nvfp4_workspace_size(F.NVFP4_OP_PACK, 0, 100, 64)
+    assert need >= 4
+    assert p(w, 0, 64, c, s, g, ws, need, None) == F.NVFP4_ERR_SHAPE
+    assert p(w, 100, 20, c, s, g, ws, need, None) == F.NVFP4_ERR_SHAPE
+    assert p(None, 100, 64, c, s, g, ws, need, None) == F.NVFP4_ERR_NULL
+    assert p(w, 100, 64, c, s, g, None, need, None) == F.NVFP4_ERR_WORKSPACE
+    assert p(w, 100, 64, c, s, g, ws, need - 1, None) == F.NVFP4_ERR_WORKSPACE
+    assert p(w, 100, 64, c + 1, s, g, ws, need, None) == F.NVFP4_ERR_ALIGN
+    assert p(w, 100, 64, w + 64, s, g, ws, need, None) == F.NVFP4_ERR_ARG
+
+
+def test_reset_state_and_workspace_helpers(L):
+    assert L.nvfp4_reset_state_size(0) == 0
+    assert L.nvfp4_reset_state_size(2000) == 0
+    for w in (1, 8, 32, 1024):
+        sz = L.nvfp4_reset_state_size(w)
+        assert sz % 16 == 0 and sz >= 4 * w + 32
+    assert L.nvfp4_reset_state_init(A, 0, 8, None) == F.NVFP4_ERR_SHAPE
+    assert L.nvfp4_reset_state_init(A, 1, 0, None) == F.NVFP4_ERR_ARG
+    assert L.nvfp4_reset_state_init(None, 1, 8, None) == F.NVFP4_ERR_NULL
+    assert L.nvfp4_reset_state_init(A + 8, 1, 8, None) == F.NVFP4_ERR_ALIGN
+    assert L.nvfp4_workspace_init(None, 16, None) == F.NVFP4_ERR_NULL
+    assert L.nvfp4_workspace_init(A + 4, 16, None) == F.NVFP4_ERR_ALIGN
+    assert L.nvfp4_workspace_init(A, 20, None) == F.NVFP4_ERR_ARG
+    assert L.nvfp4_workspace_size(F.NVFP4_OP_GEMV, 1, 4096, 4096) == 0
+    assert L.nvfp4_workspace_size(99, 1, 4096, 4096) == 0
+    # the LM-head workspace grows with N
+    a = L.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, 8, 151936, 5120)
+    b = L.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, 8, 4096, 5120)
+    assert a > b > 0

@@ -1,0 +1,119 @@
+"""GPU parity of the small-M GEMV against the oracle: every output within
+|y - y_ref| <= 1e-5 * sum_k |a_k w_k| (the oracle's exact fp64 result)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_decode_gemv_amd as F
+import workloads as W
+from oracle import nvfp4_oracle as O
+from gpu_util import assert_gemv_close, assert_same_q, bf16_dev, f32_dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(M, N, K, w, xbits, what):
+    print(f"[gemv] {what} M={M} N={N} K={K}", flush=True)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    aq = F.nvfp4_quantize_act(bf16_dev(xbits))
+    y = F.nvfp4_gemv_smallm(aq, wq)
+    torch.cuda.synchronize()
+    return wq, aq, y.cpu().numpy()
+
+
+# small shapes: several tiles, ragged row tails, K that is not a multiple of
+# the lane stride, multi-phase K for larger M
+SMALL = [(1, 1, 32), (1, 100, 64), (2, 257, 96), (3, 33, 160), (4, 1000, 512), (5, 64, 4096),
+         (6, 129, 4128), (7, 70, 8192), (8, 500, 5120), (8, 17, 12288), (8, 300, 25600), (1, 4097, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_shapes_full_compare(M, N, K):
+    w = W.small_random_weights(N * 7 + K, N, K)
+    xb = W.small_random_bf16(M * 13 + K, M, K)
+    wq, aq, y = _run(M, N, K, w, xb, "small")
+    wr, ar = O.quantize_nvfp4(w), O.quantize_act_bf16(xb)
+    assert_same_q(host(wq), wr, what="pack")
+    assert_same_q(host(aq), ar, what="act")
+    y_ref, ref_abs = O.gemv_ref(ar, wr)
+    assert_gemv_close(y, y_ref, ref_abs, what=f"M={M} N={N} K={K}")
+
+
+def _full_size(case, Ms):
+    w = W.weights(case.w_seed, case.N, case.K, case.w_outlier_rows)
+    wt = f32_dev(w)
+    wq = F.nvfp4_pack_weights(wt)
+    del wt
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, case.N - 1], W.outlier_rows_of(case.w_seed, case.N, case.K)[:6],
+                                     rng.choice(case.N, 60, replace=False)]))
+    s_g = O.global_scale(np.max(np.abs(w)))
+    wr = O.quantize_nvfp4(w[rows], s_g)
+    del w
+    for M in Ms:
+        xb = W.case_activations_bf16(case, M)
+        print(f"[gemv] {case.name} M={M} N={case.N} K={case.K}", flush=True)
+        aq = F.nvfp4_quantize_act(bf16_dev(xb))
+        y = F.nvfp4_gemv_smallm(aq, wq)
+        torch.cuda.synchronize()
+        ar = O.quantize_act_bf16(xb)
+        assert_same_q(host(aq), ar, what=f"act {case.name} M={M}")
+        y_ref, ref_abs = O.gemv_ref(ar, wr)
+        assert_gemv_close(y.cpu().numpy()[:, rows], y_ref, ref_abs, what=f"{case.name} M={M}")
+
+
+def test_single_4096_full_compare():
+    case = W.single_case()
+    w = W.weights(case.w_seed, case.N, case.K)
+    xb = W.activations_bf16(case.x_seed, case.K, 1)
+    wq, aq, y = _run(1, case.N, case.K, w, xb, case.name)
+    wr, ar = O.quantize_nvfp4(w), O.quantize_act_bf16(xb)
+    y_ref, ref_abs = O.gemv_ref(ar, wr)
+    assert_gemv_close(y, y_ref, ref_abs, what=case.name)
+
+
+@pytest.mark.parametrize("case", W.qwen3_8b_cases(), ids=lambda c: c.name)
+def test_qwen3_8b_projections(case):
+    _full_size(case, (1, 2, 4, 8))
+
+
+@pytest.mark.parametrize("case", W.qwen3_32b_cases(), ids=lambda c: c.name)
+def test_qwen3_32b_projections(case):
+    _full_size(case, (1, 2, 4, 8))
+
+
+def test_lm_head_projection():
+    _full_size(W.lm_head_case(), (1, 8))
+
+
+def test_zero_activation_and_zero_rows():
+    N, K = 300, 1024
+    w = W.small_random_weights(3, N, K)
+    w[7] = 0.0
+    w[299] = -0.0
+    xb = W.small_random_bf16(4, 4, K)
+    xb[2] = 0
+    wq, aq, y = _run(4, N, K, w, xb, "zeros")
+    assert np.all(y[2] == 0.0)
+    assert np.all(y[:, 7] == 0.0) and np.all(y[:, 299] == 0.0)
+
+
+def test_gemv_is_repeatable_and_rows_do_not_depend_on_m():
+    N, K = 5120, 8192
+    w = W.small_random_weights(11, N, K)
+    xb = W.small_random_bf16(12, 8, K)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    gs = torch.tensor([0.01], dtype=torch.float32, device="cuda:0")      # static: rows independent
+    aq8 = F.nvfp4_quantize_act(bf16_dev(xb), gscale=gs)
+    y1 = F.nvfp4_gemv_smallm(aq8, wq).cpu().numpy()
+    y2 = F.nvfp4_gemv_smallm(aq8, wq).cpu().numpy()
+    assert np.array_equal(y1, y2)
+    aq1 = F.nvfp4_quantize_act(bf16_dev(xb[:1]), gscale=gs)
+    y3 = F.nvfp4_gemv_smallm(aq1, wq).cpu().numpy()
+    # same inputs for row 0; results agree to the tolerance (tilings differ by M)
+    wr = O.quantize_nvfp4(w)
+    ar = O.quantize_act_bf16(xb[:1], np.float32(0.01))
+    y_ref, ref_abs = O.gemv_ref(ar, wr)
+    assert_gemv_close(y3, y_ref, ref_abs, what="M=1 static")
+    assert_gemv_close(y1[:1], y_ref, ref_abs, what="M=8 row 0 static")

@@ -1,0 +1,135 @@
+"""GPU parity of the fused LM-head epilogue: entropy within 1e-4 nats of the
+fp64 entropy of the GPU's own logits, and ReSET temperatures equal to the
+oracle's wherever the decision is not within the rounding band of a tie."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_decode_gemv_amd as F
+import workloads as W
+from oracle import nvfp4_oracle as O
+from oracle import reset_oracle as R
+from gpu_util import assert_gemv_close, bf16_dev, f32_dev
+
+pytestmark = pytest.mark.gpu
+
+BAND = 1e-9   # rounding band for decisions fed with the GPU's own entropies
+
+
+def _decisions_agree(tr: R.ResetTrace, T_gpu: np.ndarray, p: R.ResetParams, band: float):
+    """Compare T where neither comparison of the oracle is within `band` of a tie."""
+    tie = (np.abs(tr.Hstep - tr.Hbar) < band) | (np.abs(tr.H - tr.tau) < band)
+    ok = (T_gpu.astype(np.float64) == np.float32(tr.T).astype(np.float64)) | tie
+    return ok, int(tie.sum())
+
+
+def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None):
+    """Decode `positions` steps; returns logits of the last step, H [P][M], T [P][M]."""
+    dev = torch.device("cuda:0")
+    P = xbits_pos.shape[0]
+    st = F.new_reset_state(M, p.window, dev)
+    ent = torch.empty(M, device=dev)
+    tmp = torch.empty(M, device=dev)
+    ws = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, wq.rows, wq.K), dev)
+    Hs, Ts, logits = [], [], []
+    for t in range(P):
+        xb = xbits_pos[t]
+        aq = F.nvfp4_quantize_act(bf16_dev(xb))
+        if scale_exp is not None:
+            aq.gscale.mul_(float(2.0 ** scale_exp[t]))
+        f = torch.from_numpy(np.ascontiguousarray(flags[t])).to(dev)
+        epi = F.Epilogue(step_start=f, state=st, entropy=ent, temperature=tmp, tau0=p.tau0, t_low=p.t_low,
+                         t_high=p.t_high, t_base=p.t_base, window=p.window, mode=p.mode)
+        y = F.nvfp4_gemv_smallm(aq, wq, epi=epi, ws=ws)
+        Hs.append(ent.cpu().numpy().copy())
+        Ts.append(tmp.cpu().numpy().copy())
+        logits.append(y.cpu().numpy())
+    return logits, np.array(Hs), np.array(Ts)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_small_vocab_sequence(mode):
+    M, N, K, P = 4, 3000, 512, 60
+    w = W.small_random_weights(41, N, K, scale=0.2)
+    rng = np.random.default_rng(42)
+    xs = np.stack([W.small_random_bf16(100 + t, M, K) for t in range(P)])
+    u = rng.integers(0, 7, P)                 # activation scale 2^u: exact, spans H in ~[0, ln N]
+    flags = W.step_flags(43, P, M, p=0.15)
+    p = R.ResetParams(tau0=0.6, t_low=0.4, t_high=1.0, t_base=0.6, window=4, mode=mode)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    logits, H, T = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
+    for t in range(P):
+        Href = R.entropy_rows(logits[t].astype(np.float64))
+        assert np.all(np.abs(H[t] - Href) <= 1e-4), (t, H[t], Href)
+    assert H.min() < 0.6 < H.max(), "sequence must exercise both sides of tau0"
+    ties = 0
+    for m in range(M):
+        tr = R.reset_sequence(H[:, m].astype(np.float32).astype(np.float64), flags[:, m], p)
+        ok, nt = _decisions_agree(tr, T[:, m], p, BAND)
+        ties += nt
+        assert ok.all(), (m, np.nonzero(~ok))
+        if mode == 1:
+            assert np.all(T[:, m] == np.float32(0.6))
+    # logits of the last step against the oracle
+    wr = O.quantize_nvfp4(w)
+    ar = O.quantize_act_bf16(xs[-1])
+    ar = (ar[0], ar[1], np.float32(ar[2] * np.float32(2.0 ** u[-1])))
+    y_ref, ref_abs = O.gemv_ref(ar, wr)
+    assert_gemv_close(logits[-1], y_ref, ref_abs, what="lm logits")
+
+
+def test_chunked_runs_carry_state():
+    """One run of 40 positions equals two runs of 20 with the state kept."""
+    M, N, K = 2, 2000, 256
+    w = W.small_random_weights(51, N, K, scale=0.3)
+    xs = np.stack([W.small_random_bf16(200 + t, M, K) for t in range(40)])
+    flags = W.step_flags(52, 40, M, p=0.2)
+    p = R.ResetParams(window=3)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    _, H1, T1 = _run_sequence(wq, xs, flags, p, M)
+    # same thing, state re-initialised only once, in two halves
+    dev = torch.device("cuda:0")
+    st = F.new_reset_state(M, p.window, dev)
+    ent, tmp = torch.empty(M, device=dev), torch.empty(M, device=dev)
+    ws = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, N, K), dev)
+    T2 = []
+    for half in (range(0, 20), range(20, 40)):
+        for t in half:
+            aq = F.nvfp4_quantize_act(bf16_dev(xs[t]))
+            f = torch.from_numpy(np.ascontiguousarray(flags[t])).to(dev)
+            F.nvfp4_gemv_smallm(aq, wq, epi=F.Epilogue(f, st, ent, tmp, window=p.window), ws=ws)
+            T2.append(tmp.cpu().numpy().copy())
+    assert np.array_equal(np.array(T2), T1)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_lm_head_sequence(M):
+    case = W.lm_head_case()
+    P = 48
+    print(f"[lmhead] N={case.N} K={case.K} M={M} positions={P}", flush=True)
+    w = W.weights(case.w_seed, case.N, case.K, case.w_outlier_rows)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    torch.cuda.empty_cache()
+    xs = W.lm_head_positions_bf16(case.x_seed, P, M, case.K)
+    flags = W.step_flags(3300, P, M)
+    u = W.pow2_exponents(3400, P)
+    p = R.ResetParams(tau0=0.6, t_low=0.4, t_high=1.0, t_base=0.6, window=8)
+    logits, H, T = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
+    for t in range(P):
+        Href = R.entropy_rows(logits[t].astype(np.float64))
+        assert np.all(np.abs(H[t] - Href) <= 1e-4), (t, H[t], Href)
+    for m in range(M):
+        tr = R.reset_sequence(H[:, m].astype(np.float32).astype(np.float64), flags[:, m], p)
+        ok, _ = _decisions_agree(tr, T[:, m], p, BAND)
+        assert ok.all(), (m, np.nonzero(~ok))
+    # sampled logits of two positions against the oracle
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, case.N - 1], rng.choice(case.N, 64, replace=False)]))
+    s_g = O.global_scale(np.max(np.abs(w)))
+    wr = O.quantize_nvfp4(w[rows], s_g)
+    for t in (0, P - 1):
+        ar = O.quantize_act_bf16(xs[t])
+        ar = (ar[0], ar[1], np.float32(ar[2] * np.float32(2.0 ** u[t])))
+        y_ref, ref_abs = O.gemv_ref(ar, wr)
+        assert_gemv_close(logits[t][:, rows], y_ref, ref_abs, what=f"lm head t={t}")
