@@ -1,0 +1,283 @@
+"""Benchmark of the NVFP4 small-M decode projection on one MI355X.
+
+Workload: the four Qwen3-32B decode projections (fused QKV 10240x5120,
+o_proj 5120x8192, fused gate_up 51200x5120, down_proj 5120x25600) at
+M = 1, 2, 4 and 8 active tokens.  One step = for every M and every
+projection, quantize the bf16 activation on the GPU (the per-layer "Q" step)
+and run the GEMV against the packed NVFP4 weights: 16 quantize launches and
+16 GEMV launches.  Inputs are seeded synthetic tensors (workloads/), resident
+in HBM before timing starts.  Every projection has several packed copies
+that are rotated launch by launch, so no GEMV finds its weights in the
+256 MB Infinity Cache from an earlier launch.
+
+Prints one JSON line:
+  value        effective GB/s over the step = weight+scale bytes streamed per
+               step / step time (quantization included)
+  roofline     the GEMV kernel: algorithmic bytes of all GEMV launches of a
+               step / their summed average durations (HIP events on the
+               launch stream), against the 8 TB/s HBM peak
+  cpu_baseline the CPU oracle (quantize + dequantize + fp64 GEMV) on a
+               bounded row sample of the same projections, same byte formula
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs and effective HBM GB/s per NVFP4 GEMV at M=1/2/4/8; % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+M_LIST = (1, 2, 4, 8)
+CPU_ROWS = 2048
+
+
+def weight_bytes(N: int, K: int) -> int:
+    """Algorithmic bytes of one GEMV: codes + E4M3 scales + global scale."""
+    return N * K // 2 + N * K // 16 + 4
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="packed copies per projection (MALL rotation)")
+    ap.add_argument("--reps", type=int, default=30, help="timed launches per (projection, M) for per-kernel times")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle baseline")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def setup(args):
+    import torch
+
+    import fp4_decode_gemv_amd as F
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    cases = W.qwen3_32b_cases()
+    wq = {}      # name -> list of NvFp4Tensor copies
+    samples = {}  # name -> (first CPU_ROWS rows of W, global scale of the whole W)
+    for c in cases:
+        t0 = time.perf_counter()
+        w = W.weights(c.w_seed, c.N, c.K, c.w_outlier_rows)
+        samples[c.name] = (w[:CPU_ROWS].copy(), float(np.max(np.abs(w))))
+        wt = torch.from_numpy(w).to(dev)
+        del w
+        base = F.nvfp4_pack_weights(wt)
+        del wt
+        copies = [base]
+        for _ in range(args.copies - 1):
+            copies.append(F.NvFp4Tensor(base.codes.clone(), base.scales.clone(), base.gscale.clone()))
+        wq[c.name] = copies
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log(args, f"[setup] packed {c.name} {c.N}x{c.K} x{args.copies} in {time.perf_counter() - t0:.1f}s")
+    acts = {}
+    for c in cases:
+        for M in M_LIST:
+            bits = W.case_activations_bf16(c, M)
+            x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16).contiguous()
+            aq = F.NvFp4Tensor(torch.empty((M, c.K // 2), dtype=torch.uint8, device=dev),
+                               torch.empty((M, c.K // 16), dtype=torch.uint8, device=dev),
+                               torch.empty(1, dtype=torch.float32, device=dev))
+            need = F.nvfp4_workspace_size(F.NVFP4_OP_QUANT, M, 0, c.K)
+            ws = F.new_workspace(need, dev) if need else None
+            need = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, c.N, c.K)
+            gws = F.new_workspace(need, dev) if need else None
+            y = torch.empty((M, c.N), dtype=torch.float32, device=dev)
+            acts[(c.name, M)] = (x, aq, ws, gws, y)
+    torch.cuda.synchronize()
+    return cases, wq, acts, samples
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the design notes describe "
+              "how the projection would shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_decode_gemv_amd as F
+
+    F.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    cases, wq, acts, samples = setup(args)
+    stream = torch.cuda.current_stream()
+    use = {c.name: 0 for c in cases}
+
+    def gemv(c, M):
+        x, aq, ws, gws, y = acts[(c.name, M)]
+        w = wq[c.name][use[c.name] % args.copies]
+        use[c.name] += 1
+        F.nvfp4_gemv_smallm(aq, w, y=y, ws=gws, stream=stream)
+
+    def quant(c, M):
+        x, aq, ws, gws, y = acts[(c.name, M)]
+        F.nvfp4_quantize_act(x, ws=ws, out=aq, stream=stream)
+
+    def step():
+        for M in M_LIST:
+            for c in cases:
+                quant(c, M)
+                gemv(c, M)
+
+    # ---------------- whole-step throughput ----------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    bytes_per_step = sum(weight_bytes(c.N, c.K) for c in cases) * len(M_LIST)
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    log(args, f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s effective (quantization included)")
+
+    # ---------------- per-kernel durations (HIP events on the launch stream) ----------------
+    # `reps` launches of one case back to back between two events: the
+    # average is the kernel's duration as the hardware runs it in a decode
+    # step (it agrees with rocprofv3's per-dispatch durations); an event pair
+    # around every single launch would add the event overhead to each.
+    detail = []
+    gemv_bytes = 0
+    gemv_us = 0.0
+
+    def b2b(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(args.reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.reps
+
+    for c in cases:
+        for M in M_LIST:
+            gus = b2b(lambda: gemv(c, M))
+            qus = b2b(lambda: quant(c, M))
+            wb = weight_bytes(c.N, c.K)
+            detail.append({
+                "proj": c.name, "M": M, "N": c.N, "K": c.K, "weight_bytes": wb,
+                "variant": F.nvfp4_gemv_variant(M, c.N, c.K),
+                "gemv_us": round(gus, 3),
+                "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1),
+                "gemv_hbm_frac": round(wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "quant_us": round(qus, 3),
+            })
+            gemv_bytes += wb
+            gemv_us += gus
+            log(args, f"[kern] {c.name:18s} M={M} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s "
+                      f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us")
+    achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args, cases, samples)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-32B decode projections, NVFP4 W4A4: qkv 10240x5120, o 5120x8192, "
+                        "gate_up 51200x5120, down 5120x25600; M in {1,2,4,8}; one step = activation "
+                        "quantization + GEMV for each (projection, M)",
+            "global_batch": list(M_LIST),
+            "weight_bytes_per_step": bytes_per_step,
+            "weight_copies_rotated": args.copies,
+            "parallelism": "single-gpu",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "gemv_kernel, all 16 (projection, M) cases of a step: summed algorithmic bytes / summed "
+                      "average launch durations (back-to-back launches between HIP events)",
+        },
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, cases, samples):
+    """Time the oracle on the host: activation quantization plus dequantize +
+    fp64 GEMV over a row sample of each projection (M = 1..8 as in a step)."""
+    from oracle import nvfp4_oracle as O
+    import workloads as W
+
+    rows = CPU_ROWS
+    t_start = time.perf_counter()
+    # pack the sampled rows with the oracle (weight packing is offline, not timed)
+    packed = {}
+    for c in cases:
+        w, amax = samples[c.name]
+        packed[c.name] = O.quantize_nvfp4(w, O.global_scale(amax))
+    xs = {(c.name, M): W.case_activations_bf16(c, M) for c in cases for M in M_LIST}
+    runs = []
+    for _ in range(7):
+        t0 = time.perf_counter()
+        for M in M_LIST:
+            for c in cases:
+                aq = O.quantize_act_bf16(xs[(c.name, M)])
+                O.gemv_ref(aq, packed[c.name])
+        runs.append(time.perf_counter() - t0)
+        if len(runs) >= 3 and time.perf_counter() - t_start > args.cpu_seconds:
+            break
+    t = float(np.median(runs))
+    sample_bytes = sum(weight_bytes(rows, c.K) for c in cases) * len(M_LIST)
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    return {
+        "value": round(sample_bytes / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {rows} weight rows of each of the 4 projections x M in {{1,2,4,8}} "
+                  f"(activation quantization + dequantize + fp64 GEMV), median of {len(runs)} runs, "
+                  f"{t * 1e3:.0f} ms per sampled step; host {os.cpu_count()} logical CPUs",
+    }
+
+
+if __name__ == "__main__":
+    main()

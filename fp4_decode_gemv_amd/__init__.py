@@ -52,6 +52,8 @@ EXPORTED = (
     "nvfp4_reset_state_size",
     "nvfp4_reset_state_init",
     "nvfp4_gemv_smallm",
+    "nvfp4_gemv_variant",
+    "nvfp4_gemv_variant_name",
 )
 
 
@@ -107,6 +109,10 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_reset_state_size.argtypes = [c_int]
     L.nvfp4_reset_state_init.restype = c_int
     L.nvfp4_reset_state_init.argtypes = [vp, c_int, c_int, vp]
+    L.nvfp4_gemv_variant.restype = ctypes.c_char_p
+    L.nvfp4_gemv_variant.argtypes = [c_int, i64, i64, c_int]
+    L.nvfp4_gemv_variant_name.restype = ctypes.c_char_p
+    L.nvfp4_gemv_variant_name.argtypes = [c_int]
     L.nvfp4_gemv_smallm.restype = c_int
     L.nvfp4_gemv_smallm.argtypes = [c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(LmheadEpilogue), vp, sz, vp]
@@ -213,6 +219,27 @@ def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, 
     return out
 
 
+def nvfp4_gemv_variant(M: int, N: int, K: int, lmhead: bool = False) -> str:
+    """Kernel variant the library launches for this shape."""
+    return lib().nvfp4_gemv_variant(M, N, K, int(bool(lmhead))).decode()
+
+
+def nvfp4_gemv_variant_names() -> list[str]:
+    """Every compiled GEMV kernel variant (names usable in NVFP4_GEMV_VARIANT)."""
+    out, i = [], 0
+    while True:
+        n = lib().nvfp4_gemv_variant_name(i)
+        if n is None:
+            return out
+        out.append(n.decode())
+        i += 1
+
+
+def variant_tokens(name: str) -> int:
+    """Compiled token count of a variant name (``..._m<MT>_...``)."""
+    return int(name.split("_m")[1].split("_")[0])
+
+
 def nvfp4_reset_state_size(window: int) -> int:
     return int(lib().nvfp4_reset_state_size(window))
 
@@ -252,21 +279,20 @@ class Epilogue:
 
 def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | None = None, ws=None,
                       M: int | None = None, stream=None):
-    """y [M][N] fp32 = dequant(a) . dequant(w)^T."""
+    """y [M][N] fp32 = dequant(a) . dequant(w)^T.  ``ws``: a zero-filled
+    workspace of at least nvfp4_workspace_size(...) bytes (allocated here
+    when needed and not given)."""
     import torch
 
     M = a.rows if M is None else M
     N, K = w.rows, w.K
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=w.codes.device)
-    ce = None
-    ws_bytes = 0
-    if epi is not None:
-        ce = epi.as_c()
-        need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD, M, N, K)
-        if ws is None:
-            ws = new_workspace(need, w.codes.device, stream)
-        ws_bytes = ws.numel()
+    ce = None if epi is None else epi.as_c()
+    need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD if epi is not None else NVFP4_OP_GEMV, M, N, K)
+    if need and ws is None:
+        ws = new_workspace(need, w.codes.device, stream)
+    ws_bytes = 0 if ws is None else ws.numel()
     _check(lib().nvfp4_gemv_smallm(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale),
                                    _ptr(w.codes), _ptr(w.scales), _ptr(w.gscale), _ptr(y),
                                    None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,

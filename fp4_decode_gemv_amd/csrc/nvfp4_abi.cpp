@@ -82,10 +82,11 @@ size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K) {
       if (M < 1 || M > 8 || !shape_ok_k(K)) return 0;
       return quant_ws_bytes((int64_t)M * K, (int64_t)M * K > kActSelfAmaxMaxElems);
     case NVFP4_OP_GEMV:
-      return 0;
+      if (!shape_ok(M, N, K)) return 0;
+      return gemv_workspace_bytes(M, N, K, false);
     case NVFP4_OP_GEMV_LMHEAD:
       if (!shape_ok(M, N, K)) return 0;
-      return lmhead_workspace_bytes(M, N, K);
+      return gemv_workspace_bytes(M, N, K, true);
   }
   return 0;
 }
@@ -175,21 +176,27 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
   if (overlaps(y, yb, a_codes, acb) || overlaps(y, yb, a_scales, asb) || overlaps(y, yb, a_gscale, 4) ||
       overlaps(y, yb, w_codes, wcb) || overlaps(y, yb, w_scales, wsb) || overlaps(y, yb, w_gscale, 4))
     return NVFP4_ERR_ARG;
+  const GemvConfig cfg = choose_gemv_config(M, N, K, epi != nullptr);
+  const size_t need = (size_t)cfg.ws_bytes;
+  if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return NVFP4_ERR_ALIGN;
+  if (need > 0 && (overlaps(ws, need, y, yb) || overlaps(ws, need, a_codes, acb) || overlaps(ws, need, a_scales, asb) ||
+                   overlaps(ws, need, a_gscale, 4) || overlaps(ws, need, w_codes, wcb) ||
+                   overlaps(ws, need, w_scales, wsb) || overlaps(ws, need, w_gscale, 4)))
+    return NVFP4_ERR_ARG;
   EpilogueArgs ea{};
   if (epi) {
     if (!epi->step_start || !epi->state || !epi->entropy || !epi->temperature) return NVFP4_ERR_NULL;
     if (epi->window < 1 || epi->window > kResetMaxWindow || (epi->mode != 0 && epi->mode != 1))
       return NVFP4_ERR_ARG;
     if (!aligned16(epi->state)) return NVFP4_ERR_ALIGN;
-    const size_t need = lmhead_workspace_bytes(M, N, K);
-    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
     const size_t stb = (size_t)M * reset_state_bytes(epi->window);
-    if (overlaps(ws, need, y, yb) || overlaps(ws, need, epi->state, stb) || overlaps(y, yb, epi->state, stb) ||
+    if (overlaps(ws, need, epi->state, stb) || overlaps(y, yb, epi->state, stb) ||
         overlaps(y, yb, epi->entropy, (size_t)M * 4) || overlaps(y, yb, epi->temperature, (size_t)M * 4) ||
         overlaps(epi->entropy, (size_t)M * 4, epi->temperature, (size_t)M * 4) ||
         overlaps(epi->state, stb, epi->entropy, (size_t)M * 4) ||
-        overlaps(epi->state, stb, epi->temperature, (size_t)M * 4))
+        overlaps(epi->state, stb, epi->temperature, (size_t)M * 4) ||
+        overlaps(ws, need, epi->entropy, (size_t)M * 4) || overlaps(ws, need, epi->temperature, (size_t)M * 4))
       return NVFP4_ERR_ARG;
     ea.tau0 = epi->tau0;
     ea.t_low = epi->t_low;
@@ -204,9 +211,15 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
   }
   const int d = check_device();
   if (d != NVFP4_OK) return d;
-  const GemvConfig cfg = choose_gemv_config(M, N, K, epi != nullptr);
   return hip_status(launch_gemv(cfg, M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y,
                                 epi ? &ea : nullptr, ws, static_cast<hipStream_t>(stream)));
 }
+
+const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead) {
+  if (!shape_ok(M, N, K)) return "invalid shape";
+  return gemv_variant_name(choose_gemv_config(M, N, K, lmhead != 0).variant);
+}
+
+const char* nvfp4_gemv_variant_name(int index) { return gemv_variant_by_index(index); }
 
 }  // extern "C"

@@ -4,32 +4,50 @@
 // nvfp4r CUDA-core kernel", C1-C3; reading notes section 5.2): every weight
 // tile streamed from HBM once for all M tokens (C1), several independent
 // accumulator chains per thread (C2), FP4 unpacked in registers and fed
-// straight to the multiply-adds (C3).  The pages' Blackwell design is prior
-// art; this is the CDNA4 form of the same idea:
+// straight to the multiply-adds (C3).  The pages' design targets Blackwell
+// CUDA cores; two CDNA4 forms of it live here, and the launch table picks
+// one per (M, N, K) from measured latency, fixed for the life of a captured
+// graph (reading notes section 5.2, runtime dispatch):
 //
-//   * A workgroup owns a tile of weight rows.  G consecutive lanes of a
-//     wave64 share one row; each lane loads 16 bytes (32 codes = 2 blocks)
-//     per step with one dwordx4 load, so a row-group streams G*16 contiguous
-//     bytes per instruction, and R rows per lane give R*M independent chains.
-//   * The quantized activation of a K phase is decoded ONCE per workgroup
-//     into LDS as f16 values a = E2M1(q) * E4M3(s_b) (exact in f16: at most
-//     6 significant bits, magnitudes in [2^-10, 2688]), laid out so that the
-//     G lanes of a row-group read 16 consecutive bytes each (no bank
-//     conflicts) and the row-groups of a wave read the same addresses
-//     (broadcast).
-//   * Weight codes are decoded in registers with v_cvt_scalef32_pk_f16_fp4
-//     (scale 1.0: that instruction applies only the exponent of its scale
-//     operand, so the E4M3 block scale is applied separately).
-//   * Per 16-element block and token, 8 v_dot2c_f32_f16 give the exact block
-//     sum (products have <= 8 significant bits, a block sum <= 16 bits), and
-//     one FMA applies the weight block scale, decoded with v_cvt_pk_f32_fp8
-//     (OCP E4M3).  Two accumulators per (row, token) alternate blocks.
-//   * Lanes of a row-group are reduced with cross-lane shuffles; the two
-//     global scales multiply the result once.
+// Direct VALU kernel (gemv_direct_kernel), for M <= 2
+//   * G consecutive lanes of a wave64 share one weight row; each lane loads
+//     16 bytes (32 codes = 2 blocks) per step with one dwordx4 load; R rows
+//     per lane give R*M independent accumulator chains; a P-deep register
+//     ring keeps loads in flight.  No LDS and no barrier: every lane loads
+//     the activation codes and scales of its own K positions straight from
+//     L1/L2 (the activation is a few KB and shared by every workgroup) and
+//     decodes them in registers once for its R rows.
+//   * E2M1 codes become f16 with v_cvt_scalef32_pk_f16_fp4 (scale 1.0: the
+//     instruction applies only the exponent of its scale operand).  Per
+//     16-element block and token, 8 v_dot2c_f32_f16 give the exact block sum
+//     of E2M1 x E2M1 products (multiples of 1/4, at most 576 in magnitude),
+//     and one FMA applies sa*sw, the product of the two E4M3 block scales
+//     (exact in f32), decoded with v_cvt_pk_f32_fp8 (OCP E4M3).
 //
-// Error: products and block sums are exact; every accumulation chain is at
-// most K/(32G) + 1 + log2(G) + 2 roundings long, far inside the 1e-5
-// relative bound for the shapes served.
+// LDS VALU kernel (gemv_valu_kernel), any M <= 8
+//   * The same row mapping, but the activation of a K phase is decoded once
+//     per workgroup into LDS as f16 values E2M1(q) * E4M3(s_b) (exact in
+//     f16), so a block needs 8 v_dot2c per token and one FMA with sw.  Cost:
+//     about 0.5 + 0.56*M VALU operations per weight element, so the VALU
+//     issue rate, not HBM, bounds it from M of about 4 up.
+//
+// MFMA-assisted kernel (gemv_mfma_kernel), M <= 8
+//   * The same in-register weight decode, then the weight block scale is
+//     applied in f16 (E2M1 * E4M3 is exact in f16) and
+//     v_mfma_f32_16x16x32_f16 does the multiply-adds: rows of W are the
+//     16-row side of the instruction, tokens the 16-column side (columns
+//     >= M are ignored).  Lane (i, kg) loads 32 bytes (64 codes) of row i at
+//     element offset 64*kg of each 256-element step, so one wave
+//     instruction covers 16 full 128-byte lines; its eight 32-bit words feed
+//     eight MFMAs whose k index is permuted the same way on the activation
+//     side.  The activation operand is decoded in registers the
+//     same way (E2M1 * E4M3 of the activation, exact in f16) straight from
+//     L1/L2, so nothing is staged in LDS.
+//   * The waves of a workgroup share its 16*R rows and split K; their 16x16
+//     partial tiles are added in LDS in a fixed order.  VALU work is about
+//     (1 + 1/R) operations per weight element whatever M is.
+//
+// Every kernel multiplies by the two global scales once at the end.
 //
 // Optional LM-head epilogue (ReSET project page, "Step-aware temperature
 // scaling"; reading notes sections 3.1, 4.1-4.3): each workgroup also
@@ -40,6 +58,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "nvfp4_internal.h"
 
@@ -47,12 +67,14 @@ namespace nvfp4 {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
 struct GemvParams {
   int M;
   int64_t N, K;
-  int kp;  // K elements per LDS phase (multiple of 32)
+  int kp;  // K elements per LDS phase (multiple of 128)
   const uint8_t* a_codes;
   const uint8_t* a_scales;
   const float* a_gscale;
@@ -62,9 +84,9 @@ struct GemvParams {
   float* y;
   // LM-head epilogue (used only by the EPI instantiations)
   EpilogueArgs epi;
-  unsigned* counter;
-  float* partials;      // [gridDim.x][MT][3]
-  size_t state_bytes;   // bytes per ReSET state
+  unsigned* counter;       // epilogue: workgroups (row tiles) done
+  float* partials;         // epilogue: [row tiles][MT][3]
+  size_t state_bytes;      // bytes per ReSET state
 };
 
 // ReSET per-sequence state (device).  Followed by float ring[window].
@@ -78,10 +100,19 @@ struct ResetState {
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
+// two f32 -> packed f16 pair (round toward zero; callers only pass values
+// that are exactly representable, so the rounding mode never matters)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
 template <int B>
 __device__ __forceinline__ half2_t fp4x2(uint32_t word) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, B);
 }
+
+// Activation block-scale byte -> f32 (OCP E4M3, exact).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) { return __builtin_amdgcn_cvt_pk_f32_fp8(byte, false)[0]; }
 
 // 8 activation elements (4 bytes of codes) -> 4 half2 of E2M1 * block scale.
 __device__ __forceinline__ uint4 act_decode8(uint32_t word, float sa) {
@@ -95,7 +126,7 @@ __device__ __forceinline__ uint4 act_decode8(uint32_t word, float sa) {
     if (b == 3) f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
     // both products are exact and representable in f16, so the rounding
     // mode of the conversion does not matter
-    out[b] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0] * sa, f[1] * sa));
+    out[b] = pack_f16x2(f[0] * sa, f[1] * sa);
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
@@ -110,12 +141,201 @@ __device__ __forceinline__ float dot8(uint32_t wword, const uint4& a, float t) {
   return t;
 }
 
+// 8 weight codes times one block scale (f16 pair, both halves equal) -> half8.
+// E2M1 * E4M3 is exact in f16, so the packed multiply is exact.
+__device__ __forceinline__ half8_t wdecode8_scaled(uint32_t word, half2_t s) {
+  const half2_t a = fp4x2<0>(word) * s, b = fp4x2<1>(word) * s;
+  const half2_t c = fp4x2<2>(word) * s, d = fp4x2<3>(word) * s;
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-template <int MT, int G, int R, int NW, bool EPI>
-__global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvParams p) {
+// ----------------------------------------------------------------------------
+// LM-head epilogue, shared by both kernels.  Every thread passes NV values
+// with their token index and a validity flag.
+// ----------------------------------------------------------------------------
+
+// Device-scope (agent) relaxed atomic store / load: on gfx950 these are
+// written through to, and read from, the device coherence point, so no
+// whole-L2 write-back is needed to publish them to other workgroups.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MT, int NW>
+struct EpiSmem {
+  float wred[NW][MT][2];
+  float gmax[MT];
+  float mred[NW * 64];
+  float sred[NW * 64];
+  float tred[NW * 64];
+  unsigned last;
+};
+
+template <int MT, int NW, int NV>
+__device__ void lmhead_epilogue(const GemvParams& p, const float (&val)[NV], const int (&tok)[NV],
+                                const bool (&ok)[NV], EpiSmem<MT, NW>& sm, int64_t tile, int ntiles) {
+  constexpr int NT = NW * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // ---- tile maximum per token ----
+  float mx[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    mx[m] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (ok[i] && tok[i] == m) mx[m] = fmaxf(mx[m], val[i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], o, 64));
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) sm.wred[wave][m][0] = mx[m];
+  __syncthreads();
+  if (threadIdx.x < MT) {
+    float v = -INFINITY;
+    for (int w = 0; w < NW; ++w) v = fmaxf(v, sm.wred[w][threadIdx.x][0]);
+    sm.gmax[threadIdx.x] = v;
+  }
+  __syncthreads();
+  // ---- tile sums S = sum e^(z-max), T = sum e^(z-max)(z-max) per token ----
+  float S[MT], T[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    S[m] = 0.0f;
+    T[m] = 0.0f;
+    const float gm = sm.gmax[m];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (ok[i] && tok[i] == m) {
+        const float d = val[i] - gm;
+        const float e = expf(d);
+        S[m] += e;
+        T[m] = __builtin_fmaf(e, d, T[m]);
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      S[m] += __shfl_xor(S[m], o, 64);
+      T[m] += __shfl_xor(T[m], o, 64);
+    }
+  }
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      sm.wred[wave][m][0] = S[m];
+      sm.wred[wave][m][1] = T[m];
+    }
+  __syncthreads();
+  if (threadIdx.x < MT) {
+    float s = 0.0f, t = 0.0f;
+    for (int w = 0; w < NW; ++w) {
+      s += sm.wred[w][threadIdx.x][0];
+      t += sm.wred[w][threadIdx.x][1];
+    }
+    float* dst = p.partials + (tile * MT + threadIdx.x) * 3;
+    st_agent(dst, sm.gmax[threadIdx.x]);
+    st_agent(dst + 1, s);
+    st_agent(dst + 2, t);
+  }
+  // ---- the last workgroup to finish merges all partials ----
+  // The partials were written through to the device coherence point; wait
+  // until those stores have completed, then count this workgroup in.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm.last = (__hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (unsigned)ntiles - 1u)
+                  ? 1u
+                  : 0u;
+  __syncthreads();
+  if (!sm.last) return;
+  const int nwg = ntiles;
+  for (int m = 0; m < p.M; ++m) {
+    float gm = -INFINITY;
+    for (int b = threadIdx.x; b < nwg; b += NT)
+      gm = fmaxf(gm, ld_agent(p.partials + ((int64_t)b * MT + m) * 3));
+    sm.mred[threadIdx.x] = gm;
+    __syncthreads();
+    for (int s = NT / 2; s >= 1; s >>= 1) {
+      if (threadIdx.x < s) sm.mred[threadIdx.x] = fmaxf(sm.mred[threadIdx.x], sm.mred[threadIdx.x + s]);
+      __syncthreads();
+    }
+    gm = sm.mred[0];
+    // S = sum_b S_b e^(m_b - gm);  T = sum_b e^(m_b - gm) (T_b + (m_b - gm) S_b)
+    float Sm = 0.0f, Tm = 0.0f;
+    for (int b = threadIdx.x; b < nwg; b += NT) {
+      const float* src = p.partials + ((int64_t)b * MT + m) * 3;
+      const float mb = ld_agent(src);
+      const float Sb = ld_agent(src + 1);
+      const float Tb = ld_agent(src + 2);
+      if (mb == -INFINITY) continue;
+      const float d = mb - gm;
+      const float f = expf(d);
+      Sm = __builtin_fmaf(Sb, f, Sm);
+      Tm = __builtin_fmaf(f, __builtin_fmaf(d, Sb, Tb), Tm);
+    }
+    __syncthreads();
+    sm.sred[threadIdx.x] = Sm;
+    sm.tred[threadIdx.x] = Tm;
+    __syncthreads();
+    for (int s = NT / 2; s >= 1; s >>= 1) {
+      if (threadIdx.x < s) {
+        sm.sred[threadIdx.x] += sm.sred[threadIdx.x + s];
+        sm.tred[threadIdx.x] += sm.tred[threadIdx.x + s];
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      const double Sd = sm.sred[0], Td = sm.tred[0];
+      const float H = (float)(log(Sd) - Td / Sd);
+      p.epi.entropy[m] = H;
+      // ---- ReSET update: update with H first, then decide ----
+      ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
+      float* ring = reinterpret_cast<float*>(st + 1);
+      // the ring holds the window the state was initialised with; never
+      // index past the smaller of that and the caller's window
+      int w = st->window < p.epi.window ? st->window : p.epi.window;
+      if (w < 1) w = 1;
+      const double h = (double)H;
+      if (st->count == 0 || p.epi.step_start[m]) {
+        st->step_sum = 0.0;
+        st->step_len = 0;
+      }
+      ring[st->count % w] = H;
+      st->count += 1;
+      st->sum_all += h;
+      st->step_sum += h;
+      st->step_len += 1;
+      const int64_t nwin = st->count < w ? st->count : w;
+      double wsum = 0.0;
+      for (int64_t i = st->count - nwin; i < st->count; ++i) wsum += (double)ring[i % w];
+      const double hbar = st->sum_all / (double)st->count;
+      const double hstep = st->step_len <= w ? wsum / (double)nwin : st->step_sum / (double)st->step_len;
+      const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
+      float T_t;
+      if (p.epi.mode == 1) T_t = p.epi.t_base;
+      else T_t = h < tau ? p.epi.t_low : p.epi.t_high;
+      p.epi.temperature[m] = T_t;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0)  // ready for the next call / graph replay
+    __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------------------
+// VALU kernel
+// ----------------------------------------------------------------------------
+
+template <int MT, int G, int R, int NW, int P, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_valu_kernel(GemvParams p) {
   extern __shared__ uint4 lds[];  // activation phase [MT][4][C] of 16 bytes
   constexpr int RG = 64 / G;      // row-groups per wave
   constexpr int ROWS = R * NW * RG;
@@ -145,7 +365,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvParams p) {
     for (int m = 0; m < MT; ++m) acc[r][m][0] = acc[r][m][1] = 0.0f;
 
   for (int64_t kb = 0; kb < K; kb += p.kp) {
-    const int C = (int)((K - kb < p.kp ? K - kb : p.kp) / 32);  // chunks in this phase
+    const int C = (int)((K - kb < p.kp ? K - kb : p.kp) / 32);  // 32-element chunks in this phase
+    const int n = g < C ? (C - g + G - 1) / G : 0;              // chunks of this lane: g, g+G, ...
     const uint8_t* wcp[R];
     const uint8_t* wsp[R];
 #pragma unroll
@@ -153,16 +374,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvParams p) {
       wcp[r] = wc[r] + kb / 2;
       wsp[r] = ws[r] + kb / 16;
     }
-    // first weight chunk of the phase, in flight while the activation is staged
-    uint4 wn[R];
-    uint32_t sn[R];
-    if (g < C) {
+    // the first P chunks go in flight before the activation is staged
+    uint4 wb[P][R];
+    uint32_t sbuf[P][R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        wn[r] = *reinterpret_cast<const uint4*>(wcp[r] + g * 16);
-        sn[r] = *reinterpret_cast<const uint16_t*>(wsp[r] + g * 2);
-      }
-    }
+    for (int j = 0; j < P; ++j)
+      if (j < n)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int c = g + j * G;
+          wb[j][r] = *reinterpret_cast<const uint4*>(wcp[r] + c * 16);
+          sbuf[j][r] = *reinterpret_cast<const uint16_t*>(wsp[r] + c * 2);
+        }
     __syncthreads();  // the previous phase is done with the LDS tile
     for (int it = threadIdx.x; it < MT * 4 * C; it += NW * 64) {
       const int m = it / (4 * C);
@@ -173,53 +396,59 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvParams p) {
       if (m < M) {
         const int64_t k = kb + (int64_t)c * 32 + q * 8;
         const uint32_t word = *reinterpret_cast<const uint32_t*>(p.a_codes + (int64_t)m * (K / 2) + k / 2);
-        const uint32_t sb = p.a_scales[(int64_t)m * (K / 16) + k / 16];
-        const float sa = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false)[0];
-        v = act_decode8(word, sa);
+        v = act_decode8(word, e4m3_to_f32(p.a_scales[(int64_t)m * (K / 16) + k / 16]));
       }
       lds[(m * 4 + q) * C + c] = v;
     }
     __syncthreads();
 
-    for (int c = g; c < C; c += G) {
-      uint4 w[R];
-      uint32_t s[R];
+    for (int i0 = 0; i0 < n; i0 += P) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        w[r] = wn[r];
-        s[r] = sn[r];
-      }
-      if (c + G < C) {
+      for (int j = 0; j < P; ++j) {
+        const int i = i0 + j;
+        if (i < n) {
+          const int c = g + i * G;
+          uint4 w[R];
+          uint32_t s[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          wn[r] = *reinterpret_cast<const uint4*>(wcp[r] + (c + G) * 16);
-          sn[r] = *reinterpret_cast<const uint16_t*>(wsp[r] + (c + G) * 2);
-        }
-      }
-      float t[R][MT][2];
+          for (int r = 0; r < R; ++r) {
+            w[r] = wb[j][r];
+            s[r] = sbuf[j][r];
+          }
+          if (i + P < n) {
+            const int cn = c + P * G;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+            for (int r = 0; r < R; ++r) {
+              wb[j][r] = *reinterpret_cast<const uint4*>(wcp[r] + cn * 16);
+              sbuf[j][r] = *reinterpret_cast<const uint16_t*>(wsp[r] + cn * 2);
+            }
+          }
+          float t[R][MT][2];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) t[r][m][0] = t[r][m][1] = 0.0f;
+          for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint4 a[MT];
+            for (int m = 0; m < MT; ++m) t[r][m][0] = t[r][m][1] = 0.0f;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) a[m] = lds[(m * 4 + q) * C + c];
+          for (int q = 0; q < 4; ++q) {
+            uint4 a[MT];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t ww = word_of(w[r], q);
+            for (int m = 0; m < MT; ++m) a[m] = lds[(m * 4 + q) * C + c];
 #pragma unroll
-          for (int m = 0; m < MT; ++m) t[r][m][q >> 1] = dot8(ww, a[m], t[r][m][q >> 1]);
-        }
-      }
+            for (int r = 0; r < R; ++r) {
+              const uint32_t ww = word_of(w[r], q);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float2_t sw = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
+              for (int m = 0; m < MT; ++m) t[r][m][q >> 1] = dot8(ww, a[m], t[r][m][q >> 1]);
+            }
+          }
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          acc[r][m][0] = __builtin_fmaf(t[r][m][0], sw[0], acc[r][m][0]);
-          acc[r][m][1] = __builtin_fmaf(t[r][m][1], sw[1], acc[r][m][1]);
+          for (int r = 0; r < R; ++r) {
+            const float2_t sw = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              acc[r][m][0] = __builtin_fmaf(t[r][m][0], sw[0], acc[r][m][0]);
+              acc[r][m][1] = __builtin_fmaf(t[r][m][1], sw[1], acc[r][m][1]);
+            }
+          }
         }
       }
     }
@@ -227,7 +456,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvParams p) {
 
   // reduce the G lanes of each row-group
   const float scale = (*p.a_gscale) * (*p.w_gscale);
-  float out[R][MT];
+  float out[R * MT];
+  int tok[R * MT];
+  bool ok[R * MT];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -235,154 +466,329 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(GemvParams p) {
       float v = acc[r][m][0] + acc[r][m][1];
 #pragma unroll
       for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-      out[r][m] = v * scale;
+      out[r * MT + m] = v * scale;
+      tok[r * MT + m] = m;
+      ok[r * MT + m] = g == 0 && row[r] < N && m < M;
     }
-  if (g == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (row[r] < N)
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-          if (m < M) p.y[(int64_t)m * N + row[r]] = out[r][m];
-  }
+    for (int m = 0; m < MT; ++m)
+      if (ok[r * MT + m]) p.y[(int64_t)m * N + row[r]] = out[r * MT + m];
 
   if constexpr (EPI) {
-    // ---- per-workgroup softmax partials of this tile's logits ----
-    __shared__ float red[NW * RG][MT][3];
-    __shared__ float fin[MT][3];
-    __shared__ unsigned last;
-    float mx[MT];
+    __shared__ EpiSmem<MT, NW> sm;
+    lmhead_epilogue<MT, NW, R * MT>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Direct VALU kernel (M <= 2): no LDS, activation decoded in registers
+// ----------------------------------------------------------------------------
+
+template <int MT, int G, int R, int NW, int P, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
+  constexpr int RG = 64 / G;
+  constexpr int ROWS = R * NW * RG;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % G;
+  const int rg = lane / G;
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * ROWS;
+
+  const uint8_t* wc[R];
+  const uint8_t* ws[R];
+  int64_t row[R];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = -INFINITY;
+  for (int r = 0; r < R; ++r) {
+    row[r] = tile0 + (int64_t)(r * NW + wave) * RG + rg;
+    const int64_t rr = row[r] < N ? row[r] : N - 1;  // clamp: loads stay in bounds
+    wc[r] = p.w_codes + rr * (K / 2);
+    ws[r] = p.w_scales + rr * (K / 16);
+  }
+  const uint8_t* ac[MT];
+  const uint8_t* as[MT];
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (row[r] < N) v = fmaxf(v, out[r][m]);
-      mx[m] = v;
-    }
-    const int slot = wave * RG + rg;
-    if (g == 0)
+  for (int m = 0; m < MT; ++m) {
+    const int mm = m < M ? m : M - 1;  // tokens >= M reuse a valid row; their sums are never stored
+    ac[m] = p.a_codes + (int64_t)mm * (K / 2);
+    as[m] = p.a_scales + (int64_t)mm * (K / 16);
+  }
+
+  float acc[R][MT][2];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) red[slot][m][0] = mx[m];
-    __syncthreads();
-    if (threadIdx.x < MT) {
-      float v = -INFINITY;
-      for (int s = 0; s < NW * RG; ++s) v = fmaxf(v, red[s][threadIdx.x][0]);
-      fin[threadIdx.x][0] = v;
-    }
-    __syncthreads();
-    if (g == 0) {
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m][0] = acc[r][m][1] = 0.0f;
+
+  const int C = (int)(K / 32);                    // 32-element chunks per row
+  const int n = g < C ? (C - g + G - 1) / G : 0;  // chunks of this lane: g, g+G, ...
+  uint4 wb[P][R], ab[P][MT];
+  uint32_t sb[P][R], asb[P][MT];
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (j < n) {
+      const int c = g + j * G;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        wb[j][r] = *reinterpret_cast<const uint4*>(wc[r] + c * 16);
+        sb[j][r] = *reinterpret_cast<const uint16_t*>(ws[r] + c * 2);
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const float gm = fin[m][0];
-        float S = 0.0f, T = 0.0f;
+        ab[j][m] = *reinterpret_cast<const uint4*>(ac[m] + c * 16);
+        asb[j][m] = *reinterpret_cast<const uint16_t*>(as[m] + c * 2);
+      }
+    }
+  for (int i0 = 0; i0 < n; i0 += P) {
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          if (row[r] < N) {
-            const float d = out[r][m] - gm;
-            const float e = expf(d);
-            S += e;
-            T = __builtin_fmaf(e, d, T);
+    for (int j = 0; j < P; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        uint4 w[R], a[MT];
+        uint32_t s[R], sa[MT];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          w[r] = wb[j][r];
+          s[r] = sb[j][r];
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          a[m] = ab[j][m];
+          sa[m] = asb[j][m];
+        }
+        if (i + P < n) {
+          const int cn = g + (i + P) * G;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            wb[j][r] = *reinterpret_cast<const uint4*>(wc[r] + cn * 16);
+            sb[j][r] = *reinterpret_cast<const uint16_t*>(ws[r] + cn * 2);
           }
-        red[slot][m][1] = S;
-        red[slot][m][2] = T;
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x < MT) {
-      float S = 0.0f, T = 0.0f;
-      for (int s = 0; s < NW * RG; ++s) {
-        S += red[s][threadIdx.x][1];
-        T += red[s][threadIdx.x][2];
-      }
-      float* dst = p.partials + ((int64_t)blockIdx.x * MT + threadIdx.x) * 3;
-      dst[0] = fin[threadIdx.x][0];
-      dst[1] = S;
-      dst[2] = T;
-    }
-    // ---- the last workgroup merges ----
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last = (atomicAdd(p.counter, 1u) == gridDim.x - 1) ? 1u : 0u;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const int nwg = gridDim.x;
-    constexpr int NT = NW * 64;
-    __shared__ float mred[NT];
-    __shared__ float sred[NT];
-    __shared__ float tred[NT];
-    for (int m = 0; m < M; ++m) {
-      // global max
-      float gm = -INFINITY;
-      for (int b = threadIdx.x; b < nwg; b += NT)
-        gm = fmaxf(gm, __builtin_nontemporal_load(p.partials + ((int64_t)b * MT + m) * 3));
-      mred[threadIdx.x] = gm;
-      __syncthreads();
-      for (int s = NT / 2; s >= 1; s >>= 1) {
-        if (threadIdx.x < s) mred[threadIdx.x] = fmaxf(mred[threadIdx.x], mred[threadIdx.x + s]);
-        __syncthreads();
-      }
-      gm = mred[0];
-      // rescaled sums: S = sum_b S_b e^(m_b - gm); T = sum_b e^(m_b - gm) (T_b + (m_b - gm) S_b)
-      float S = 0.0f, T = 0.0f;
-      for (int b = threadIdx.x; b < nwg; b += NT) {
-        const float* src = p.partials + ((int64_t)b * MT + m) * 3;
-        const float mb = __builtin_nontemporal_load(src);
-        const float Sb = __builtin_nontemporal_load(src + 1);
-        const float Tb = __builtin_nontemporal_load(src + 2);
-        if (mb == -INFINITY) continue;
-        const float d = mb - gm;
-        const float f = expf(d);
-        S = __builtin_fmaf(Sb, f, S);
-        T = __builtin_fmaf(f, __builtin_fmaf(d, Sb, Tb), T);
-      }
-      __syncthreads();
-      sred[threadIdx.x] = S;
-      tred[threadIdx.x] = T;
-      __syncthreads();
-      for (int s = NT / 2; s >= 1; s >>= 1) {
-        if (threadIdx.x < s) {
-          sred[threadIdx.x] += sred[threadIdx.x + s];
-          tred[threadIdx.x] += tred[threadIdx.x + s];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            ab[j][m] = *reinterpret_cast<const uint4*>(ac[m] + cn * 16);
+            asb[j][m] = *reinterpret_cast<const uint16_t*>(as[m] + cn * 2);
+          }
         }
-        __syncthreads();
-      }
-      if (threadIdx.x == 0) {
-        const double Sd = sred[0], Td = tred[0];
-        const double H = log(Sd) - Td / Sd;
-        p.epi.entropy[m] = (float)H;
-        // ---- ReSET update: update with H first, then decide ----
-        ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
-        float* ring = reinterpret_cast<float*>(st + 1);
-        // the ring holds the window the state was initialised with; never
-        // index past the smaller of that and the caller's window
-        int w = st->window < p.epi.window ? st->window : p.epi.window;
-        if (w < 1) w = 1;
-        const double h = (double)(float)H;
-        if (st->count == 0 || p.epi.step_start[m]) {
-          st->step_sum = 0.0;
-          st->step_len = 0;
+        // activation: 32 E2M1 values as f16 pairs, and its two block scales
+        half2_t ah[MT][16];
+        float2_t saf[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = word_of(a[m], q);
+            ah[m][4 * q + 0] = fp4x2<0>(word);
+            ah[m][4 * q + 1] = fp4x2<1>(word);
+            ah[m][4 * q + 2] = fp4x2<2>(word);
+            ah[m][4 * q + 3] = fp4x2<3>(word);
+          }
+          saf[m] = __builtin_amdgcn_cvt_pk_f32_fp8(sa[m], false);
         }
-        ring[st->count % w] = (float)H;
-        st->count += 1;
-        st->sum_all += h;
-        st->step_sum += h;
-        st->step_len += 1;
-        const int64_t nwin = st->count < w ? st->count : w;
-        double wsum = 0.0;
-        for (int64_t i = st->count - nwin; i < st->count; ++i) wsum += (double)ring[i % w];
-        const double hbar = st->sum_all / (double)st->count;
-        const double hstep = st->step_len <= w ? wsum / (double)nwin : st->step_sum / (double)st->step_len;
-        const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
-        float T_t;
-        if (p.epi.mode == 1) T_t = p.epi.t_base;
-        else T_t = h < tau ? p.epi.t_low : p.epi.t_high;
-        p.epi.temperature[m] = T_t;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float2_t sw = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
+          half2_t wh[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = word_of(w[r], q);
+            wh[4 * q + 0] = fp4x2<0>(word);
+            wh[4 * q + 1] = fp4x2<1>(word);
+            wh[4 * q + 2] = fp4x2<2>(word);
+            wh[4 * q + 3] = fp4x2<3>(word);
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              t0 = __builtin_amdgcn_fdot2(wh[k], ah[m][k], t0, false);
+              t1 = __builtin_amdgcn_fdot2(wh[8 + k], ah[m][8 + k], t1, false);
+            }
+            acc[r][m][0] = __builtin_fmaf(t0, saf[m][0] * sw[0], acc[r][m][0]);
+            acc[r][m][1] = __builtin_fmaf(t1, saf[m][1] * sw[1], acc[r][m][1]);
+          }
+        }
       }
-      __syncthreads();
     }
-    if (threadIdx.x == 0) *p.counter = 0u;  // ready for the next call / graph replay
+  }
+
+  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  float out[R * MT];
+  int tok[R * MT];
+  bool ok[R * MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = acc[r][m][0] + acc[r][m][1];
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+      out[r * MT + m] = v * scale;
+      tok[r * MT + m] = m;
+      ok[r * MT + m] = g == 0 && row[r] < N && m < M;
+    }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (ok[r * MT + m]) p.y[(int64_t)m * N + row[r]] = out[r * MT + m];
+
+  if constexpr (EPI) {
+    __shared__ EpiSmem<MT, NW> sm;
+    lmhead_epilogue<MT, NW, R * MT>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// MFMA-assisted kernel
+// ----------------------------------------------------------------------------
+
+template <int MT, int R, int NW, int P, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(GemvParams p) {
+  extern __shared__ uint4 lds4[];  // [NW][R][4][64] partial tiles at the end
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15;   // row of the A operand / column (token) of B and D
+  const int kg = lane >> 4;   // k group: elements 64*kg .. 64*kg+63 of a 256-step
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int nsteps = (int)((K + 255) / 256);
+  const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps of this wave: wave, wave+NW, ...
+  (void)MT;
+
+  const uint8_t* wc[R];
+  const uint8_t* ws[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t rr = tile0 + 16 * r + li;
+    rr = rr < N ? rr : N - 1;  // clamp: loads stay in bounds
+    wc[r] = p.w_codes + rr * (K / 2);
+    ws[r] = p.w_scales + rr * (K / 16);
+  }
+  // activation row fed to B column li (columns >= M read a valid row; ignored)
+  const int btok = li < M ? li : M - 1;
+  const uint8_t* ac = p.a_codes + (int64_t)btok * (K / 2);
+  const uint8_t* as = p.a_scales + (int64_t)btok * (K / 16);
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // one step = 256 elements of K: lane (li, kg) holds 64 codes (32 bytes, 4
+  // blocks) of its weight rows and of its activation row
+  uint4 wb[P][R][2], ab[P][2];
+  uint32_t sbuf[P][R], asb[P];
+  auto load = [&](int slot, int step) {
+    const int64_t e = (int64_t)step * 256 + 64 * kg;  // first element of this lane
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t eh = e + 32 * h;  // K % 32 == 0: a 32-element half is all in or all out
+      const bool in = eh < K;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        wb[slot][r][h] = in ? *reinterpret_cast<const uint4*>(wc[r] + eh / 2) : make_uint4(0, 0, 0, 0);
+      ab[slot][h] = in ? *reinterpret_cast<const uint4*>(ac + eh / 2) : make_uint4(0, 0, 0, 0);
+    }
+    // four block scales; the second pair only when the second half is inside
+    const bool in0 = e < K, in1 = e + 32 < K;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      sbuf[slot][r] = in1 ? *reinterpret_cast<const uint32_t*>(ws[r] + e / 16)
+                          : (in0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(ws[r] + e / 16) : 0u);
+    asb[slot] = in1 ? *reinterpret_cast<const uint32_t*>(as + e / 16)
+                    : (in0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(as + e / 16) : 0u);
+  };
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (j < n) load(j, wave + j * NW);
+
+  for (int i0 = 0; i0 < n; i0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        uint4 w[R][2];
+        uint32_t s[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          w[r][0] = wb[j][r][0];
+          w[r][1] = wb[j][r][1];
+          s[r] = sbuf[j][r];
+        }
+        const uint4 a0 = ab[j][0], a1 = ab[j][1];
+        const uint32_t sa = asb[j];
+        if (i + P < n) load(j, wave + (i + P) * NW);
+        // B operands: E2M1 * E4M3 of the activation, exact in f16
+        const float2_t sa01 = __builtin_amdgcn_cvt_pk_f32_fp8(sa, false);
+        const float2_t sa23 = __builtin_amdgcn_cvt_pk_f32_fp8(sa, true);
+        const half2_t h0 = as_half2(pack_f16x2(sa01[0], sa01[0]));
+        const half2_t h1 = as_half2(pack_f16x2(sa01[1], sa01[1]));
+        const half2_t h2 = as_half2(pack_f16x2(sa23[0], sa23[0]));
+        const half2_t h3 = as_half2(pack_f16x2(sa23[1], sa23[1]));
+        const half8_t b[8] = {wdecode8_scaled(a0.x, h0), wdecode8_scaled(a0.y, h0), wdecode8_scaled(a0.z, h1),
+                              wdecode8_scaled(a0.w, h1), wdecode8_scaled(a1.x, h2), wdecode8_scaled(a1.y, h2),
+                              wdecode8_scaled(a1.z, h3), wdecode8_scaled(a1.w, h3)};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          // weight block scales of this lane's four blocks, as f16 pairs (exact)
+          const float2_t sw01 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
+          const float2_t sw23 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], true);
+          const half2_t s0 = as_half2(pack_f16x2(sw01[0], sw01[0]));
+          const half2_t s1 = as_half2(pack_f16x2(sw01[1], sw01[1]));
+          const half2_t s2 = as_half2(pack_f16x2(sw23[0], sw23[0]));
+          const half2_t s3 = as_half2(pack_f16x2(sw23[1], sw23[1]));
+          float4_t d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].x, s0), b[0], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].y, s0), b[1], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].z, s1), b[2], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].w, s1), b[3], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].x, s2), b[4], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].y, s2), b[5], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].z, s3), b[6], d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].w, s3), b[7], d, 0, 0, 0);
+          acc[r] += d;
+        }
+      }
+    }
+  }
+
+  // add the NW waves' partial tiles in a fixed order
+  float* red = reinterpret_cast<float*>(lds4);  // [NW][R][4][64]
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
+  __syncthreads();
+  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  // wave w finalizes the (r, v) register slots w, w + NW, ...; D layout:
+  // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token li
+  constexpr int NV = (R * 4 + NW - 1) / NW;
+  float out[NV];
+  int tok[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int rv = wave + u * NW;
+    out[u] = 0.0f;
+    tok[u] = li;
+    ok[u] = false;
+    if (rv < R * 4) {
+      const int r = rv >> 2, v = rv & 3;
+      float sum = 0.0f;
+      for (int w = 0; w < NW; ++w) sum += red[((w * R + r) * 4 + v) * 64 + lane];
+      const int64_t row = tile0 + 16 * r + 4 * kg + v;
+      out[u] = sum * scale;
+      ok[u] = li < M && row < N;
+      if (ok[u]) p.y[(int64_t)li * N + row] = out[u];
+    }
+  }
+  if constexpr (EPI) {
+    __shared__ EpiSmem<MT, NW> sm;
+    lmhead_epilogue<MT, NW, NV>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
   }
 }
 
@@ -401,24 +807,79 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
   }
 }
 
-template <int MT, int G, int R, int NW>
-hipError_t launch_one(const GemvConfig& cfg, const GemvParams& p, hipStream_t stream, bool epi) {
-  const size_t lds_bytes = (size_t)MT * 4 * (cfg.kp / 32) * 16;
-  if (epi)
-    hipLaunchKernelGGL((gemv_kernel<MT, G, R, NW, true>), dim3((unsigned)cfg.grid), dim3(NW * 64), lds_bytes,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((gemv_kernel<MT, G, R, NW, false>), dim3((unsigned)cfg.grid), dim3(NW * 64), lds_bytes,
-                       stream, p);
-  return hipGetLastError();
+// ----------------------------------------------------------------------------
+// Variant table
+// ----------------------------------------------------------------------------
+
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2 };
+
+struct Variant {
+  const char* name;
+  Kind kind;
+  int mt, g, r, nw, p;
+  void (*plain)(GemvParams);
+  void (*epi)(GemvParams);
+};
+
+#define VALU_V(MT, G, R, NW, P)                                                              \
+  Variant {                                                                                \
+    "valu_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, VALU, MT, G, R, NW, P,                 \
+        gemv_valu_kernel<MT, G, R, NW, P, false>, gemv_valu_kernel<MT, G, R, NW, P, true> \
+  }
+#define DIRECT_V(MT, G, R, NW, P)                                                                \
+  Variant {                                                                                    \
+    "direct_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, DIRECT, MT, G, R, NW, P,                 \
+        gemv_direct_kernel<MT, G, R, NW, P, false>, gemv_direct_kernel<MT, G, R, NW, P, true> \
+  }
+#define MFMA_V(MT, R, NW, P)                                                            \
+  Variant {                                                                           \
+    "mfma_m" #MT "_r" #R "_w" #NW "_p" #P, MFMA, MT, 16, R, NW, P,                   \
+        gemv_mfma_kernel<MT, R, NW, P, false>, gemv_mfma_kernel<MT, R, NW, P, true>  \
+  }
+
+const Variant kVariants[] = {
+    // direct VALU (no LDS), one and two tokens
+    DIRECT_V(1, 16, 1, 4, 1), DIRECT_V(1, 16, 2, 4, 1), DIRECT_V(1, 32, 1, 4, 1), DIRECT_V(1, 32, 2, 4, 1),
+    DIRECT_V(1, 64, 1, 4, 1), DIRECT_V(1, 16, 1, 4, 2), DIRECT_V(1, 8, 2, 4, 1), DIRECT_V(1, 16, 4, 4, 1),
+    DIRECT_V(2, 16, 1, 4, 1), DIRECT_V(2, 16, 2, 4, 1), DIRECT_V(2, 32, 1, 4, 1), DIRECT_V(2, 64, 1, 4, 1),
+    // LDS VALU, any M
+    VALU_V(1, 16, 2, 4, 1), VALU_V(2, 16, 2, 4, 1), VALU_V(4, 16, 2, 4, 1), VALU_V(8, 16, 1, 4, 1),
+    VALU_V(8, 16, 2, 4, 1),
+    // MFMA-assisted (the compiled token count only sizes the epilogue)
+    MFMA_V(2, 1, 4, 1), MFMA_V(2, 2, 8, 1), MFMA_V(2, 1, 8, 2), MFMA_V(4, 1, 4, 1), MFMA_V(4, 2, 8, 1),
+    MFMA_V(4, 1, 8, 2), MFMA_V(8, 1, 4, 1), MFMA_V(8, 1, 8, 1), MFMA_V(8, 2, 4, 1), MFMA_V(8, 2, 8, 1),
+    MFMA_V(8, 1, 4, 2), MFMA_V(8, 1, 8, 2), MFMA_V(8, 2, 8, 2), MFMA_V(8, 1, 16, 1),
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+int find_variant(const char* name) {
+  for (int i = 0; i < kNumVariants; ++i)
+    if (strcmp(kVariants[i].name, name) == 0) return i;
+  return -1;
 }
 
-template <int MT>
-hipError_t launch_mt(const GemvConfig& cfg, const GemvParams& p, hipStream_t stream, bool epi) {
-  if (cfg.g == 16 && cfg.r == 1 && cfg.waves == 4) return launch_one<MT, 16, 1, 4>(cfg, p, stream, epi);
-  if (cfg.g == 16 && cfg.r == 2 && cfg.waves == 4) return launch_one<MT, 16, 2, 4>(cfg, p, stream, epi);
-  return hipErrorInvalidConfiguration;
+// Default variant per (M, N, K): the fastest variant of an MI355X sweep over
+// the Qwen3-8B/32B projection and LM-head shapes (back-to-back launches,
+// weights rotated past the Infinity Cache), generalised by N and K.
+int default_variant(int M, int64_t N, int64_t K, bool epi) {
+  (void)epi;
+  const char* name;
+  switch (mt_of(M)) {
+    case 1:
+      name = N >= 16384 ? "direct_m1_g32_r2_w4_p1" : K >= 12288 ? "direct_m1_g64_r1_w4_p1" : "direct_m1_g32_r1_w4_p1";
+      break;
+    case 2:
+      name = N >= 16384 ? "direct_m2_g16_r2_w4_p1" : K >= 8192 ? "direct_m2_g64_r1_w4_p1" : "direct_m2_g32_r1_w4_p1";
+      break;
+    case 4: name = N >= 8192 && K < 8192 ? "mfma_m4_r1_w4_p1" : "mfma_m4_r2_w8_p1"; break;
+    default: name = N >= 8192 && K < 8192 ? "mfma_m8_r1_w8_p1" : "mfma_m8_r2_w8_p1"; break;
+  }
+  return find_variant(name);
 }
+
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
 
@@ -428,33 +889,61 @@ size_t reset_state_bytes(int window) {
 }
 
 GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
+  int vi = -1;
+  // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
+  // compiled token count covers M
+  if (const char* env = getenv("NVFP4_GEMV_VARIANT")) {
+    const int i = find_variant(env);
+    if (i >= 0 && kVariants[i].mt >= M) vi = i;
+  }
+  if (vi < 0) vi = default_variant(M, N, K, epi);
+  const Variant& v = kVariants[vi];
   GemvConfig c{};
-  c.mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
-  c.g = 16;
-  c.waves = 4;
-  c.r = N >= 16384 ? 2 : 1;
-  // LDS phase: at most 64 KiB of f16 activation per workgroup (48 KiB when
-  // the epilogue's reduction buffers share the LDS), in whole rounds of G
-  // chunks when K allows it
-  int64_t kp = (epi ? (int64_t)24576 : (int64_t)32768) / c.mt;
-  const int64_t unit = (int64_t)32 * c.g;
-  if (kp >= unit) kp = kp / unit * unit;
-  if (kp > K) kp = K;
-  c.kp = (int)kp;
-  c.rows_per_wg = (int64_t)c.r * c.waves * (64 / c.g);
-  c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
+  c.variant = vi;
+  c.mt = v.mt;
+  c.g = v.g;
+  c.r = v.r;
+  c.waves = v.nw;
+  // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
+  // when the epilogue's reduction buffers share the LDS
+  const int64_t budget = epi ? 24576 : 32768;
+  if (v.kind == MFMA) {
+    c.kp = (int)K;
+    c.rows_per_wg = (int64_t)16 * v.r;
+    c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
+    c.lds_bytes = (int64_t)v.nw * v.r * 4 * 64 * 4;
+  } else if (v.kind == VALU) {
+    int64_t kp = budget / v.mt / 512 * 512;
+    const int64_t kr = (K + 127) / 128 * 128;
+    if (kp > kr) kp = kr;
+    c.kp = (int)kp;
+    c.rows_per_wg = (int64_t)v.r * v.nw * (64 / v.g);
+    c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
+    c.lds_bytes = (int64_t)v.mt * kp * 2;
+  } else {
+    c.kp = (int)K;
+    c.rows_per_wg = (int64_t)v.r * v.nw * (64 / v.g);
+    c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
+    c.lds_bytes = 0;
+  }
+  // workspace (epilogue only): [counter | per-workgroup softmax partials]
+  c.ws_epi_partials = 256;
+  c.ws_bytes = epi ? c.ws_epi_partials + align256(c.grid * c.mt * 3 * 4) : 0;
   return c;
 }
 
-size_t lmhead_workspace_bytes(int M, int64_t N, int64_t K) {
-  const GemvConfig c = choose_gemv_config(M, N, K, true);
-  return 256 + (size_t)c.grid * c.mt * 3 * sizeof(float);
+const char* gemv_variant_name(int vi) { return vi >= 0 && vi < kNumVariants ? kVariants[vi].name : "?"; }
+const char* gemv_variant_by_index(int i) { return i >= 0 && i < kNumVariants ? kVariants[i].name : nullptr; }
+
+size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi) {
+  return (size_t)choose_gemv_config(M, N, K, epi).ws_bytes;
 }
 
 hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_gscale, const uint8_t* w_codes,
                        const uint8_t* w_scales, const float* w_gscale, float* y,
                        const EpilogueArgs* epi, void* ws, hipStream_t stream) {
+  if (cfg.variant < 0 || cfg.variant >= kNumVariants) return hipErrorInvalidConfiguration;
   GemvParams p{};
   p.M = M;
   p.N = N;
@@ -467,20 +956,17 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   p.w_scales = w_scales;
   p.w_gscale = w_gscale;
   p.y = y;
+  char* wsb = reinterpret_cast<char*>(ws);
   if (epi) {
     p.epi = *epi;
-    p.counter = reinterpret_cast<unsigned*>(ws);
-    p.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + 256);
+    p.counter = reinterpret_cast<unsigned*>(wsb);
+    p.partials = reinterpret_cast<float*>(wsb + cfg.ws_epi_partials);
     p.state_bytes = reset_state_bytes(epi->window);
   }
-  const bool e = epi != nullptr;
-  switch (cfg.mt) {
-    case 1: return launch_mt<1>(cfg, p, stream, e);
-    case 2: return launch_mt<2>(cfg, p, stream, e);
-    case 4: return launch_mt<4>(cfg, p, stream, e);
-    case 8: return launch_mt<8>(cfg, p, stream, e);
-  }
-  return hipErrorInvalidConfiguration;
+  const Variant& v = kVariants[cfg.variant];
+  void (*fn)(GemvParams) = epi ? v.epi : v.plain;
+  hipLaunchKernelGGL(fn, dim3((unsigned)cfg.grid), dim3(v.nw * 64), (size_t)cfg.lds_bytes, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_reset_state_init(void* state, int M, int window, hipStream_t stream) {

@@ -20,9 +20,10 @@ enum GsMode : int {
 // Number of amax partials the two-launch path uses for `elems` elements.
 int amax_partial_count(int64_t elems);
 
-// Activation quantization is done in one launch (GS_SELF) up to this many
-// elements, in two launches (amax partials, then quantize) above it.
-constexpr int64_t kActSelfAmaxMaxElems = 32768;
+// Activation quantization is done by one workgroup in one launch up to this
+// many elements, in two launches (parallel amax partials, then quantize)
+// above it.
+constexpr int64_t kActSelfAmaxMaxElems = 65536;
 
 // Launchers (no validation: the C-ABI layer has done it).
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
@@ -47,19 +48,27 @@ struct EpilogueArgs {
 // Launch configuration of the small-M GEMV, chosen per (M, N, K) on the
 // host and fixed for the life of a captured graph.
 struct GemvConfig {
+  int variant;     // index into the kernel variant table
   int mt;          // compiled token count (1, 2, 4 or 8) >= M
   int g;           // lanes per weight row
   int r;           // rows per lane
   int waves;       // waves per workgroup
   int kp;          // K elements per LDS phase
   int64_t rows_per_wg;
-  int64_t grid;
+  int64_t grid;       // workgroups (row tiles)
+  int64_t lds_bytes;  // dynamic LDS per workgroup
+  // workspace layout (byte offset of the epilogue partials) and total size
+  // (0 = none needed)
+  int64_t ws_epi_partials, ws_bytes;
 };
 
 GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi);
+const char* gemv_variant_name(int variant);
+const char* gemv_variant_by_index(int index);  // NULL past the end
 
-// Workspace bytes the LM-head epilogue needs for this shape.
-size_t lmhead_workspace_bytes(int M, int64_t N, int64_t K);
+// Workspace bytes the GEMV needs for this shape (with or without the
+// LM-head epilogue); 0 = none.
+size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi);
 size_t reset_state_bytes(int window);
 constexpr int kResetMaxWindow = 1024;
 

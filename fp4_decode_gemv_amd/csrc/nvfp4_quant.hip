@@ -58,13 +58,18 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
          (uint32_t)(a > 5.0f);
 }
 
-// Quantize one 16-element block.  Returns the block-scale code; writes the
-// 16 codes packed two per byte (element 2j in the low nibble) into c0/c1.
-__device__ __forceinline__ uint32_t quant_block(const float (&x)[16], float s_g, uint32_t& c0,
-                                                uint32_t& c1) {
+__device__ __forceinline__ float block_amax(const float (&x)[16]) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  return amax;
+}
+
+// Quantize one 16-element block whose max |x| is `amax`.  Returns the
+// block-scale code; writes the 16 codes packed two per byte (element 2j in
+// the low nibble) into c0/c1.
+__device__ __forceinline__ uint32_t quant_block(const float (&x)[16], float amax, float s_g, uint32_t& c0,
+                                                uint32_t& c1) {
   float t = 0.0f;
   if (s_g != 0.0f) {
     const float denom = 6.0f * s_g;
@@ -132,7 +137,8 @@ struct Loader<float> {
   }
 };
 
-// Max over a workgroup of kThreads threads; result valid in every thread.
+// Max over a workgroup of NT threads; result valid in every thread.
+template <int NT = kThreads>
 __device__ __forceinline__ float wg_max(float v, float* red) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -142,7 +148,7 @@ __device__ __forceinline__ float wg_max(float v, float* red) {
   __syncthreads();
   float m = red[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
   return m;
 }
 
@@ -197,9 +203,51 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     float v[16];
     Loader<T>::block(x + row * K + j * 16, v);
     uint32_t c0, c1;
-    const uint32_t sb = quant_block(v, s_g, c0, c1);
+    const uint32_t sb = quant_block(v, block_amax(v), s_g, c0, c1);
     *reinterpret_cast<uint2*>(codes + row * (K / 2) + j * 8) = make_uint2(c0, c1);
     scales[row * bpr + j] = (uint8_t)sb;
+  }
+}
+
+// Small tensors (<= kSmallThreads * kSmallBlocksPerThread blocks) in ONE
+// workgroup and one launch: every thread loads its blocks once, the global
+// amax is reduced in LDS, and the blocks are quantized from registers.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallBlocksPerThread = 4;
+
+__global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(
+    const uint16_t* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode) {
+  __shared__ float red[kSmallThreads / 64];
+  float v[kSmallBlocksPerThread][16];
+  float bmax[kSmallBlocksPerThread];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSmallBlocksPerThread; ++j) {
+    const int64_t b = (int64_t)threadIdx.x + (int64_t)j * kSmallThreads;
+    bmax[j] = 0.0f;
+    if (b < nblocks) {
+      Loader<uint16_t>::block(x + b * 16, v[j]);
+      bmax[j] = block_amax(v[j]);
+      m = fmaxf(m, bmax[j]);
+    }
+  }
+  float s_g;
+  if (mode == GS_STATIC) {
+    s_g = *gscale;
+  } else {
+    s_g = wg_max<kSmallThreads>(m, red) / 2688.0f;
+    if (threadIdx.x == 0) *gscale = s_g;
+  }
+#pragma unroll
+  for (int j = 0; j < kSmallBlocksPerThread; ++j) {
+    const int64_t b = (int64_t)threadIdx.x + (int64_t)j * kSmallThreads;
+    if (b < nblocks) {
+      uint32_t c0, c1;
+      const uint32_t sb = quant_block(v[j], bmax[j], s_g, c0, c1);
+      *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(c0, c1);
+      scales[b] = (uint8_t)sb;
+    }
   }
 }
 
@@ -218,7 +266,7 @@ int64_t quant_grid(int64_t nblocks) {
 }  // namespace
 
 int amax_partial_count(int64_t elems) {
-  int64_t p = (elems + 65535) / 65536;
+  int64_t p = (elems + 4095) / 4096;
   if (p > 2048) p = 2048;
   return (int)(p < 1 ? 1 : p);
 }
@@ -227,6 +275,11 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint
                                 uint8_t* scales, float* gscale, GsMode mode, float* partials,
                                 int n_parts, hipStream_t stream) {
   const int64_t nblocks = rows * (K / 16);
+  if (mode != GS_FROM_PARTIALS && nblocks <= (int64_t)kSmallThreads * kSmallBlocksPerThread) {
+    hipLaunchKernelGGL(quantize_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, x, nblocks, codes, scales,
+                       gscale, (int)mode);
+    return hipGetLastError();
+  }
   if (mode == GS_FROM_PARTIALS) {
     hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x,
                        rows * K, partials);

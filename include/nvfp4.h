@@ -147,16 +147,34 @@ typedef struct {
  * [N][K/2], w_scales [N][K/16], *w_gscale); both global scales are device
  * pointers.  Each weight byte is read from HBM once for all M tokens.
  * Result: within |y - y_exact| <= 1e-5 * sum_k |a_k w_k| of the exact real
- * dot product of the dequantized rows.
- * epi == NULL: plain projection, no workspace needed.
- * epi != NULL: LM-head epilogue as above; needs
- *   nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD, M, N, K) bytes of zeroed ws.
+ * dot product of the dequantized rows; repeated calls give identical bits.
+ * Workspace: nvfp4_workspace_size(NVFP4_OP_GEMV, M, N, K) bytes for the
+ *   plain projection (0 for shapes served without splitting K; ws may then
+ *   be NULL) and nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD, M, N, K) bytes
+ *   with the epilogue, zero-filled once after allocation.
+ * epi == NULL: plain projection.
+ * epi != NULL: LM-head epilogue as above.
  */
 int nvfp4_gemv_smallm(int M, int64_t N, int64_t K,
                       const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
                       float* y, const nvfp4_lmhead_epilogue_t* epi,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Name of the kernel variant nvfp4_gemv_smallm launches for this shape
+ * (lmhead != 0: with the epilogue).  Static string; pure host function.
+ * The launch table is chosen per (M, N, K) on the host, like the pages'
+ * runtime dispatch (reading notes, section 5.2), and is fixed for the life
+ * of the process, so a captured graph replays the same kernels.
+ */
+const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead);
+
+/* Name of compiled kernel variant `index` (0-based), NULL past the end.
+ * Setting the environment variable NVFP4_GEMV_VARIANT to one of these
+ * names makes nvfp4_gemv_smallm launch that variant for every M it covers
+ * (for tuning and testing; read on each call). */
+const char* nvfp4_gemv_variant_name(int index);
 
 #ifdef __cplusplus
 }

@@ -117,3 +117,23 @@ def test_gemv_is_repeatable_and_rows_do_not_depend_on_m():
     y_ref, ref_abs = O.gemv_ref(ar, wr)
     assert_gemv_close(y3, y_ref, ref_abs, what="M=1 static")
     assert_gemv_close(y1[:1], y_ref, ref_abs, what="M=8 row 0 static")
+
+
+VARIANT_SHAPES = [(1, 37, 160), (16, 515, 4128), (16, 300, 5120), (16, 129, 25600)]
+
+
+@pytest.mark.parametrize("variant", F.nvfp4_gemv_variant_names() if __import__("os").path.exists(F.LIB_PATH) else [])
+def test_every_kernel_variant(variant, monkeypatch):
+    """Each compiled variant (forced through NVFP4_GEMV_VARIANT) against the
+    oracle: ragged row tails, K not a multiple of 128, several K phases, and
+    M below and at the variant's token count."""
+    mt = F.variant_tokens(variant)
+    monkeypatch.setenv("NVFP4_GEMV_VARIANT", variant)
+    for M in sorted({1, max(1, mt - 1), mt}):
+        for (nmul, N, K) in VARIANT_SHAPES:
+            assert F.nvfp4_gemv_variant(M, N, K) == variant
+            w = W.small_random_weights(N + K + M, N, K)
+            xb = W.small_random_bf16(3 * N + M, M, K)
+            wq, aq, y = _run(M, N, K, w, xb, variant)
+            y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+            assert_gemv_close(y, y_ref, ref_abs, what=f"{variant} M={M} N={N} K={K}")

@@ -48,9 +48,10 @@ def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None):
     return logits, np.array(Hs), np.array(Ts)
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-def test_small_vocab_sequence(mode):
-    M, N, K, P = 4, 3000, 512, 60
+@pytest.mark.parametrize("mode,M,N,K", [(0, 4, 3000, 512), (1, 4, 3000, 512), (0, 1, 2500, 1024),
+                                         (0, 8, 2000, 8192), (0, 2, 4099, 256)])
+def test_small_vocab_sequence(mode, M, N, K):
+    P = 60
     w = W.small_random_weights(41, N, K, scale=0.2)
     rng = np.random.default_rng(42)
     xs = np.stack([W.small_random_bf16(100 + t, M, K) for t in range(P)])
