@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=30, help="timed launches per (projection, M) for per-kernel times")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle baseline")
+    ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head + ReSET epilogue figures")
+    ap.add_argument("--no-chain", action="store_true", help="skip the 64-layer hipGraph chain figures")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -193,6 +195,12 @@ def main():
                       f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us")
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
 
+    extra = {}
+    if not args.no_lmhead:
+        extra["lm_head"] = bench_lm_head(args, stream)
+    if not args.no_chain:
+        extra["chain"] = bench_chain(args, stream)
+
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu:
@@ -232,8 +240,159 @@ def main():
         },
         "cpu_baseline": cpu,
         "detail": detail,
+        "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def _b2b_us(fn, reps, stream):
+    import torch
+
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_lm_head(args, stream):
+    """LM head N=151936 K=5120 at M = 1 and 8: quantization + GEMV with the
+    fused entropy / ReSET epilogue, and the plain GEMV for comparison."""
+    import torch
+
+    import fp4_decode_gemv_amd as F
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    case = W.lm_head_case()
+    w = W.chain_weights_gpu(case, dev)
+    base = F.nvfp4_pack_weights(w)
+    del w
+    copies = [base, F.NvFp4Tensor(base.codes.clone(), base.scales.clone(), base.gscale.clone())]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    wb = weight_bytes(case.N, case.K)
+    out = []
+    for M in (1, 8):
+        x = torch.from_numpy(W.activations_bf16(case.x_seed, case.K, M).view(np.int16)).to(dev).view(torch.bfloat16)
+        aq = F.nvfp4_quantize_act(x)
+        qn = F.nvfp4_workspace_size(F.NVFP4_OP_QUANT, M, 0, case.K)
+        qws = F.new_workspace(qn, dev) if qn else None
+        y = torch.empty((M, case.N), device=dev)
+        st = F.new_reset_state(M, 8, dev)
+        epi = F.Epilogue(step_start=torch.zeros(M, dtype=torch.uint8, device=dev), state=st,
+                         entropy=torch.empty(M, device=dev), temperature=torch.empty(M, device=dev), window=8)
+        ews = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, case.N, case.K), dev)
+        gn = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, case.N, case.K)
+        gws = F.new_workspace(gn, dev) if gn else None
+        k = [0]
+
+        def with_epi():
+            F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
+            F.nvfp4_gemv_smallm(aq, copies[k[0] % 2], y=y, epi=epi, ws=ews, stream=stream)
+            k[0] += 1
+
+        def epi_only():
+            F.nvfp4_gemv_smallm(aq, copies[k[0] % 2], y=y, epi=epi, ws=ews, stream=stream)
+            k[0] += 1
+
+        def plain():
+            F.nvfp4_gemv_smallm(aq, copies[k[0] % 2], y=y, ws=gws, stream=stream)
+            k[0] += 1
+
+        t_all = _b2b_us(with_epi, args.reps, stream)
+        t_epi = _b2b_us(epi_only, args.reps, stream)
+        t_plain = _b2b_us(plain, args.reps, stream)
+        out.append({"M": M, "N": case.N, "K": case.K, "weight_bytes": wb,
+                    "variant": F.nvfp4_gemv_variant(M, case.N, case.K, True),
+                    "quant_gemv_epilogue_us": round(t_all, 2), "gemv_epilogue_us": round(t_epi, 2),
+                    "gemv_plain_us": round(t_plain, 2), "gemv_epilogue_gbs": round(wb / t_epi / 1e3, 1),
+                    "epilogue_overhead_us": round(t_epi - t_plain, 2)})
+        log(args, f"[lmhead] M={M} quant+gemv+epilogue {t_all:.2f} us, gemv+epilogue {t_epi:.2f} us "
+                  f"({wb / t_epi / 1e3:.0f} GB/s), plain gemv {t_plain:.2f} us")
+    del copies, base
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_chain(args, stream):
+    """64 Qwen3-32B layers x 4 projections (17.55 GB of packed weights)
+    captured in one hipGraph; microseconds per decode step at M = 1 and 8,
+    with the activation quantization and GEMV-only."""
+    import torch
+
+    import fp4_decode_gemv_amd as F
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    ws = {}
+    for l in range(W.CHAIN_LAYERS):
+        for p in range(4):
+            c = W.chain_case(l, p)
+            wt = W.chain_weights_gpu(c, dev)
+            ws[(l, p)] = F.nvfp4_pack_weights(wt)
+            del wt
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    total = sum(weight_bytes(W.chain_case(0, p).N, W.chain_case(0, p).K) for p in range(4)) * W.CHAIN_LAYERS
+    log(args, f"[chain] packed {W.CHAIN_LAYERS}x4 projections ({total / 1e9:.2f} GB) in {time.perf_counter() - t0:.1f}s")
+    out = []
+    for M in (1, 8):
+        io = {}
+        for l in range(W.CHAIN_LAYERS):
+            for p in range(4):
+                c = W.chain_case(l, p)
+                x = torch.from_numpy(W.chain_activations_bf16(l, p, M).view(np.int16)).to(dev).view(torch.bfloat16)
+                aq = F.nvfp4_quantize_act(x)
+                qn = F.nvfp4_workspace_size(F.NVFP4_OP_QUANT, M, 0, c.K)
+                gn = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, c.N, c.K)
+                io[(l, p)] = (x, aq, F.new_workspace(qn, dev) if qn else None,
+                              F.new_workspace(gn, dev) if gn else None, torch.empty((M, c.N), device=dev))
+        res = {"M": M, "weight_bytes": total}
+        for quantize in (True, False):
+            def step():
+                for l in range(W.CHAIN_LAYERS):
+                    for p in range(4):
+                        x, aq, qws, gws, y = io[(l, p)]
+                        if quantize:
+                            F.nvfp4_quantize_act(x, ws=qws, out=aq)
+                        F.nvfp4_gemv_smallm(aq, ws[(l, p)], y=y, ws=gws)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            torch.cuda.synchronize()
+            reps = 10
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            key = "quant_gemv" if quantize else "gemv_only"
+            res[key + "_us_per_step"] = round(us, 1)
+            res[key + "_gbs"] = round(total / us / 1e3, 1)
+            del g
+        out.append(res)
+        log(args, f"[chain] M={M} {res['quant_gemv_us_per_step']:.1f} us/step with quantization "
+                  f"({res['quant_gemv_gbs']:.0f} GB/s), {res['gemv_only_us_per_step']:.1f} us GEMV only "
+                  f"({res['gemv_only_gbs']:.0f} GB/s)")
+        del io
+    del ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(args, cases, samples):

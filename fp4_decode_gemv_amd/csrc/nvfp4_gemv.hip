@@ -84,8 +84,9 @@ struct GemvParams {
   float* y;
   // LM-head epilogue (used only by the EPI instantiations)
   EpilogueArgs epi;
-  unsigned* counter;       // epilogue: workgroups (row tiles) done
-  float* partials;         // epilogue: [row tiles][MT][3]
+  unsigned* counter;       // epilogue: groups of workgroups done
+  unsigned* group_counter; // epilogue: [groups] workgroups done in each group
+  float* partials;         // epilogue: [row tiles][MT][4] = {max, S, T, -}
   size_t state_bytes;      // bytes per ReSET state
 };
 
@@ -158,15 +159,14 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 // with their token index and a validity flag.
 // ----------------------------------------------------------------------------
 
-// Device-scope (agent) relaxed atomic store / load: on gfx950 these are
-// written through to, and read from, the device coherence point, so no
-// whole-L2 write-back is needed to publish them to other workgroups.
+// Device-scope (agent) relaxed atomic store: on gfx950 it is written
+// through to the device coherence point, so no whole-L2 write-back is
+// needed to publish it to other workgroups.
 __device__ __forceinline__ void st_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+
+constexpr int kEpiGroup = 32;  // workgroups per first-level epilogue counter
 
 template <int MT, int NW>
 struct EpiSmem {
@@ -177,6 +177,25 @@ struct EpiSmem {
   float tred[NW * 64];
   unsigned last;
 };
+
+// Merge two softmax partials (m, S, T) with S = sum e^(z-m),
+// T = sum e^(z-m) (z-m):  m = max, S = S_a e^(m_a-m) + S_b e^(m_b-m),
+// T = e^(m_a-m) (T_a + (m_a-m) S_a) + e^(m_b-m) (T_b + (m_b-m) S_b).
+__device__ __forceinline__ void merge_partial(float& m, float& S, float& T, float mb, float Sb, float Tb) {
+  if (mb == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = mb;
+    S = Sb;
+    T = Tb;
+    return;
+  }
+  const float mn = fmaxf(m, mb);
+  const float da = m - mn, db = mb - mn;
+  const float fa = expf(da), fb = expf(db);
+  T = __builtin_fmaf(fa, __builtin_fmaf(da, S, T), fb * __builtin_fmaf(db, Sb, Tb));
+  S = __builtin_fmaf(S, fa, Sb * fb);
+  m = mn;
+}
 
 template <int MT, int NW, int NV>
 __device__ void lmhead_epilogue(const GemvParams& p, const float (&val)[NV], const int (&tok)[NV],
@@ -239,56 +258,56 @@ __device__ void lmhead_epilogue(const GemvParams& p, const float (&val)[NV], con
       s += sm.wred[w][threadIdx.x][0];
       t += sm.wred[w][threadIdx.x][1];
     }
-    float* dst = p.partials + (tile * MT + threadIdx.x) * 3;
+    float* dst = p.partials + (tile * MT + threadIdx.x) * 4;  // {max, S, T, unused}
     st_agent(dst, sm.gmax[threadIdx.x]);
     st_agent(dst + 1, s);
     st_agent(dst + 2, t);
   }
   // ---- the last workgroup to finish merges all partials ----
   // The partials were written through to the device coherence point; wait
-  // until those stores have completed, then count this workgroup in.
+  // until those stores have completed, then count this workgroup in: first
+  // in its group of kEpiGroup tiles, and the last of a group in the top
+  // counter (one hot counter for thousands of workgroups serializes them).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0)
-    sm.last = (__hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (unsigned)ntiles - 1u)
-                  ? 1u
-                  : 0u;
+  if (threadIdx.x == 0) {
+    const int64_t grp = tile / kEpiGroup;
+    const int64_t ngroups = (ntiles + kEpiGroup - 1) / kEpiGroup;
+    const int64_t gsize = ntiles - grp * kEpiGroup < kEpiGroup ? ntiles - grp * kEpiGroup : kEpiGroup;
+    unsigned last = 0u;
+    if (__hip_atomic_fetch_add(p.group_counter + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        (unsigned)gsize - 1u) {
+      __hip_atomic_store(p.group_counter + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     (unsigned)ngroups - 1u
+                 ? 1u
+                 : 0u;
+    }
+    sm.last = last;
+  }
   __syncthreads();
   if (!sm.last) return;
-  const int nwg = ntiles;
+  // drop any stale cached copy of the partials, then read them with wide loads
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const float4* part = reinterpret_cast<const float4*>(p.partials);
   for (int m = 0; m < p.M; ++m) {
-    float gm = -INFINITY;
-    for (int b = threadIdx.x; b < nwg; b += NT)
-      gm = fmaxf(gm, ld_agent(p.partials + ((int64_t)b * MT + m) * 3));
+    // each thread merges tiles threadIdx.x, +NT, ... in order; then a fixed tree
+    float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
+    for (int b = threadIdx.x; b < ntiles; b += NT) {
+      const float4 q = part[(int64_t)b * MT + m];
+      merge_partial(gm, Sm, Tm, q.x, q.y, q.z);
+    }
     sm.mred[threadIdx.x] = gm;
-    __syncthreads();
-    for (int s = NT / 2; s >= 1; s >>= 1) {
-      if (threadIdx.x < s) sm.mred[threadIdx.x] = fmaxf(sm.mred[threadIdx.x], sm.mred[threadIdx.x + s]);
-      __syncthreads();
-    }
-    gm = sm.mred[0];
-    // S = sum_b S_b e^(m_b - gm);  T = sum_b e^(m_b - gm) (T_b + (m_b - gm) S_b)
-    float Sm = 0.0f, Tm = 0.0f;
-    for (int b = threadIdx.x; b < nwg; b += NT) {
-      const float* src = p.partials + ((int64_t)b * MT + m) * 3;
-      const float mb = ld_agent(src);
-      const float Sb = ld_agent(src + 1);
-      const float Tb = ld_agent(src + 2);
-      if (mb == -INFINITY) continue;
-      const float d = mb - gm;
-      const float f = expf(d);
-      Sm = __builtin_fmaf(Sb, f, Sm);
-      Tm = __builtin_fmaf(f, __builtin_fmaf(d, Sb, Tb), Tm);
-    }
-    __syncthreads();
     sm.sred[threadIdx.x] = Sm;
     sm.tred[threadIdx.x] = Tm;
     __syncthreads();
     for (int s = NT / 2; s >= 1; s >>= 1) {
       if (threadIdx.x < s) {
-        sm.sred[threadIdx.x] += sm.sred[threadIdx.x + s];
-        sm.tred[threadIdx.x] += sm.tred[threadIdx.x + s];
+        float a = sm.mred[threadIdx.x], sa = sm.sred[threadIdx.x], ta = sm.tred[threadIdx.x];
+        merge_partial(a, sa, ta, sm.mred[threadIdx.x + s], sm.sred[threadIdx.x + s], sm.tred[threadIdx.x + s]);
+        sm.mred[threadIdx.x] = a;
+        sm.sred[threadIdx.x] = sa;
+        sm.tred[threadIdx.x] = ta;
       }
       __syncthreads();
     }
@@ -926,9 +945,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = 0;
   }
-  // workspace (epilogue only): [counter | per-workgroup softmax partials]
-  c.ws_epi_partials = 256;
-  c.ws_bytes = epi ? c.ws_epi_partials + align256(c.grid * c.mt * 3 * 4) : 0;
+  // workspace (epilogue only): [top counter | group counters | per-workgroup softmax partials]
+  c.ws_group_counters = 256;
+  c.ws_epi_partials = c.ws_group_counters + align256((c.grid + kEpiGroup - 1) / kEpiGroup * 4);
+  c.ws_bytes = epi ? c.ws_epi_partials + align256(c.grid * c.mt * 4 * 4) : 0;
   return c;
 }
 
@@ -960,6 +980,7 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   if (epi) {
     p.epi = *epi;
     p.counter = reinterpret_cast<unsigned*>(wsb);
+    p.group_counter = reinterpret_cast<unsigned*>(wsb + cfg.ws_group_counters);
     p.partials = reinterpret_cast<float*>(wsb + cfg.ws_epi_partials);
     p.state_bytes = reset_state_bytes(epi->window);
   }

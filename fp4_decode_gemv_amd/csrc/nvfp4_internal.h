@@ -20,10 +20,10 @@ enum GsMode : int {
 // Number of amax partials the two-launch path uses for `elems` elements.
 int amax_partial_count(int64_t elems);
 
-// Activation quantization is done by one workgroup in one launch up to this
-// many elements, in two launches (parallel amax partials, then quantize)
-// above it.
-constexpr int64_t kActSelfAmaxMaxElems = 65536;
+// Activation quantization takes one launch up to this many elements (every
+// workgroup reduces the whole tensor for the global amax), two launches
+// above it (parallel amax partials, then quantize).
+constexpr int64_t kActSelfAmaxMaxElems = 131072;
 
 // Launchers (no validation: the C-ABI layer has done it).
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
@@ -59,7 +59,7 @@ struct GemvConfig {
   int64_t lds_bytes;  // dynamic LDS per workgroup
   // workspace layout (byte offset of the epilogue partials) and total size
   // (0 = none needed)
-  int64_t ws_epi_partials, ws_bytes;
+  int64_t ws_group_counters, ws_epi_partials, ws_bytes;
 };
 
 GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi);

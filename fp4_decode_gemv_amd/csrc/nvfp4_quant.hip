@@ -209,45 +209,89 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
   }
 }
 
-// Small tensors (<= kSmallThreads * kSmallBlocksPerThread blocks) in ONE
-// workgroup and one launch: every thread loads its blocks once, the global
-// amax is reduced in LDS, and the blocks are quantized from registers.
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallBlocksPerThread = 4;
+// Activation quantization.  Thread t of workgroup w owns the 8 elements at
+// (w * kActThreads + t) * 8, half of one 16-element block; the other half is
+// in the neighbouring lane.  The E2M1 rounding uses v_cvt_scalef32_pk_fp4_f32
+// with scale 1.0: on gfx950 it rounds to nearest, ties to the even code,
+// saturates at 6 and copies the sign, exactly the rule above (checked on
+// hardware over every midpoint and its neighbours).  The division before it
+// stays the IEEE one.
+//   mode GS_SELF: every workgroup loads the whole tensor (at most
+//   kActSelfElems elements, every load in flight at once) for the global
+//   amax and then quantizes, from registers, the chunk whose index is its
+//   own workgroup index, so no element is read twice by one workgroup.
+constexpr int kActThreads = 1024;
+constexpr int kActChunks = 16;                            // 16-byte loads per thread in GS_SELF
+constexpr int kActSelfElems = kActThreads * 8 * kActChunks;
 
-__global__ __launch_bounds__(kSmallThreads) void quantize_small_kernel(
-    const uint16_t* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode) {
-  __shared__ float red[kSmallThreads / 64];
-  float v[kSmallBlocksPerThread][16];
-  float bmax[kSmallBlocksPerThread];
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kSmallBlocksPerThread; ++j) {
-    const int64_t b = (int64_t)threadIdx.x + (int64_t)j * kSmallThreads;
-    bmax[j] = 0.0f;
-    if (b < nblocks) {
-      Loader<uint16_t>::block(x + b * 16, v[j]);
-      bmax[j] = block_amax(v[j]);
-      m = fmaxf(m, bmax[j]);
-    }
-  }
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+__global__ __launch_bounds__(kActThreads) void quantize_act_kernel(
+    const uint16_t* __restrict__ x, int64_t nelem, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode,
+    const float* __restrict__ partials, int n_parts) {
+  __shared__ float red[kActThreads / 64];
+  const int64_t mine = ((int64_t)blockIdx.x * kActThreads + threadIdx.x) * 8;  // first element of this thread
+  uint4 raw = make_uint4(0, 0, 0, 0);
   float s_g;
-  if (mode == GS_STATIC) {
-    s_g = *gscale;
-  } else {
-    s_g = wg_max<kSmallThreads>(m, red) / 2688.0f;
-    if (threadIdx.x == 0) *gscale = s_g;
-  }
+  if (mode == GS_SELF) {
+    uint4 v[kActChunks];
 #pragma unroll
-  for (int j = 0; j < kSmallBlocksPerThread; ++j) {
-    const int64_t b = (int64_t)threadIdx.x + (int64_t)j * kSmallThreads;
-    if (b < nblocks) {
-      uint32_t c0, c1;
-      const uint32_t sb = quant_block(v[j], bmax[j], s_g, c0, c1);
-      *reinterpret_cast<uint2*>(codes + b * 8) = make_uint2(c0, c1);
-      scales[b] = (uint8_t)sb;
+    for (int j = 0; j < kActChunks; ++j) {
+      const int64_t i = ((int64_t)j * kActThreads + threadIdx.x) * 8;
+      v[j] = i < nelem ? *reinterpret_cast<const uint4*>(x + i) : make_uint4(0, 0, 0, 0);
     }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kActChunks; ++j) {
+      const uint32_t w[4] = {v[j].x & 0x7FFF7FFFu, v[j].y & 0x7FFF7FFFu, v[j].z & 0x7FFF7FFFu,
+                             v[j].w & 0x7FFF7FFFu};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(bf16_to_f32(w[i] & 0xFFFFu), bf16_to_f32(w[i] >> 16)));
+      if (j == (int)blockIdx.x) raw = v[j];
+    }
+    s_g = wg_max<kActThreads>(m, red) / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
+  } else {
+    if (mine < nelem) raw = *reinterpret_cast<const uint4*>(x + mine);
+    if (mode == GS_STATIC) {
+      s_g = *gscale;
+    } else {
+      float m = 0.0f;
+      for (int i = threadIdx.x; i < n_parts; i += kActThreads) m = fmaxf(m, partials[i]);
+      s_g = wg_max<kActThreads>(m, red) / 2688.0f;
+      if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
+    }
+  }
+  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(rw[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(rw[i] >> 16);
+  }
+  // block amax over the two halves (neighbouring lanes)
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  if (mine < nelem) {
+    float tb = 0.0f;
+    if (s_g != 0.0f) {
+      const float denom = 6.0f * s_g;
+      tb = amax / denom;
+    }
+    const uint32_t sb = e4m3_code(tb);
+    const float e = e4m3_value(sb) * s_g;
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = e != 0.0f ? v[i] / e : copysignf(0.0f, v[i]);
+    const uint32_t c = e2m1_pair(r[0], r[1]) | (e2m1_pair(r[2], r[3]) << 8) | (e2m1_pair(r[4], r[5]) << 16) |
+                       (e2m1_pair(r[6], r[7]) << 24);
+    *reinterpret_cast<uint32_t*>(codes + mine / 2) = c;
+    if ((threadIdx.x & 1) == 0) scales[mine / 16] = (uint8_t)sb;
   }
 }
 
@@ -274,18 +318,15 @@ int amax_partial_count(int64_t elems) {
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
                                 uint8_t* scales, float* gscale, GsMode mode, float* partials,
                                 int n_parts, hipStream_t stream) {
-  const int64_t nblocks = rows * (K / 16);
-  if (mode != GS_FROM_PARTIALS && nblocks <= (int64_t)kSmallThreads * kSmallBlocksPerThread) {
-    hipLaunchKernelGGL(quantize_small_kernel, dim3(1), dim3(kSmallThreads), 0, stream, x, nblocks, codes, scales,
-                       gscale, (int)mode);
-    return hipGetLastError();
-  }
+  const int64_t nelem = rows * K;
+  if (mode == GS_SELF && nelem > kActSelfElems) return hipErrorInvalidValue;
   if (mode == GS_FROM_PARTIALS) {
-    hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x,
-                       rows * K, partials);
+    hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x, nelem,
+                       partials);
   }
-  hipLaunchKernelGGL(quantize_kernel<uint16_t>, dim3((unsigned)quant_grid(nblocks)), dim3(kThreads),
-                     0, stream, x, rows, K, codes, scales, gscale, (int)mode, partials, n_parts);
+  const int64_t grid = (nelem + (int64_t)kActThreads * 8 - 1) / ((int64_t)kActThreads * 8);
+  hipLaunchKernelGGL(quantize_act_kernel, dim3((unsigned)grid), dim3(kActThreads), 0, stream, x, nelem, codes,
+                     scales, gscale, (int)mode, partials, n_parts);
   return hipGetLastError();
 }
 

@@ -107,6 +107,10 @@ def lm_head_case() -> ProjectionCase:
     return ProjectionCase("qwen3_32b_lm_head", N, K, 3100, 3200, w_outlier_rows=True)
 
 
+CHAIN_LAYERS = 64
+CHAIN_CHECKED_LAYERS = (0, 31, 63)
+
+
 def chain_case(layer: int, proj_index: int) -> ProjectionCase:
     """Projection ``proj_index`` of layer ``layer`` of the 64-layer chain."""
     p = PROJ_ORDER[proj_index]
@@ -269,3 +273,27 @@ def small_random_bf16(seed: int, M: int, K: int, scale: float = 1.0) -> np.ndarr
 def small_random_weights(seed: int, N: int, K: int, scale: float = 0.02) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return rng.standard_normal((N, K), dtype=np.float32) * np.float32(scale)
+
+
+def chain_weights_gpu(case: ProjectionCase, device):
+    """Weights of an unchecked chain layer, drawn on the GPU with torch's
+    seeded generator (same distribution as ``weights``: 0.02 * N(0,1), then
+    floor(0.001 N) rows * 8).  Checked layers use ``weights`` instead, so the
+    CPU oracle can regenerate them."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(case.w_seed)
+    w = torch.randn((case.N, case.K), generator=g, device=device, dtype=torch.float32)
+    w.mul_(0.02)
+    if case.w_outlier_rows:
+        cnt = math.floor(0.001 * case.N)
+        if cnt:
+            rows = torch.randperm(case.N, generator=g, device=device)[:cnt]
+            w[rows] *= 8.0
+    return w
+
+
+def chain_activations_bf16(layer: int, proj_index: int, M: int) -> np.ndarray:
+    c = chain_case(layer, proj_index)
+    return activations_bf16(c.x_seed, c.K, M)
