@@ -39,6 +39,28 @@ HBM_PEAK_GBS = 8000.0
 M_LIST = (1, 2, 4, 8)
 CPU_ROWS = 2048
 
+# Measured HBM traffic of the 16 GEMV launches of one step: rocprofv3
+# FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a plain
+# 512 MiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only for the
+# kernel source it was measured on; reported as null once that changes.
+GEMV_TRAFFIC = {
+    "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
+    "sha256": "8620d42eca412419884dd1be88ae4127ca1974f9a0b84ea0f7767874c28c4350",
+    "bytes_per_step": 1115083354,
+}
+
+
+def measured_traffic():
+    import hashlib
+
+    try:
+        src = open(os.path.join(ROOT, GEMV_TRAFFIC["source"]), "rb").read()
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest() != GEMV_TRAFFIC["sha256"]:
+        return None
+    return GEMV_TRAFFIC["bytes_per_step"]
+
 
 def weight_bytes(N: int, K: int) -> int:
     """Algorithmic bytes of one GEMV: codes + E4M3 scales + global scale."""
@@ -56,6 +78,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle baseline")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head + ReSET epilogue figures")
     ap.add_argument("--no-chain", action="store_true", help="skip the 64-layer hipGraph chain figures")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="at the end, fill and copy a buffer of this many MiB three times: a plain copy of "
+                         "known size to calibrate hardware byte counters against")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -201,6 +226,17 @@ def main():
     if not args.no_chain:
         extra["chain"] = bench_chain(args, stream)
 
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            src.fill_(1)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(args, f"[copy-probe] filled and copied {n} bytes x3")
+        del src, dst
+
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu:
@@ -234,8 +270,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "gemv_kernel, all 16 (projection, M) cases of a step: summed algorithmic bytes / summed "
+            "traffic": measured_traffic(),
+            "traffic_unit": "HBM bytes read + written by the 16 GEMV launches of one step (rocprofv3 "
+                            "FETCH_SIZE / WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": gemv_bytes,
+            "kernel": "gemv kernels, all 16 (projection, M) cases of a step: summed algorithmic bytes / summed "
                       "average launch durations (back-to-back launches between HIP events)",
         },
         "cpu_baseline": cpu,
