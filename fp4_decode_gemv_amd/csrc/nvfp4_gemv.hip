@@ -661,6 +661,88 @@ __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
   }
 }
 
+// One 256-element step of the MFMA kernels.  Lane (li, kg) holds, for each
+// of its R weight rows li (+16r) and for its activation row, the 64 codes of
+// elements 64*kg .. 64*kg+63 of the step (two uint4) and their four block
+// scales (one byte each).  Both sides are decoded to exact f16 values
+// E2M1 * E4M3 and eight v_mfma_f32_16x16x32_f16 per row tile add the step
+// into acc[r] (D layout: lane (li, kg) holds rows 4*kg + v, token li).
+template <int R>
+__device__ __forceinline__ void mfma_step(const uint4 (&w)[R][2], const uint32_t (&s)[R], const uint4& a0,
+                                          const uint4& a1, uint32_t sa, float4_t (&acc)[R]) {
+  // block scales as f16 pairs (both halves equal; E4M3 values are exact in f16)
+  const float2_t sa01 = __builtin_amdgcn_cvt_pk_f32_fp8(sa, false);
+  const float2_t sa23 = __builtin_amdgcn_cvt_pk_f32_fp8(sa, true);
+  const half2_t ha[4] = {as_half2(pack_f16x2(sa01[0], sa01[0])), as_half2(pack_f16x2(sa01[1], sa01[1])),
+                         as_half2(pack_f16x2(sa23[0], sa23[0])), as_half2(pack_f16x2(sa23[1], sa23[1]))};
+  half2_t hw[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float2_t sw01 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
+    const float2_t sw23 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], true);
+    hw[r][0] = as_half2(pack_f16x2(sw01[0], sw01[0]));
+    hw[r][1] = as_half2(pack_f16x2(sw01[1], sw01[1]));
+    hw[r][2] = as_half2(pack_f16x2(sw23[0], sw23[0]));
+    hw[r][3] = as_half2(pack_f16x2(sw23[1], sw23[1]));
+  }
+  // word j of the lane's 64 codes: B operand decoded once, used by all R tiles
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t aw = word_of(j < 4 ? a0 : a1, j & 3);
+    const half8_t b = wdecode8_scaled(aw, ha[j >> 1]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t ww = word_of(w[r][j >> 2], j & 3);
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(ww, hw[r][j >> 1]), b, acc[r], 0, 0, 0);
+    }
+  }
+}
+
+// Add the NW waves' partial tiles in a fixed order (through LDS; every wave
+// must have left its main loop), scale by the global scales, store y and run
+// the optional epilogue.
+template <int MT, int R, int NW, bool EPI>
+__device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t (&acc)[R], float* red,
+                                            int64_t tile0) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15, kg = lane >> 4;
+  const int64_t N = p.N;
+  const int M = p.M;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
+  __syncthreads();
+  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  // wave w finalizes the (r, v) register slots w, w + NW, ...; D layout:
+  // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token li
+  constexpr int NV = (R * 4 + NW - 1) / NW;
+  float out[NV];
+  int tok[NV];
+  bool ok[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int rv = wave + u * NW;
+    out[u] = 0.0f;
+    tok[u] = li;
+    ok[u] = false;
+    if (rv < R * 4) {
+      const int r = rv >> 2, v = rv & 3;
+      float sum = 0.0f;
+      for (int w = 0; w < NW; ++w) sum += red[((w * R + r) * 4 + v) * 64 + lane];
+      const int64_t row = tile0 + 16 * r + 4 * kg + v;
+      out[u] = sum * scale;
+      ok[u] = li < M && row < N;
+      if (ok[u]) p.y[(int64_t)li * N + row] = out[u];
+    }
+  }
+  if constexpr (EPI) {
+    __shared__ EpiSmem<MT, NW> sm;
+    lmhead_epilogue<MT, NW, NV>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // MFMA-assisted kernel
 // ----------------------------------------------------------------------------
@@ -741,74 +823,180 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(GemvParams p) {
         const uint4 a0 = ab[j][0], a1 = ab[j][1];
         const uint32_t sa = asb[j];
         if (i + P < n) load(j, wave + (i + P) * NW);
-        // B operands: E2M1 * E4M3 of the activation, exact in f16
-        const float2_t sa01 = __builtin_amdgcn_cvt_pk_f32_fp8(sa, false);
-        const float2_t sa23 = __builtin_amdgcn_cvt_pk_f32_fp8(sa, true);
-        const half2_t h0 = as_half2(pack_f16x2(sa01[0], sa01[0]));
-        const half2_t h1 = as_half2(pack_f16x2(sa01[1], sa01[1]));
-        const half2_t h2 = as_half2(pack_f16x2(sa23[0], sa23[0]));
-        const half2_t h3 = as_half2(pack_f16x2(sa23[1], sa23[1]));
-        const half8_t b[8] = {wdecode8_scaled(a0.x, h0), wdecode8_scaled(a0.y, h0), wdecode8_scaled(a0.z, h1),
-                              wdecode8_scaled(a0.w, h1), wdecode8_scaled(a1.x, h2), wdecode8_scaled(a1.y, h2),
-                              wdecode8_scaled(a1.z, h3), wdecode8_scaled(a1.w, h3)};
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          // weight block scales of this lane's four blocks, as f16 pairs (exact)
-          const float2_t sw01 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
-          const float2_t sw23 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], true);
-          const half2_t s0 = as_half2(pack_f16x2(sw01[0], sw01[0]));
-          const half2_t s1 = as_half2(pack_f16x2(sw01[1], sw01[1]));
-          const half2_t s2 = as_half2(pack_f16x2(sw23[0], sw23[0]));
-          const half2_t s3 = as_half2(pack_f16x2(sw23[1], sw23[1]));
-          float4_t d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].x, s0), b[0], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].y, s0), b[1], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].z, s1), b[2], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][0].w, s1), b[3], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].x, s2), b[4], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].y, s2), b[5], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].z, s3), b[6], d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(wdecode8_scaled(w[r][1].w, s3), b[7], d, 0, 0, 0);
-          acc[r] += d;
-        }
+        mfma_step<R>(w, s, a0, a1, sa, acc);
       }
     }
   }
 
-  // add the NW waves' partial tiles in a fixed order
-  float* red = reinterpret_cast<float*>(lds4);  // [NW][R][4][64]
+  mfma_finish<MT, R, NW, EPI>(p, acc, reinterpret_cast<float*>(lds4), tile0);
+}
+
+// ----------------------------------------------------------------------------
+// LDS-staged MFMA kernel
+// ----------------------------------------------------------------------------
+// In the MFMA operand layout the 16 lanes of a row group hold 16 different
+// rows, so a 16-byte load made straight into it sends every 4-lane group of
+// the load to 4 different cache lines.  Here a wave loads each 256-element
+// step with 8 consecutive lanes per 128-byte row of codes and 4 lanes per
+// 16-byte row of scale bytes (whole lines per lane group), writes the step
+// into its own LDS slot and reads it back in the operand layout.  Code rows
+// sit 144 bytes apart in the slot, so the operand reads (16 rows x 16 bytes
+// per lane group) hit 64 different banks.  A wave touches only its own slot,
+// so no workgroup barrier is needed until the final reduction.
+constexpr int kLdsCodeRow = 144;  // LDS bytes per 128-byte row of codes
+constexpr int kLdsScaleRow = 20;  // LDS bytes per 16-byte row of scales
+
+template <int R>
+constexpr int lmfma_slot_bytes() {
+  return (16 * R + 8) * (kLdsCodeRow + kLdsScaleRow);
+}
+
+template <int R>
+struct LmfmaStep {
+  uint4 w[R][2];    // weight codes: rows 8h + lane/8 of tile r, 16 bytes at 16*(lane%8)
+  uint4 a;          // activation codes: row lane/8, 16 bytes at 16*(lane%8)
+  uint32_t ws[R];   // weight scales: row lane/4 of tile r, bytes 4*(lane%4) .. +3 (or +1)
+  uint32_t wsh[R];  // bytes 4*(lane%4) + 2, +3 when the word is loaded in halves
+  uint32_t as, ash; // activation scales: row lane/4, the same bytes
+};
+
+// Word 3 of a gfx9-family buffer resource for raw byte-addressed loads.
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int MT, int R, int NW, int P, bool K64, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
+  extern __shared__ uint4 lds4[];  // NW slots; reused by the final reduction
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int li = lane & 15, kg = lane >> 4;  // operand layout
+  const int lq = lane >> 3, lc = lane & 7;   // code loads: row, 16-byte chunk
+  const int sq = lane >> 2, sp = lane & 3;   // scale loads: row, 4-byte part
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int nsteps = (int)((K + 255) / 256);
+  const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
+  (void)MT;
+
+  // Buffer resources over this tile's weight rows and over the activation:
+  // rows past N or M lie outside num_records and load as zeros, so no load
+  // is predicated.  Code chunks past K (last step only) load bytes of the
+  // next row; their block scales are masked to zero below, which makes the
+  // decoded values zero (E2M1 codes are always finite).
+  const int64_t rows = N - tile0 < 16 * R ? N - tile0 : 16 * R;
+  const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_scales + tile0 * (K / 16)), (short)0, (int)(rows * (K / 16)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t acr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_codes), (short)0, (int)(M * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t asr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_scales), (short)0, (int)(M * (K / 16)), kBufferWord3);
+  const int code_off = lq * (int)(K / 2) + 16 * lc;  // + 8 rows for h = 1, + 16 rows per tile
+  const int scale_off = sq * (int)(K / 16) + 4 * sp;
+
+  auto load = [&](LmfmaStep<R>& st, int step) {
+    const int cstep = step * 128, sstep = step * 16;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
-  __syncthreads();
-  const float scale = (*p.a_gscale) * (*p.w_gscale);
-  // wave w finalizes the (r, v) register slots w, w + NW, ...; D layout:
-  // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token li
-  constexpr int NV = (R * 4 + NW - 1) / NW;
-  float out[NV];
-  int tok[NV];
-  bool ok[NV];
+      for (int h = 0; h < 2; ++h)
+        st.w[r][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(
+            wcr, code_off + (16 * r + 8 * h) * (int)(K / 2) + cstep, 0, 0));
+    st.a = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + cstep, 0, 0));
+    // four block scales (64 elements).  With K % 64 == 0 (K64) every 4-byte
+    // word is aligned and wholly inside its row; otherwise rows are 2-byte
+    // aligned and the last word of a row is half outside, so the word is
+    // loaded as two halves (a load that crosses num_records reads as zero as
+    // a whole).  Scales past K are masked when the step is staged, not here:
+    // using the loaded value now would wait for the load.
+    if constexpr (K64) {
 #pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int rv = wave + u * NW;
-    out[u] = 0.0f;
-    tok[u] = li;
-    ok[u] = false;
-    if (rv < R * 4) {
-      const int r = rv >> 2, v = rv & 3;
-      float sum = 0.0f;
-      for (int w = 0; w < NW; ++w) sum += red[((w * R + r) * 4 + v) * 64 + lane];
-      const int64_t row = tile0 + 16 * r + 4 * kg + v;
-      out[u] = sum * scale;
-      ok[u] = li < M && row < N;
-      if (ok[u]) p.y[(int64_t)li * N + row] = out[u];
+      for (int r = 0; r < R; ++r)
+        st.ws[r] = __builtin_amdgcn_raw_buffer_load_b32(wsr, scale_off + 16 * r * (int)(K / 16) + sstep, 0, 0);
+      st.as = __builtin_amdgcn_raw_buffer_load_b32(asr, scale_off + sstep, 0, 0);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int o = scale_off + 16 * r * (int)(K / 16) + sstep;
+        st.ws[r] = __builtin_amdgcn_raw_buffer_load_b16(wsr, o, 0, 0);
+        st.wsh[r] = __builtin_amdgcn_raw_buffer_load_b16(wsr, o + 2, 0, 0);
+      }
+      st.as = __builtin_amdgcn_raw_buffer_load_b16(asr, scale_off + sstep, 0, 0);
+      st.ash = __builtin_amdgcn_raw_buffer_load_b16(asr, scale_off + sstep + 2, 0, 0);
+    }
+  };
+  // the staged scale word of a lane: its loaded bytes with the blocks past K
+  // cleared
+  auto scale_word = [&](uint32_t lo, uint32_t hi, int step) -> uint32_t {
+    const int64_t es = (int64_t)step * 256 + 64 * sp;
+    const uint32_t w = K64 ? lo : (lo & 0xFFFFu) | (hi << 16);
+    return es + 32 < K ? w : es < K ? (w & 0xFFFFu) : 0u;
+  };
+
+  char* slot = reinterpret_cast<char*>(lds4) + wave * lmfma_slot_bytes<R>();
+  char* scl = slot + (16 * R + 8) * kLdsCodeRow;
+  // operand-layout read addresses (activation columns >= M read row M - 1; ignored)
+  const int btok = li < M ? li : M - 1;
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // P register buffers in a ring: the loads of steps i+1 .. i+P-1 stay in
+  // flight while step i is staged and computed; a buffer is refilled right
+  // after its contents went to LDS.
+  LmfmaStep<R> buf[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (j < n) load(buf[j], wave + j * NW);
+  for (int i0 = 0; i0 < n; i0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        // stage the step (the previous step's operand reads are done: fence)
+        wave_lds_fence();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<uint4*>(slot + (16 * r + 8 * h + lq) * kLdsCodeRow + 16 * lc) = buf[j].w[r][h];
+          *reinterpret_cast<uint32_t*>(scl + (16 * r + sq) * kLdsScaleRow + 4 * sp) =
+              scale_word(buf[j].ws[r], buf[j].wsh[r], wave + i * NW);
+        }
+        *reinterpret_cast<uint4*>(slot + (16 * R + lq) * kLdsCodeRow + 16 * lc) = buf[j].a;
+        if (sq < 8)
+          *reinterpret_cast<uint32_t*>(scl + (16 * R + sq) * kLdsScaleRow + 4 * sp) =
+              scale_word(buf[j].as, buf[j].ash, wave + i * NW);
+        wave_lds_fence();
+        if (i + P < n) load(buf[j], wave + (i + P) * NW);
+        // read it back in the operand layout
+        uint4 w[R][2];
+        uint32_t sw[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          w[r][0] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg);
+          w[r][1] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg + 16);
+          sw[r] = *reinterpret_cast<const uint32_t*>(scl + (16 * r + li) * kLdsScaleRow + 4 * kg);
+        }
+        const uint4 a0 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg + 16);
+        const uint32_t sa = *reinterpret_cast<const uint32_t*>(scl + (16 * R + btok) * kLdsScaleRow + 4 * kg);
+        mfma_step<R>(w, sw, a0, a1, sa, acc);
+      }
     }
   }
-  if constexpr (EPI) {
-    __shared__ EpiSmem<MT, NW> sm;
-    lmhead_epilogue<MT, NW, NV>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
-  }
+  __syncthreads();  // every wave is done with its slot before the reduction reuses the LDS
+  mfma_finish<MT, R, NW, EPI>(p, acc, reinterpret_cast<float*>(lds4), tile0);
 }
 
 __global__ void reset_state_init_kernel(char* state, int M, int window, size_t sbytes) {
@@ -830,7 +1018,7 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2 };
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3 };
 
 struct Variant {
   const char* name;
@@ -838,6 +1026,8 @@ struct Variant {
   int mt, g, r, nw, p;
   void (*plain)(GemvParams);
   void (*epi)(GemvParams);
+  void (*plain_k64)(GemvParams);  // LDS-staged kernel only: K % 64 == 0 instantiations
+  void (*epi_k64)(GemvParams);
 };
 
 #define VALU_V(MT, G, R, NW, P)                                                              \
@@ -856,6 +1046,13 @@ struct Variant {
         gemv_mfma_kernel<MT, R, NW, P, false>, gemv_mfma_kernel<MT, R, NW, P, true>  \
   }
 
+#define LMFMA_V(MT, R, NW, P)                                                                        \
+  Variant {                                                                                        \
+    "lmfma_m" #MT "_r" #R "_w" #NW "_p" #P, LMFMA, MT, 16, R, NW, P,                               \
+        gemv_lmfma_kernel<MT, R, NW, P, false, false>, gemv_lmfma_kernel<MT, R, NW, P, false, true>, \
+        gemv_lmfma_kernel<MT, R, NW, P, true, false>, gemv_lmfma_kernel<MT, R, NW, P, true, true>    \
+  }
+
 const Variant kVariants[] = {
     // direct VALU (no LDS), one and two tokens
     DIRECT_V(1, 16, 1, 4, 1), DIRECT_V(1, 16, 2, 4, 1), DIRECT_V(1, 32, 1, 4, 1), DIRECT_V(1, 32, 2, 4, 1),
@@ -868,6 +1065,13 @@ const Variant kVariants[] = {
     MFMA_V(2, 1, 4, 1), MFMA_V(2, 2, 8, 1), MFMA_V(2, 1, 8, 2), MFMA_V(4, 1, 4, 1), MFMA_V(4, 2, 8, 1),
     MFMA_V(4, 1, 8, 2), MFMA_V(8, 1, 4, 1), MFMA_V(8, 1, 8, 1), MFMA_V(8, 2, 4, 1), MFMA_V(8, 2, 8, 1),
     MFMA_V(8, 1, 4, 2), MFMA_V(8, 1, 8, 2), MFMA_V(8, 2, 8, 2), MFMA_V(8, 1, 16, 1),
+    // LDS-staged MFMA
+    LMFMA_V(2, 2, 4, 1), LMFMA_V(2, 2, 4, 2), LMFMA_V(4, 2, 4, 1), LMFMA_V(4, 2, 4, 2), LMFMA_V(4, 1, 8, 2),
+    LMFMA_V(4, 2, 8, 1), LMFMA_V(4, 2, 8, 2), LMFMA_V(8, 1, 4, 2), LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 4, 2),
+    LMFMA_V(8, 1, 8, 1), LMFMA_V(8, 1, 8, 2), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 2, 8, 2), LMFMA_V(8, 4, 4, 1),
+    LMFMA_V(8, 4, 4, 2), LMFMA_V(8, 1, 4, 1), LMFMA_V(8, 1, 2, 1), LMFMA_V(8, 2, 2, 1), LMFMA_V(8, 2, 2, 2),
+    LMFMA_V(8, 1, 8, 3), LMFMA_V(8, 1, 16, 1), LMFMA_V(4, 1, 8, 1), LMFMA_V(4, 2, 2, 1), LMFMA_V(4, 1, 4, 1),
+    LMFMA_V(2, 1, 4, 1), LMFMA_V(2, 1, 8, 1),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -890,10 +1094,10 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
       name = N >= 16384 ? "direct_m1_g32_r2_w4_p1" : K >= 12288 ? "direct_m1_g64_r1_w4_p1" : "direct_m1_g32_r1_w4_p1";
       break;
     case 2:
-      name = N >= 16384 ? "direct_m2_g16_r2_w4_p1" : K >= 8192 ? "direct_m2_g64_r1_w4_p1" : "direct_m2_g32_r1_w4_p1";
+      name = N >= 16384 ? "lmfma_m2_r2_w4_p1" : K >= 12288 ? "direct_m2_g64_r1_w4_p1" : "direct_m2_g32_r1_w4_p1";
       break;
-    case 4: name = N >= 8192 && K < 8192 ? "mfma_m4_r1_w4_p1" : "mfma_m4_r2_w8_p1"; break;
-    default: name = N >= 8192 && K < 8192 ? "mfma_m8_r1_w8_p1" : "mfma_m8_r2_w8_p1"; break;
+    case 4: name = K >= 8192 || N >= 65536 ? "lmfma_m4_r2_w8_p1" : "lmfma_m4_r2_w4_p1"; break;
+    default: name = K >= 12288 || N >= 65536 ? "lmfma_m8_r2_w8_p1" : "lmfma_m8_r1_w4_p1"; break;
   }
   return find_variant(name);
 }
@@ -909,13 +1113,18 @@ size_t reset_state_bytes(int window) {
 
 GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   int vi = -1;
+  // the LDS-staged kernel addresses a row tile and the activation with
+  // 32-bit buffer offsets
+  auto fits = [&](int i) { return kVariants[i].kind != LMFMA || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31); };
   // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
   // compiled token count covers M
   if (const char* env = getenv("NVFP4_GEMV_VARIANT")) {
     const int i = find_variant(env);
-    if (i >= 0 && kVariants[i].mt >= M) vi = i;
+    if (i >= 0 && kVariants[i].mt >= M && fits(i)) vi = i;
   }
   if (vi < 0) vi = default_variant(M, N, K, epi);
+  if (!fits(vi)) vi = find_variant(mt_of(M) <= 2 ? "direct_m2_g64_r1_w4_p1" : mt_of(M) <= 4 ? "mfma_m4_r2_w8_p1"
+                                                                                       : "mfma_m8_r2_w8_p1");
   const Variant& v = kVariants[vi];
   GemvConfig c{};
   c.variant = vi;
@@ -926,11 +1135,15 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
-  if (v.kind == MFMA) {
+  if (v.kind == MFMA || v.kind == LMFMA) {
     c.kp = (int)K;
     c.rows_per_wg = (int64_t)16 * v.r;
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
-    c.lds_bytes = (int64_t)v.nw * v.r * 4 * 64 * 4;
+    c.lds_bytes = (int64_t)v.nw * v.r * 4 * 64 * 4;  // partial tiles of the final reduction
+    if (v.kind == LMFMA) {
+      const int64_t slots = (int64_t)v.nw * (16 * v.r + 8) * (144 + 20);
+      if (slots > c.lds_bytes) c.lds_bytes = slots;
+    }
   } else if (v.kind == VALU) {
     int64_t kp = budget / v.mt / 512 * 512;
     const int64_t kr = (K + 127) / 128 * 128;
@@ -986,6 +1199,7 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   }
   const Variant& v = kVariants[cfg.variant];
   void (*fn)(GemvParams) = epi ? v.epi : v.plain;
+  if (v.plain_k64 && K % 64 == 0) fn = epi ? v.epi_k64 : v.plain_k64;
   hipLaunchKernelGGL(fn, dim3((unsigned)cfg.grid), dim3(v.nw * 64), (size_t)cfg.lds_bytes, stream, p);
   return hipGetLastError();
 }
