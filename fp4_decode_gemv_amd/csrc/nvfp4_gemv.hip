@@ -52,9 +52,10 @@
 // Optional LM-head epilogue (ReSET project page, "Step-aware temperature
 // scaling"; reading notes sections 3.1, 4.1-4.3): each workgroup also
 // writes per-token softmax partials (max, sum e^(z-max), sum e^(z-max)(z-max))
-// of its logits to the workspace; the last workgroup to finish (atomic
-// counter, reset by that workgroup) merges them in a fixed order, computes
-// the entropy and runs the ReSET update on the device-resident state.
+// of its logits to the workspace; a second launch with one workgroup per
+// token merges them in a fixed order, computes the entropy and runs the
+// ReSET update on the device-resident state.  No counters or atomics, so
+// the pair replays in a graph as launched.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -84,8 +85,6 @@ struct GemvParams {
   float* y;
   // LM-head epilogue (used only by the EPI instantiations)
   EpilogueArgs epi;
-  unsigned* counter;       // epilogue: groups of workgroups done
-  unsigned* group_counter; // epilogue: [groups] workgroups done in each group
   float* partials;         // epilogue: [row tiles][MT][4] = {max, S, T, -}
   size_t state_bytes;      // bytes per ReSET state
 };
@@ -159,24 +158,38 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int q) {
 // with their token index and a validity flag.
 // ----------------------------------------------------------------------------
 
-// Device-scope (agent) relaxed atomic store: on gfx950 it is written
-// through to the device coherence point, so no whole-L2 write-back is
-// needed to publish it to other workgroups.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-lane reductions over a wave64 with DPP (no LDS traffic): within each
+// row of 16 lanes by rotations by 8 and 4 and quad permutations, then across
+// the four rows through readlane in a fixed order, so every lane gets the
+// same, reproducible result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
-
-constexpr int kEpiGroup = 32;  // workgroups per first-level epilogue counter
-
-template <int MT, int NW>
-struct EpiSmem {
-  float wred[NW][MT][2];
-  float gmax[MT];
-  float mred[NW * 64];
-  float sred[NW * 64];
-  float tred[NW * 64];
-  unsigned last;
-};
+__device__ __forceinline__ float rowsum4(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<0x128>(x);  // row_ror:8
+  x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  return rowsum4(x);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0x128>(x));
+  x = fmaxf(x, dpp<0x124>(x));
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  const float a = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16)));
+  const float b = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32)),
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48)));
+  return fmaxf(a, b);
+}
 
 // Merge two softmax partials (m, S, T) with S = sum e^(z-m),
 // T = sum e^(z-m) (z-m):  m = max, S = S_a e^(m_a-m) + S_b e^(m_b-m),
@@ -197,156 +210,106 @@ __device__ __forceinline__ void merge_partial(float& m, float& S, float& T, floa
   m = mn;
 }
 
-template <int MT, int NW, int NV>
-__device__ void lmhead_epilogue(const GemvParams& p, const float (&val)[NV], const int (&tok)[NV],
-                                const bool (&ok)[NV], EpiSmem<MT, NW>& sm, int64_t tile, int ntiles) {
-  constexpr int NT = NW * 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // ---- tile maximum per token ----
-  float mx[MT];
+// LM-head epilogue, part 1 (in the GEMV kernel): the softmax partials
+// (max, S, T) of every token over this workgroup's ROWS rows.  Each thread
+// passes NV logits with their token, their row within the tile and two
+// flags: `own` (this thread owns the (token, row) slot: every slot of a
+// token < M is owned by exactly one thread) and `ok` (the row exists).  The
+// slots go through LDS (one barrier); wave w then reduces tokens w, w+NW, ...
+// with DPP and writes {max, S, T, 0} to partials[tile][token].
+template <int MT, int ROWS, int NV>
+__device__ __forceinline__ void lmhead_partials(const GemvParams& p, const float (&val)[NV], const int (&tok)[NV],
+                                                const int (&rowt)[NV], const bool (&own)[NV], const bool (&ok)[NV],
+                                                int64_t tile) {
+  static_assert(ROWS <= 64, "one logit per lane in the reduction");
+  __shared__ float slot[MT][ROWS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    mx[m] = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (ok[i] && tok[i] == m) mx[m] = fmaxf(mx[m], val[i]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], o, 64));
+  for (int i = 0; i < NV; ++i)
+    if (own[i]) slot[tok[i]][rowt[i]] = ok[i] ? val[i] : -INFINITY;
+  __syncthreads();
+  for (int m = wave; m < p.M; m += nw) {
+    const float x = lane < ROWS ? slot[m][lane] : -INFINITY;
+    const float mx = wave_max(x);  // finite: a tile holds at least one row
+    const float d = x - mx;
+    const float e = x == -INFINITY ? 0.0f : expf(d);
+    const float S = wave_sum(e);
+    const float T = wave_sum(e == 0.0f ? 0.0f : e * d);
+    if (lane == 0)
+      *reinterpret_cast<float4*>(p.partials + (tile * MT + m) * 4) = make_float4(mx, S, T, 0.0f);
   }
-  if (lane == 0)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) sm.wred[wave][m][0] = mx[m];
-  __syncthreads();
-  if (threadIdx.x < MT) {
-    float v = -INFINITY;
-    for (int w = 0; w < NW; ++w) v = fmaxf(v, sm.wred[w][threadIdx.x][0]);
-    sm.gmax[threadIdx.x] = v;
-  }
-  __syncthreads();
-  // ---- tile sums S = sum e^(z-max), T = sum e^(z-max)(z-max) per token ----
-  float S[MT], T[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    S[m] = 0.0f;
-    T[m] = 0.0f;
-    const float gm = sm.gmax[m];
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (ok[i] && tok[i] == m) {
-        const float d = val[i] - gm;
-        const float e = expf(d);
-        S[m] += e;
-        T[m] = __builtin_fmaf(e, d, T[m]);
-      }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      S[m] += __shfl_xor(S[m], o, 64);
-      T[m] += __shfl_xor(T[m], o, 64);
-    }
-  }
-  __syncthreads();
-  if (lane == 0)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      sm.wred[wave][m][0] = S[m];
-      sm.wred[wave][m][1] = T[m];
-    }
-  __syncthreads();
-  if (threadIdx.x < MT) {
-    float s = 0.0f, t = 0.0f;
-    for (int w = 0; w < NW; ++w) {
-      s += sm.wred[w][threadIdx.x][0];
-      t += sm.wred[w][threadIdx.x][1];
-    }
-    float* dst = p.partials + (tile * MT + threadIdx.x) * 4;  // {max, S, T, unused}
-    st_agent(dst, sm.gmax[threadIdx.x]);
-    st_agent(dst + 1, s);
-    st_agent(dst + 2, t);
-  }
-  // ---- the last workgroup to finish merges all partials ----
-  // The partials were written through to the device coherence point; wait
-  // until those stores have completed, then count this workgroup in: first
-  // in its group of kEpiGroup tiles, and the last of a group in the top
-  // counter (one hot counter for thousands of workgroups serializes them).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int64_t grp = tile / kEpiGroup;
-    const int64_t ngroups = (ntiles + kEpiGroup - 1) / kEpiGroup;
-    const int64_t gsize = ntiles - grp * kEpiGroup < kEpiGroup ? ntiles - grp * kEpiGroup : kEpiGroup;
-    unsigned last = 0u;
-    if (__hip_atomic_fetch_add(p.group_counter + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        (unsigned)gsize - 1u) {
-      __hip_atomic_store(p.group_counter + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                     (unsigned)ngroups - 1u
-                 ? 1u
-                 : 0u;
-    }
-    sm.last = last;
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  // drop any stale cached copy of the partials, then read them with wide loads
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// LM-head epilogue, part 2 (its own launch, one workgroup per token, after
+// the GEMV): merge the token's partials of all row tiles in a fixed order,
+// H = log S - T/S (natural log), then the ReSET update of the token's
+// sequence state and its temperature.
+constexpr int kMergeThreads = 1024;
+
+__global__ __launch_bounds__(kMergeThreads) void lmhead_merge_kernel(GemvParams p, int mt, int ntiles) {
+  __shared__ float mred[kMergeThreads], sred[kMergeThreads], tred[kMergeThreads];
+  const int m = blockIdx.x;
+  if (m >= p.M) return;
   const float4* part = reinterpret_cast<const float4*>(p.partials);
-  for (int m = 0; m < p.M; ++m) {
-    // each thread merges tiles threadIdx.x, +NT, ... in order; then a fixed tree
-    float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
-    for (int b = threadIdx.x; b < ntiles; b += NT) {
-      const float4 q = part[(int64_t)b * MT + m];
-      merge_partial(gm, Sm, Tm, q.x, q.y, q.z);
-    }
-    sm.mred[threadIdx.x] = gm;
-    sm.sred[threadIdx.x] = Sm;
-    sm.tred[threadIdx.x] = Tm;
-    __syncthreads();
-    for (int s = NT / 2; s >= 1; s >>= 1) {
-      if (threadIdx.x < s) {
-        float a = sm.mred[threadIdx.x], sa = sm.sred[threadIdx.x], ta = sm.tred[threadIdx.x];
-        merge_partial(a, sa, ta, sm.mred[threadIdx.x + s], sm.sred[threadIdx.x + s], sm.tred[threadIdx.x + s]);
-        sm.mred[threadIdx.x] = a;
-        sm.sred[threadIdx.x] = sa;
-        sm.tred[threadIdx.x] = ta;
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-      const double Sd = sm.sred[0], Td = sm.tred[0];
-      const float H = (float)(log(Sd) - Td / Sd);
-      p.epi.entropy[m] = H;
-      // ---- ReSET update: update with H first, then decide ----
-      ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
-      float* ring = reinterpret_cast<float*>(st + 1);
-      // the ring holds the window the state was initialised with; never
-      // index past the smaller of that and the caller's window
-      int w = st->window < p.epi.window ? st->window : p.epi.window;
-      if (w < 1) w = 1;
-      const double h = (double)H;
-      if (st->count == 0 || p.epi.step_start[m]) {
-        st->step_sum = 0.0;
-        st->step_len = 0;
-      }
-      ring[st->count % w] = H;
-      st->count += 1;
-      st->sum_all += h;
-      st->step_sum += h;
-      st->step_len += 1;
-      const int64_t nwin = st->count < w ? st->count : w;
-      double wsum = 0.0;
-      for (int64_t i = st->count - nwin; i < st->count; ++i) wsum += (double)ring[i % w];
-      const double hbar = st->sum_all / (double)st->count;
-      const double hstep = st->step_len <= w ? wsum / (double)nwin : st->step_sum / (double)st->step_len;
-      const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
-      float T_t;
-      if (p.epi.mode == 1) T_t = p.epi.t_base;
-      else T_t = h < tau ? p.epi.t_low : p.epi.t_high;
-      p.epi.temperature[m] = T_t;
+  // thread t merges tiles t, t + NT, ... in order; then a fixed tree
+  float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
+  int b = threadIdx.x;
+  for (; b + 3 * kMergeThreads < ntiles; b += 4 * kMergeThreads) {
+    float4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = part[(int64_t)(b + j * kMergeThreads) * mt + m];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) merge_partial(gm, Sm, Tm, q[j].x, q[j].y, q[j].z);
+  }
+  for (; b < ntiles; b += kMergeThreads) {
+    const float4 q = part[(int64_t)b * mt + m];
+    merge_partial(gm, Sm, Tm, q.x, q.y, q.z);
+  }
+  mred[threadIdx.x] = gm;
+  sred[threadIdx.x] = Sm;
+  tred[threadIdx.x] = Tm;
+  __syncthreads();
+  for (int s = kMergeThreads / 2; s >= 1; s >>= 1) {
+    if (threadIdx.x < s) {
+      float a = mred[threadIdx.x], sa = sred[threadIdx.x], ta = tred[threadIdx.x];
+      merge_partial(a, sa, ta, mred[threadIdx.x + s], sred[threadIdx.x + s], tred[threadIdx.x + s]);
+      mred[threadIdx.x] = a;
+      sred[threadIdx.x] = sa;
+      tred[threadIdx.x] = ta;
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0)  // ready for the next call / graph replay
-    __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x != 0) return;
+  const double Sd = sred[0], Td = tred[0];
+  const float H = (float)(log(Sd) - Td / Sd);
+  p.epi.entropy[m] = H;
+  // ---- ReSET update: update with H first, then decide ----
+  ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
+  float* ring = reinterpret_cast<float*>(st + 1);
+  // the ring holds the window the state was initialised with; never index
+  // past the smaller of that and the caller's window
+  int w = st->window < p.epi.window ? st->window : p.epi.window;
+  if (w < 1) w = 1;
+  const double h = (double)H;
+  if (st->count == 0 || p.epi.step_start[m]) {
+    st->step_sum = 0.0;
+    st->step_len = 0;
+  }
+  ring[st->count % w] = H;
+  st->count += 1;
+  st->sum_all += h;
+  st->step_sum += h;
+  st->step_len += 1;
+  const int64_t nwin = st->count < w ? st->count : w;
+  double wsum = 0.0;
+  for (int64_t i = st->count - nwin; i < st->count; ++i) wsum += (double)ring[i % w];
+  const double hbar = st->sum_all / (double)st->count;
+  const double hstep = st->step_len <= w ? wsum / (double)nwin : st->step_sum / (double)st->step_len;
+  const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
+  float T_t;
+  if (p.epi.mode == 1) T_t = p.epi.t_base;
+  else T_t = h < tau ? p.epi.t_low : p.epi.t_high;
+  p.epi.temperature[m] = T_t;
 }
 
 // ----------------------------------------------------------------------------
@@ -496,8 +459,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_valu_kernel(GemvParams p) {
       if (ok[r * MT + m]) p.y[(int64_t)m * N + row[r]] = out[r * MT + m];
 
   if constexpr (EPI) {
-    __shared__ EpiSmem<MT, NW> sm;
-    lmhead_epilogue<MT, NW, R * MT>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
+    int rowt[R * MT];
+    bool own[R * MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        rowt[r * MT + m] = (int)(row[r] - tile0);
+        own[r * MT + m] = g == 0 && m < M;
+      }
+    lmhead_partials<MT, R * NW * (64 / G), R * MT>(p, out, tok, rowt, own, ok, blockIdx.x);
   }
 }
 
@@ -656,8 +627,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
       if (ok[r * MT + m]) p.y[(int64_t)m * N + row[r]] = out[r * MT + m];
 
   if constexpr (EPI) {
-    __shared__ EpiSmem<MT, NW> sm;
-    lmhead_epilogue<MT, NW, R * MT>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
+    int rowt[R * MT];
+    bool own[R * MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        rowt[r * MT + m] = (int)(row[r] - tile0);
+        own[r * MT + m] = g == 0 && m < M;
+      }
+    lmhead_partials<MT, R * NW * (64 / G), R * MT>(p, out, tok, rowt, own, ok, blockIdx.x);
   }
 }
 
@@ -719,28 +698,28 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
   // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token li
   constexpr int NV = (R * 4 + NW - 1) / NW;
   float out[NV];
-  int tok[NV];
-  bool ok[NV];
+  int tok[NV], rowt[NV];
+  bool ok[NV], own[NV];
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     const int rv = wave + u * NW;
     out[u] = 0.0f;
-    tok[u] = li;
-    ok[u] = false;
+    tok[u] = li < MT ? li : 0;
+    rowt[u] = 0;
+    ok[u] = own[u] = false;
     if (rv < R * 4) {
       const int r = rv >> 2, v = rv & 3;
       float sum = 0.0f;
       for (int w = 0; w < NW; ++w) sum += red[((w * R + r) * 4 + v) * 64 + lane];
       const int64_t row = tile0 + 16 * r + 4 * kg + v;
       out[u] = sum * scale;
+      rowt[u] = 16 * r + 4 * kg + v;
+      own[u] = li < M;
       ok[u] = li < M && row < N;
       if (ok[u]) p.y[(int64_t)li * N + row] = out[u];
     }
   }
-  if constexpr (EPI) {
-    __shared__ EpiSmem<MT, NW> sm;
-    lmhead_epilogue<MT, NW, NV>(p, out, tok, ok, sm, blockIdx.x, gridDim.x);
-  }
+  if constexpr (EPI) lmhead_partials<MT, 16 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
 }
 
 // ----------------------------------------------------------------------------
@@ -1158,10 +1137,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = 0;
   }
-  // workspace (epilogue only): [top counter | group counters | per-workgroup softmax partials]
-  c.ws_group_counters = 256;
-  c.ws_epi_partials = c.ws_group_counters + align256((c.grid + kEpiGroup - 1) / kEpiGroup * 4);
-  c.ws_bytes = epi ? c.ws_epi_partials + align256(c.grid * c.mt * 4 * 4) : 0;
+  // workspace (epilogue only): per-workgroup softmax partials
+  c.ws_bytes = epi ? align256(c.grid * c.mt * 4 * 4) : 0;
   return c;
 }
 
@@ -1192,15 +1169,18 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   char* wsb = reinterpret_cast<char*>(ws);
   if (epi) {
     p.epi = *epi;
-    p.counter = reinterpret_cast<unsigned*>(wsb);
-    p.group_counter = reinterpret_cast<unsigned*>(wsb + cfg.ws_group_counters);
-    p.partials = reinterpret_cast<float*>(wsb + cfg.ws_epi_partials);
+    p.partials = reinterpret_cast<float*>(wsb);
     p.state_bytes = reset_state_bytes(epi->window);
   }
   const Variant& v = kVariants[cfg.variant];
   void (*fn)(GemvParams) = epi ? v.epi : v.plain;
   if (v.plain_k64 && K % 64 == 0) fn = epi ? v.epi_k64 : v.plain_k64;
   hipLaunchKernelGGL(fn, dim3((unsigned)cfg.grid), dim3(v.nw * 64), (size_t)cfg.lds_bytes, stream, p);
+  if (epi) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(M), dim3(kMergeThreads), 0, stream, p, cfg.mt, (int)cfg.grid);
+  }
   return hipGetLastError();
 }
 

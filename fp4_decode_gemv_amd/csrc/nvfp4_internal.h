@@ -59,7 +59,7 @@ struct GemvConfig {
   int64_t lds_bytes;  // dynamic LDS per workgroup
   // workspace layout (byte offset of the epilogue partials) and total size
   // (0 = none needed)
-  int64_t ws_group_counters, ws_epi_partials, ws_bytes;
+  int64_t ws_bytes;
 };
 
 GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi);

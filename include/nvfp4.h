@@ -36,9 +36,9 @@
  *   - Workspace `ws` is caller-owned device scratch of at least
  *     nvfp4_workspace_size(op, M, N, K) bytes; it must be zero-filled once
  *     after allocation (nvfp4_workspace_init does that with a kernel).
- *     Kernels that use counters in it reset them before they finish, so
- *     graph replays are safe.  Calls that share one workspace must be
- *     ordered on one stream.
+ *     It holds only per-call intermediates (no state carried between
+ *     calls), so graph replays are safe.  Calls that share one workspace
+ *     must be ordered on one stream.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
