@@ -26,7 +26,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-bool shape_ok_k(int64_t K) { return K >= 32 && K % 32 == 0 && K <= ((int64_t)1 << 40); }
+bool shape_ok_k(int64_t K) { return K >= 32 && K % 32 == 0 && K <= ((int64_t)1 << 24); }
 bool shape_ok(int M, int64_t N, int64_t K) {
   return M >= 1 && M <= 8 && N >= 1 && N <= ((int64_t)1 << 40) && shape_ok_k(K);
 }
@@ -63,7 +63,7 @@ const char* nvfp4_status_str(int status) {
   switch (status) {
     case NVFP4_OK: return "NVFP4_OK";
     case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
-    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: need 1<=M<=8, N>=1, K>=32, K%32==0";
+    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: need 1<=M<=8, N>=1, 32<=K<=2^24, K%32==0";
     case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
     case NVFP4_ERR_DEVICE: return "NVFP4_ERR_DEVICE: the current device is not a gfx950";

@@ -217,66 +217,102 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 // hardware over every midpoint and its neighbours).  The division before it
 // stays the IEEE one.
 //   mode GS_SELF: every workgroup loads the whole tensor (at most
-//   kActSelfElems elements, every load in flight at once) for the global
-//   amax and then quantizes, from registers, the chunk whose index is its
-//   own workgroup index, so no element is read twice by one workgroup.
+//   kActSelfElems elements, all loads in flight at once) for the global
+//   amax, so one launch does the whole step.
+// Loads go through a buffer resource over x: chunks past the end read as
+// zero, so no load is predicated and no loaded value is used before the
+// whole batch has been issued.  The amax of bf16 values is the unsigned max
+// of their sign-cleared bit patterns (non-negative floats order like their
+// bits), two per packed 16-bit max; wave maxima use DPP.
 constexpr int kActThreads = 1024;
 constexpr int kActChunks = 16;                            // 16-byte loads per thread in GS_SELF
 constexpr int kActSelfElems = kActThreads * 8 * kActChunks;
+constexpr int kBufferWord3 = 0x00020000;                  // gfx9-family raw buffer resource, word 3
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// max over the wave (every lane gets it)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0x128>(x));  // row_ror:8
+  x = max(x, dpp_u32<0x124>(x));  // row_ror:4
+  x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return max(a, b);
+}
+
+// max over the workgroup (kActThreads threads); one barrier
+__device__ __forceinline__ uint32_t wg_max_u32(uint32_t x, uint32_t* red) {
+  x = wave_max_u32(x);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  const uint4* r4 = reinterpret_cast<const uint4*>(red);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kActThreads / 256; ++i) {
+    const uint4 v = r4[i];
+    m = max(m, max(max(v.x, v.y), max(v.z, v.w)));
+  }
+  return m;
 }
 
 __global__ __launch_bounds__(kActThreads) void quantize_act_kernel(
     const uint16_t* __restrict__ x, int64_t nelem, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode,
     const float* __restrict__ partials, int n_parts) {
-  __shared__ float red[kActThreads / 64];
-  const int64_t mine = ((int64_t)blockIdx.x * kActThreads + threadIdx.x) * 8;  // first element of this thread
-  uint4 raw = make_uint4(0, 0, 0, 0);
+  __shared__ __align__(16) uint32_t red[kActThreads / 64];
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, (int)(nelem * 2), kBufferWord3);
+  const int mine = ((int)blockIdx.x * kActThreads + (int)threadIdx.x) * 8;  // first element of this thread
+  const u32x4_t raw = __builtin_amdgcn_raw_buffer_load_b128(xr, mine * 2, 0, 0);
   float s_g;
   if (mode == GS_SELF) {
-    uint4 v[kActChunks];
+    u32x4_t v[kActChunks];
 #pragma unroll
-    for (int j = 0; j < kActChunks; ++j) {
-      const int64_t i = ((int64_t)j * kActThreads + threadIdx.x) * 8;
-      v[j] = i < nelem ? *reinterpret_cast<const uint4*>(x + i) : make_uint4(0, 0, 0, 0);
-    }
-    float m = 0.0f;
+    for (int j = 0; j < kActChunks; ++j)
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (j * kActThreads + (int)threadIdx.x) * 16, 0, 0);
+    uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kActChunks; ++j) {
-      const uint32_t w[4] = {v[j].x & 0x7FFF7FFFu, v[j].y & 0x7FFF7FFFu, v[j].z & 0x7FFF7FFFu,
-                             v[j].w & 0x7FFF7FFFu};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(bf16_to_f32(w[i] & 0xFFFFu), bf16_to_f32(w[i] >> 16)));
-      if (j == (int)blockIdx.x) raw = v[j];
-    }
-    s_g = wg_max<kActThreads>(m, red) / 2688.0f;
+    for (int j = 0; j < kActChunks; ++j)
+      m = pk_max_u16(pk_max_u16(m, v[j][0] & 0x7FFF7FFFu), pk_max_u16(v[j][1] & 0x7FFF7FFFu, pk_max_u16(v[j][2] & 0x7FFF7FFFu, v[j][3] & 0x7FFF7FFFu)));
+    m = max(m & 0xFFFFu, m >> 16);
+    s_g = bf16_to_f32(wg_max_u32(m, red)) / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
+  } else if (mode == GS_STATIC) {
+    s_g = *gscale;
   } else {
-    if (mine < nelem) raw = *reinterpret_cast<const uint4*>(x + mine);
-    if (mode == GS_STATIC) {
-      s_g = *gscale;
-    } else {
-      float m = 0.0f;
-      for (int i = threadIdx.x; i < n_parts; i += kActThreads) m = fmaxf(m, partials[i]);
-      s_g = wg_max<kActThreads>(m, red) / 2688.0f;
-      if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
-    }
+    uint32_t m = 0;  // partial maxima are non-negative floats: compare their bits
+    for (int i = threadIdx.x; i < n_parts; i += kActThreads) m = max(m, __float_as_uint(partials[i]));
+    s_g = __uint_as_float(wg_max_u32(m, red)) / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
   }
-  const uint32_t rw[4] = {raw.x, raw.y, raw.z, raw.w};
   float v[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_to_f32(rw[i] & 0xFFFFu);
-    v[2 * i + 1] = bf16_to_f32(rw[i] >> 16);
+    v[2 * i] = bf16_to_f32(raw[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(raw[i] >> 16);
   }
-  // block amax over the two halves (neighbouring lanes)
+  // block amax over the two halves (neighbouring lanes 2k, 2k+1)
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(amax))));
   if (mine < nelem) {
     float tb = 0.0f;
     if (s_g != 0.0f) {

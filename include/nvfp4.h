@@ -30,7 +30,7 @@
  *     status means nothing was launched and no output was touched.
  *   - Device pointers must be 16-byte aligned (NVFP4_ERR_ALIGN otherwise),
  *     except scalars (global scales, entropy/temperature outputs, flags).
- *   - Shapes: 1 <= M <= 8, N >= 1, K >= 32, K % 32 == 0.
+ *   - Shapes: 1 <= M <= 8, N >= 1, 32 <= K <= 2^24, K % 32 == 0.
  *   - Outputs must not overlap inputs (NVFP4_ERR_ARG).
  *   - Non-finite inputs give undefined (but memory-safe) results.
  *   - Workspace `ws` is caller-owned device scratch of at least
@@ -53,7 +53,8 @@ extern "C" {
 typedef enum {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = -1,      /* a required pointer is NULL                     */
-  NVFP4_ERR_SHAPE = -2,     /* M not in [1,8], N < 1, K < 32 or K % 32 != 0    */
+  NVFP4_ERR_SHAPE = -2,     /* M not in [1,8], N < 1, K outside [32, 2^24] or
+                               K % 32 != 0                                    */
   NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned        */
   NVFP4_ERR_WORKSPACE = -4, /* ws is NULL or ws_bytes is too small             */
   NVFP4_ERR_DEVICE = -5,    /* the current HIP device is not a gfx950         */
