@@ -45,8 +45,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "8620d42eca412419884dd1be88ae4127ca1974f9a0b84ea0f7767874c28c4350",
-    "bytes_per_step": 1115083354,
+    "sha256": "de81e091a9d0ebc5669c0302995e407e1e6db00fa32b3a10b5e3437e7a3a388c",
+    "bytes_per_step": 1117117492,
 }
 
 

@@ -932,16 +932,25 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
 
   // P register buffers in a ring: the loads of steps i+1 .. i+P-1 stay in
   // flight while step i is staged and computed; a buffer is refilled right
-  // after its contents went to LDS.
-  LmfmaStep<R> buf[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j)
-    if (j < n) load(buf[j], wave + j * NW);
-  for (int i0 = 0; i0 < n; i0 += P) {
+  // after its contents went to LDS.  Loads and staging are unconditional
+  // (the step index is clamped to the wave's last step, so the few extra
+  // loads re-read data already in flight) and only the compute is skipped
+  // past the end: with no load behind a branch, the compiler's wait counts
+  // stay exact and the P-deep pipeline is kept.
+  if (n > 0) {
+    LmfmaStep<R> buf[P];
+    // buffers are filled one after the other, never interleaved, so the
+    // wait before staging buffer j counts exactly the later buffers' loads
 #pragma unroll
     for (int j = 0; j < P; ++j) {
-      const int i = i0 + j;
-      if (i < n) {
+      load(buf[j], wave + (j < n ? j : n - 1) * NW);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int i0 = 0; i0 < n; i0 += P) {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        const int i = i0 + j;
+        const int si = wave + (i < n ? i : n - 1) * NW;  // the step held by buf[j]
         // stage the step (the previous step's operand reads are done: fence)
         wave_lds_fence();
 #pragma unroll
@@ -950,27 +959,31 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
           for (int h = 0; h < 2; ++h)
             *reinterpret_cast<uint4*>(slot + (16 * r + 8 * h + lq) * kLdsCodeRow + 16 * lc) = buf[j].w[r][h];
           *reinterpret_cast<uint32_t*>(scl + (16 * r + sq) * kLdsScaleRow + 4 * sp) =
-              scale_word(buf[j].ws[r], buf[j].wsh[r], wave + i * NW);
+              scale_word(buf[j].ws[r], buf[j].wsh[r], si);
         }
         *reinterpret_cast<uint4*>(slot + (16 * R + lq) * kLdsCodeRow + 16 * lc) = buf[j].a;
         if (sq < 8)
           *reinterpret_cast<uint32_t*>(scl + (16 * R + sq) * kLdsScaleRow + 4 * sp) =
-              scale_word(buf[j].as, buf[j].ash, wave + i * NW);
+              scale_word(buf[j].as, buf[j].ash, si);
         wave_lds_fence();
-        if (i + P < n) load(buf[j], wave + (i + P) * NW);
-        // read it back in the operand layout
-        uint4 w[R][2];
-        uint32_t sw[R];
+        __builtin_amdgcn_sched_barrier(0);
+        load(buf[j], wave + (i + P < n ? i + P : n - 1) * NW);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < n) {
+          // read it back in the operand layout
+          uint4 w[R][2];
+          uint32_t sw[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          w[r][0] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg);
-          w[r][1] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg + 16);
-          sw[r] = *reinterpret_cast<const uint32_t*>(scl + (16 * r + li) * kLdsScaleRow + 4 * kg);
+          for (int r = 0; r < R; ++r) {
+            w[r][0] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg);
+            w[r][1] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg + 16);
+            sw[r] = *reinterpret_cast<const uint32_t*>(scl + (16 * r + li) * kLdsScaleRow + 4 * kg);
+          }
+          const uint4 a0 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg + 16);
+          const uint32_t sa = *reinterpret_cast<const uint32_t*>(scl + (16 * R + btok) * kLdsScaleRow + 4 * kg);
+          mfma_step<R>(w, sw, a0, a1, sa, acc);
         }
-        const uint4 a0 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg + 16);
-        const uint32_t sa = *reinterpret_cast<const uint32_t*>(scl + (16 * R + btok) * kLdsScaleRow + 4 * kg);
-        mfma_step<R>(w, sw, a0, a1, sa, acc);
       }
     }
   }
