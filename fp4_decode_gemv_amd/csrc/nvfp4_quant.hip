@@ -217,16 +217,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 // hardware over every midpoint and its neighbours).  The division before it
 // stays the IEEE one.
 //   mode GS_SELF: every workgroup loads the whole tensor (at most
-//   kActSelfElems elements, all loads in flight at once) for the global
-//   amax, so one launch does the whole step.
+//   kActSelfElems elements, 16 loads per thread in flight per round) for
+//   the global amax, so one launch does the whole step.  Workgroups are
+//   small (T threads, 8 elements each): the per-element work (an IEEE
+//   division per element) then spreads over many CUs instead of queueing
+//   on the SIMDs of one.
 // Loads go through a buffer resource over x: chunks past the end read as
 // zero, so no load is predicated and no loaded value is used before the
 // whole batch has been issued.  The amax of bf16 values is the unsigned max
 // of their sign-cleared bit patterns (non-negative floats order like their
 // bits), two per packed 16-bit max; wave maxima use DPP.
-constexpr int kActThreads = 1024;
-constexpr int kActChunks = 16;                            // 16-byte loads per thread in GS_SELF
-constexpr int kActSelfElems = kActThreads * 8 * kActChunks;
+constexpr int kActBatch = 16;         // 16-byte amax loads per thread in flight at once
+constexpr int kActSelfElems = 131072;  // GS_SELF limit (above it: two launches)
 constexpr int kBufferWord3 = 0x00020000;                  // gfx9-family raw buffer resource, word 3
 
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
@@ -257,49 +259,51 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return max(a, b);
 }
 
-// max over the workgroup (kActThreads threads); one barrier
+// max over the workgroup (T threads); one barrier when T > 64
+template <int T>
 __device__ __forceinline__ uint32_t wg_max_u32(uint32_t x, uint32_t* red) {
   x = wave_max_u32(x);
+  if constexpr (T == 64) return x;
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  const uint4* r4 = reinterpret_cast<const uint4*>(red);
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < kActThreads / 256; ++i) {
-    const uint4 v = r4[i];
-    m = max(m, max(max(v.x, v.y), max(v.z, v.w)));
-  }
+  for (int i = 0; i < T / 64; ++i) m = max(m, red[i]);
   return m;
 }
 
-__global__ __launch_bounds__(kActThreads) void quantize_act_kernel(
+template <int T>
+__global__ __launch_bounds__(T) void quantize_act_kernel(
     const uint16_t* __restrict__ x, int64_t nelem, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode,
     const float* __restrict__ partials, int n_parts) {
-  __shared__ __align__(16) uint32_t red[kActThreads / 64];
+  __shared__ __align__(16) uint32_t red[T / 64];
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, (int)(nelem * 2), kBufferWord3);
-  const int mine = ((int)blockIdx.x * kActThreads + (int)threadIdx.x) * 8;  // first element of this thread
+  const int mine = ((int)blockIdx.x * T + (int)threadIdx.x) * 8;  // first element of this thread
   const u32x4_t raw = __builtin_amdgcn_raw_buffer_load_b128(xr, mine * 2, 0, 0);
   float s_g;
   if (mode == GS_SELF) {
-    u32x4_t v[kActChunks];
-#pragma unroll
-    for (int j = 0; j < kActChunks; ++j)
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (j * kActThreads + (int)threadIdx.x) * 16, 0, 0);
     uint32_t m = 0;
+    for (int base = 0; base < (int)nelem; base += T * 8 * kActBatch) {  // uniform trip count
+      u32x4_t v[kActBatch];
 #pragma unroll
-    for (int j = 0; j < kActChunks; ++j)
-      m = pk_max_u16(pk_max_u16(m, v[j][0] & 0x7FFF7FFFu), pk_max_u16(v[j][1] & 0x7FFF7FFFu, pk_max_u16(v[j][2] & 0x7FFF7FFFu, v[j][3] & 0x7FFF7FFFu)));
+      for (int j = 0; j < kActBatch; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (base + (j * T + (int)threadIdx.x) * 8) * 2, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kActBatch; ++j)
+        m = pk_max_u16(pk_max_u16(m, v[j][0] & 0x7FFF7FFFu),
+                       pk_max_u16(v[j][1] & 0x7FFF7FFFu, pk_max_u16(v[j][2] & 0x7FFF7FFFu, v[j][3] & 0x7FFF7FFFu)));
+    }
     m = max(m & 0xFFFFu, m >> 16);
-    s_g = bf16_to_f32(wg_max_u32(m, red)) / 2688.0f;
+    s_g = bf16_to_f32(wg_max_u32<T>(m, red)) / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
   } else if (mode == GS_STATIC) {
     s_g = *gscale;
   } else {
     uint32_t m = 0;  // partial maxima are non-negative floats: compare their bits
-    for (int i = threadIdx.x; i < n_parts; i += kActThreads) m = max(m, __float_as_uint(partials[i]));
-    s_g = __uint_as_float(wg_max_u32(m, red)) / 2688.0f;
+    for (int i = threadIdx.x; i < n_parts; i += T) m = max(m, __float_as_uint(partials[i]));
+    s_g = __uint_as_float(wg_max_u32<T>(m, red)) / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
   }
   float v[8];
@@ -360,9 +364,12 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint
     hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x, nelem,
                        partials);
   }
-  const int64_t grid = (nelem + (int64_t)kActThreads * 8 - 1) / ((int64_t)kActThreads * 8);
-  hipLaunchKernelGGL(quantize_act_kernel, dim3((unsigned)grid), dim3(kActThreads), 0, stream, x, nelem, codes,
-                     scales, gscale, (int)mode, partials, n_parts);
+  // workgroup size: small tensors spread over more CUs
+  const int threads = nelem <= 16384 ? 64 : nelem <= 65536 ? 256 : 1024;
+  const int64_t grid = (nelem + (int64_t)threads * 8 - 1) / ((int64_t)threads * 8);
+  auto fn = threads == 64 ? quantize_act_kernel<64> : threads == 256 ? quantize_act_kernel<256> : quantize_act_kernel<1024>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, stream, x, nelem, codes, scales, gscale, (int)mode,
+                     partials, n_parts);
   return hipGetLastError();
 }
 
