@@ -10,12 +10,17 @@ in HBM before timing starts.  Every projection has several packed copies
 that are rotated launch by launch, so no GEMV finds its weights in the
 256 MB Infinity Cache from an earlier launch.
 
+A step is captured once in a HIP graph (as a decode loop replays it; the
+dispatch choices are fixed at capture) and replayed; one graph per phase of
+the weight-copy rotation.
+
 Prints one JSON line:
   value        effective GB/s over the step = weight+scale bytes streamed per
                step / step time (quantization included)
   roofline     the GEMV kernel: algorithmic bytes of all GEMV launches of a
-               step / their summed average durations (HIP events on the
-               launch stream), against the 8 TB/s HBM peak
+               step / their summed average durations (each case: `reps`
+               back-to-back launches captured in a graph, HIP events around
+               its replay on the launch stream), against the 8 TB/s HBM peak
   cpu_baseline the CPU oracle (quantize + dequantize + fp64 GEMV) on a
                bounded row sample of the same projections, same byte formula
 """
@@ -24,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -149,62 +155,83 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     cases, wq, acts, samples = setup(args)
-    stream = torch.cuda.current_stream()
-    use = {c.name: 0 for c in cases}
+    # one non-default stream (default priority) for capture, replay and events
+    stream = torch.cuda.Stream()
 
-    def gemv(c, M):
+    def gemv(c, M, copy):
         x, aq, ws, gws, y = acts[(c.name, M)]
-        w = wq[c.name][use[c.name] % args.copies]
-        use[c.name] += 1
-        F.nvfp4_gemv_smallm(aq, w, y=y, ws=gws, stream=stream)
+        F.nvfp4_gemv_smallm(aq, wq[c.name][copy % args.copies], y=y, ws=gws, stream=stream)
 
     def quant(c, M):
         x, aq, ws, gws, y = acts[(c.name, M)]
         F.nvfp4_quantize_act(x, ws=ws, out=aq, stream=stream)
 
-    def step():
-        for M in M_LIST:
+    def step(s):
+        # launch i of a projection in the run reads packed copy i % copies
+        for mi, M in enumerate(M_LIST):
             for c in cases:
                 quant(c, M)
-                gemv(c, M)
+                gemv(c, M, s * len(M_LIST) + mi)
 
-    # ---------------- whole-step throughput ----------------
-    for _ in range(args.warmup):
-        step()
+    def capture(fn):
+        with torch.cuda.stream(stream):
+            fn()  # eager run first: nothing is lazily initialised inside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    # ---------------- whole-step throughput (graph replay) ----------------
+    period = args.copies // math.gcd(args.copies, len(M_LIST))
+    graphs = [capture(lambda s=s: step(s)) for s in range(period)]
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            graphs[i % period].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            graphs[i % period].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     bytes_per_step = sum(weight_bytes(c.N, c.K) for c in cases) * len(M_LIST)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log(args, f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s effective (quantization included)")
+    del graphs
 
-    # ---------------- per-kernel durations (HIP events on the launch stream) ----------------
-    # `reps` launches of one case back to back between two events: the
-    # average is the kernel's duration as the hardware runs it in a decode
-    # step (it agrees with rocprofv3's per-dispatch durations); an event pair
-    # around every single launch would add the event overhead to each.
+    # the same step launched eagerly from Python, for reference (host-bound)
+    with torch.cuda.stream(stream):
+        step(0)
+    torch.cuda.synchronize()
+    te = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - te) * 1e3 / 10
+    log(args, f"[bench] eager Python launches: {eager_ms * 1e3:.1f} us/step")
+
+    # ---------------- per-kernel durations ----------------
+    # `reps` launches of one case back to back, captured in a graph and
+    # timed by HIP events on the launch stream around its replay: the
+    # average is the kernel's duration as a decode step runs it (it agrees
+    # with rocprofv3's per-dispatch durations); host launch overhead is not
+    # in it.
     detail = []
     gemv_bytes = 0
     gemv_us = 0.0
 
     def b2b(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        e0.record(stream)
-        for _ in range(args.reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / args.reps
+        g = capture(lambda: [fn(i) for i in range(args.reps)])
+        return _replay_us(g, args.reps, stream)
 
     for c in cases:
         for M in M_LIST:
-            gus = b2b(lambda: gemv(c, M))
-            qus = b2b(lambda: quant(c, M))
+            gus = b2b(lambda i: gemv(c, M, i))
+            qus = b2b(lambda i: quant(c, M))
             wb = weight_bytes(c.N, c.K)
             detail.append({
                 "proj": c.name, "M": M, "N": c.N, "K": c.K, "weight_bytes": wb,
@@ -220,7 +247,7 @@ def main():
                       f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us")
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
 
-    extra = {}
+    extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4)}
     if not args.no_lmhead:
         extra["lm_head"] = bench_lm_head(args, stream)
     if not args.no_chain:
@@ -284,17 +311,38 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _b2b_us(fn, reps, stream):
+def _replay_us(g, reps, stream, replays=5):
+    """Average microseconds per launch of a graph holding `reps` launches:
+    one warm replay, then the mean over `replays` replays (HIP events on the
+    replay stream)."""
     import torch
 
-    fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        fn()
-    e1.record(stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    return e0.elapsed_time(e1) * 1e3 / (reps * replays)
+
+
+def _graph_us(fn, reps, stream):
+    """Capture `reps` calls of fn(i) in a graph on `stream` and time it."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(reps):
+            fn(i)
+    torch.cuda.synchronize()
+    us = _replay_us(g, reps, stream)
+    del g
+    return us
 
 
 def bench_lm_head(args, stream):
@@ -327,24 +375,20 @@ def bench_lm_head(args, stream):
         ews = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, case.N, case.K), dev)
         gn = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, case.N, case.K)
         gws = F.new_workspace(gn, dev) if gn else None
-        k = [0]
 
-        def with_epi():
+        def with_epi(i):
             F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
-            F.nvfp4_gemv_smallm(aq, copies[k[0] % 2], y=y, epi=epi, ws=ews, stream=stream)
-            k[0] += 1
+            F.nvfp4_gemv_smallm(aq, copies[i % 2], y=y, epi=epi, ws=ews, stream=stream)
 
-        def epi_only():
-            F.nvfp4_gemv_smallm(aq, copies[k[0] % 2], y=y, epi=epi, ws=ews, stream=stream)
-            k[0] += 1
+        def epi_only(i):
+            F.nvfp4_gemv_smallm(aq, copies[i % 2], y=y, epi=epi, ws=ews, stream=stream)
 
-        def plain():
-            F.nvfp4_gemv_smallm(aq, copies[k[0] % 2], y=y, ws=gws, stream=stream)
-            k[0] += 1
+        def plain(i):
+            F.nvfp4_gemv_smallm(aq, copies[i % 2], y=y, ws=gws, stream=stream)
 
-        t_all = _b2b_us(with_epi, args.reps, stream)
-        t_epi = _b2b_us(epi_only, args.reps, stream)
-        t_plain = _b2b_us(plain, args.reps, stream)
+        t_all = _graph_us(with_epi, args.reps, stream)
+        t_epi = _graph_us(epi_only, args.reps, stream)
+        t_plain = _graph_us(plain, args.reps, stream)
         out.append({"M": M, "N": case.N, "K": case.K, "weight_bytes": wb,
                     "variant": F.nvfp4_gemv_variant(M, case.N, case.K, True),
                     "quant_gemv_epilogue_us": round(t_all, 2), "gemv_epilogue_us": round(t_epi, 2),
@@ -393,37 +437,17 @@ def bench_chain(args, stream):
                               F.new_workspace(gn, dev) if gn else None, torch.empty((M, c.N), device=dev))
         res = {"M": M, "weight_bytes": total}
         for quantize in (True, False):
-            def step():
+            def step(_i):
                 for l in range(W.CHAIN_LAYERS):
                     for p in range(4):
                         x, aq, qws, gws, y = io[(l, p)]
                         if quantize:
-                            F.nvfp4_quantize_act(x, ws=qws, out=aq)
-                        F.nvfp4_gemv_smallm(aq, ws[(l, p)], y=y, ws=gws)
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                step()
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step()
-            torch.cuda.synchronize()
-            reps = 10
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+                            F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
+                        F.nvfp4_gemv_smallm(aq, ws[(l, p)], y=y, ws=gws, stream=stream)
+            us = _graph_us(step, 1, stream)
             key = "quant_gemv" if quantize else "gemv_only"
             res[key + "_us_per_step"] = round(us, 1)
             res[key + "_gbs"] = round(total / us / 1e3, 1)
-            del g
         out.append(res)
         log(args, f"[chain] M={M} {res['quant_gemv_us_per_step']:.1f} us/step with quantization "
                   f"({res['quant_gemv_gbs']:.0f} GB/s), {res['gemv_only_us_per_step']:.1f} us GEMV only "

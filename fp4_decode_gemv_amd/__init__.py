@@ -162,8 +162,16 @@ class NvFp4Tensor:
         return int(self.codes.shape[1]) * 2
 
 
+_WS_SIZES: dict = {}
+
+
 def nvfp4_workspace_size(op: int, M: int, N: int, K: int) -> int:
-    return int(lib().nvfp4_workspace_size(op, M, N, K))
+    # remembered per shape (and per forced kernel variant, which can change it)
+    key = (op, M, N, K, os.environ.get("NVFP4_GEMV_VARIANT"))
+    n = _WS_SIZES.get(key)
+    if n is None:
+        n = _WS_SIZES[key] = int(lib().nvfp4_workspace_size(op, M, N, K))
+    return n
 
 
 def nvfp4_workspace_init(ws, stream=None) -> None:
@@ -238,6 +246,12 @@ def nvfp4_gemv_variant_names() -> list[str]:
 def variant_tokens(name: str) -> int:
     """Compiled token count of a variant name (``..._m<MT>_...``)."""
     return int(name.split("_m")[1].split("_")[0])
+
+
+def variant_k_multiple(name: str) -> int:
+    """K granularity a variant needs: the direct-to-LDS kernels (``dma_*``)
+    load whole 256-element steps, every other kernel 32-element chunks."""
+    return 256 if name.startswith("dma_") else 32
 
 
 def nvfp4_reset_state_size(window: int) -> int:

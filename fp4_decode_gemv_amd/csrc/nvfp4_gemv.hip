@@ -476,7 +476,22 @@ __global__ __launch_bounds__(NW * 64) void gemv_valu_kernel(GemvParams p) {
 // Direct VALU kernel (M <= 2): no LDS, activation decoded in registers
 // ----------------------------------------------------------------------------
 
-template <int MT, int G, int R, int NW, int P, bool EPI>
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+// Word 3 of a gfx9-family buffer resource for raw byte-addressed loads.
+constexpr int kBufferWord3 = 0x00020000;
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld_w16(const uint8_t* ptr) {
+  if constexpr (NT) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ptr));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(ptr);
+  }
+}
+
+template <int MT, int G, int R, int NW, int P, bool NT, bool EPI>
 __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
   constexpr int RG = 64 / G;
   constexpr int ROWS = R * NW * RG;
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
       const int c = g + j * G;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        wb[j][r] = *reinterpret_cast<const uint4*>(wc[r] + c * 16);
+        wb[j][r] = ld_w16<NT>(wc[r] + c * 16);
         sb[j][r] = *reinterpret_cast<const uint16_t*>(ws[r] + c * 2);
       }
 #pragma unroll
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
           const int cn = g + (i + P) * G;
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            wb[j][r] = *reinterpret_cast<const uint4*>(wc[r] + cn * 16);
+            wb[j][r] = ld_w16<NT>(wc[r] + cn * 16);
             sb[j][r] = *reinterpret_cast<const uint16_t*>(ws[r] + cn * 2);
           }
 #pragma unroll
@@ -839,12 +854,6 @@ struct LmfmaStep {
   uint32_t as, ash; // activation scales: row lane/4, the same bytes
 };
 
-// Word 3 of a gfx9-family buffer resource for raw byte-addressed loads.
-constexpr int kBufferWord3 = 0x00020000;
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
-
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -991,6 +1000,156 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
   mfma_finish<MT, R, NW, EPI>(p, acc, reinterpret_cast<float*>(lds4), tile0);
 }
 
+// ----------------------------------------------------------------------------
+// Direct-to-LDS MFMA kernel (K % 256 == 0)
+// ----------------------------------------------------------------------------
+// The same operand layout and arithmetic as the LDS-staged kernel, but the
+// weight, activation and scale bytes of a step travel from memory straight
+// into LDS (gfx950 buffer_load ... lds: lane i of a 16-byte load lands at
+// byte 16*i of the destination, 4-byte loads at 4*i), so no VGPRs hold
+// loads in flight.  Each wave keeps a ring of D step slots and D - 1 steps
+// in flight while it computes one.  The compiler does not see these loads
+// (inline asm), so its own waits never drain the ring; the kernel waits
+// with explicit vmcnt counts instead.  Its only other memory instructions
+// come after the loop.
+//
+// Slot layout (bytes), for a 16R-row tile:
+//   [0, 2048 R)          weight codes: block 2r + h holds rows 16r + 8h + q
+//                        (q = 0..7) of tile r, 128 bytes each
+//   [2048 R, +1024)      activation codes: rows q = 0..7, 128 bytes each
+//   [+0, +256 R)         weight scales: tile r rows 0..15, 16 bytes each
+//   [+256 R, +256)       activation scales: rows 0..15 (rows >= M unused)
+// A 128-byte code row holds 16-byte chunk c at position c ^ q ^ h, so the
+// operand reads (16 rows, one chunk each, per 16 lanes) spread over every
+// bank.  Loads of rows past N or M fall outside their buffer resource and
+// are never used: their outputs are not stored and tokens >= M read row
+// M - 1.
+template <int R>
+constexpr int dma_slot_bytes() {
+  return (2 * R + 1) * 1024 + (R + 1) * 256;
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t raw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int n = bytes < 0x7FFFFFFF ? (int)bytes : 0x7FFFFFFF;
+  return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), n, kBufferWord3};
+}
+
+// lane i: 16 bytes from rsrc at voff + soff to LDS byte lds + 16 i
+__device__ __forceinline__ void dma_b128(const i32x4_t& rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
+}
+// lane i: 4 bytes to LDS byte lds + 4 i
+__device__ __forceinline__ void dma_b32(const i32x4_t& rsrc, uint32_t lds, int voff, int soff) {
+  asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int MT, int R, int NW, int D, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  constexpr int SLOT = dma_slot_bytes<R>();
+  constexpr int L = 3 * R + 2;  // loads per step
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: step offsets go to SGPRs
+  const int li = lane & 15, kg = lane >> 4;  // operand layout
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int nsteps = (int)(K / 256);
+  const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
+  (void)MT;
+
+  const int64_t rows = N - tile0 < 16 * R ? N - tile0 : 16 * R;
+  const i32x4_t wcr = raw_rsrc(p.w_codes + tile0 * (K / 2), rows * (K / 2));
+  const i32x4_t wsr = raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16));
+  const i32x4_t acr = raw_rsrc(p.a_codes, (int64_t)M * (K / 2));
+  const i32x4_t asr = raw_rsrc(p.a_scales, (int64_t)M * (K / 16));
+  // per-lane source offsets (every row-dependent term here, so a row past
+  // the buffer is out of range whatever the step offset)
+  const int q = lane >> 3, c = lane & 7;
+  int vcode[2 * R], vscale[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vcode[2 * r + h] = (16 * r + 8 * h + q) * (int)(K / 2) + 16 * (c ^ q ^ h);
+    vscale[r] = (16 * r + (lane >> 2)) * (int)(K / 16) + 4 * (lane & 3);
+  }
+
+  const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4)) +
+                        (uint32_t)(wave * D * SLOT);
+  auto issue = [&](int i) {  // the wave's i-th step into slot i % D
+    const int step = wave + i * NW;
+    const uint32_t s = ring + (uint32_t)((i % D) * SLOT);
+    const int co = step * 128, so = step * 16;
+#pragma unroll
+    for (int b = 0; b < 2 * R; ++b) dma_b128(wcr, s + 1024 * b, vcode[b], co);
+    dma_b128(acr, s + 2048 * R, vcode[0], co);
+#pragma unroll
+    for (int r = 0; r < R; ++r) dma_b32(wsr, s + 2048 * R + 1024 + 256 * r, vscale[r], so);
+    dma_b32(asr, s + 2048 * R + 1024 + 256 * R, vscale[0], so);
+  };
+
+  const int btok = li < M ? li : M - 1;
+  const char* lbase = reinterpret_cast<const char*>(lds4) + wave * D * SLOT;
+  // operand read offsets within a slot
+  int wro[R][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int h = li >> 3, qq = li & 7;
+      wro[r][u] = (2 * r + h) * 1024 + qq * 128 + 16 * ((2 * kg + u) ^ qq ^ h);
+    }
+  const int aro0 = 2048 * R + btok * 128 + 16 * ((2 * kg) ^ btok);
+  const int aro1 = 2048 * R + btok * 128 + 16 * ((2 * kg + 1) ^ btok);
+  const int sro = 2048 * R + 1024 + li * 16 + 4 * kg;
+  const int asro = 2048 * R + 1024 + 256 * R + btok * 16 + 4 * kg;
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (j < n) issue(j);
+  for (int i = 0; i < n; ++i) {
+    if (i + D - 1 < n) {
+      // into the slot of step i - 1: its operand reads must have returned
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(i + D - 1);
+    }
+    // steps issued after step i: min(D - 1, n - 1 - i)
+    const int later = n - 1 - i;
+    if (later >= D - 1) wait_vmcnt<(D - 1) * L>();
+    else if (D > 3 && later == 2) wait_vmcnt<(D > 3 ? 2 * L : 0)>();
+    else if (D > 2 && later == 1) wait_vmcnt<(D > 2 ? L : 0)>();
+    else wait_vmcnt<0>();
+    const char* sl = lbase + (i % D) * SLOT;
+    uint4 w[R][2];
+    uint32_t sw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      w[r][0] = *reinterpret_cast<const uint4*>(sl + wro[r][0]);
+      w[r][1] = *reinterpret_cast<const uint4*>(sl + wro[r][1]);
+      sw[r] = *reinterpret_cast<const uint32_t*>(sl + sro + 256 * r);
+    }
+    const uint4 a0 = *reinterpret_cast<const uint4*>(sl + aro0);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(sl + aro1);
+    const uint32_t sa = *reinterpret_cast<const uint32_t*>(sl + asro);
+    mfma_step<R>(w, sw, a0, a1, sa, acc);
+  }
+  __syncthreads();  // every wave is done with its ring before the reduction reuses the LDS
+  mfma_finish<MT, R, NW, EPI>(p, acc, reinterpret_cast<float*>(lds4), tile0);
+}
+
 __global__ void reset_state_init_kernel(char* state, int M, int window, size_t sbytes) {
   const int m = blockIdx.x;
   if (m >= M) return;
@@ -1010,7 +1169,7 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3 };
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4 };
 
 struct Variant {
   const char* name;
@@ -1027,10 +1186,15 @@ struct Variant {
     "valu_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, VALU, MT, G, R, NW, P,                 \
         gemv_valu_kernel<MT, G, R, NW, P, false>, gemv_valu_kernel<MT, G, R, NW, P, true> \
   }
-#define DIRECT_V(MT, G, R, NW, P)                                                                \
-  Variant {                                                                                    \
-    "direct_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, DIRECT, MT, G, R, NW, P,                 \
-        gemv_direct_kernel<MT, G, R, NW, P, false>, gemv_direct_kernel<MT, G, R, NW, P, true> \
+#define DIRECT_V(MT, G, R, NW, P)                                                                              \
+  Variant {                                                                                                  \
+    "direct_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, DIRECT, MT, G, R, NW, P,                               \
+        gemv_direct_kernel<MT, G, R, NW, P, false, false>, gemv_direct_kernel<MT, G, R, NW, P, false, true> \
+  }
+#define DIRECT_NT_V(MT, G, R, NW, P)                                                                         \
+  Variant {                                                                                                \
+    "direct_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P "_nt", DIRECT, MT, G, R, NW, P,                       \
+        gemv_direct_kernel<MT, G, R, NW, P, true, false>, gemv_direct_kernel<MT, G, R, NW, P, true, true> \
   }
 #define MFMA_V(MT, R, NW, P)                                                            \
   Variant {                                                                           \
@@ -1044,26 +1208,28 @@ struct Variant {
         gemv_lmfma_kernel<MT, R, NW, P, false, false>, gemv_lmfma_kernel<MT, R, NW, P, false, true>, \
         gemv_lmfma_kernel<MT, R, NW, P, true, false>, gemv_lmfma_kernel<MT, R, NW, P, true, true>    \
   }
+#define DMA_V(MT, R, NW, D)                                                          \
+  Variant {                                                                        \
+    "dma_m" #MT "_r" #R "_w" #NW "_d" #D, DMA, MT, 16, R, NW, D,                   \
+        gemv_dma_kernel<MT, R, NW, D, false>, gemv_dma_kernel<MT, R, NW, D, true> \
+  }
 
 const Variant kVariants[] = {
-    // direct VALU (no LDS), one and two tokens
-    DIRECT_V(1, 16, 1, 4, 1), DIRECT_V(1, 16, 2, 4, 1), DIRECT_V(1, 32, 1, 4, 1), DIRECT_V(1, 32, 2, 4, 1),
-    DIRECT_V(1, 64, 1, 4, 1), DIRECT_V(1, 16, 1, 4, 2), DIRECT_V(1, 8, 2, 4, 1), DIRECT_V(1, 16, 4, 4, 1),
-    DIRECT_V(2, 16, 1, 4, 1), DIRECT_V(2, 16, 2, 4, 1), DIRECT_V(2, 32, 1, 4, 1), DIRECT_V(2, 64, 1, 4, 1),
-    // LDS VALU, any M
-    VALU_V(1, 16, 2, 4, 1), VALU_V(2, 16, 2, 4, 1), VALU_V(4, 16, 2, 4, 1), VALU_V(8, 16, 1, 4, 1),
-    VALU_V(8, 16, 2, 4, 1),
-    // MFMA-assisted (the compiled token count only sizes the epilogue)
-    MFMA_V(2, 1, 4, 1), MFMA_V(2, 2, 8, 1), MFMA_V(2, 1, 8, 2), MFMA_V(4, 1, 4, 1), MFMA_V(4, 2, 8, 1),
-    MFMA_V(4, 1, 8, 2), MFMA_V(8, 1, 4, 1), MFMA_V(8, 1, 8, 1), MFMA_V(8, 2, 4, 1), MFMA_V(8, 2, 8, 1),
-    MFMA_V(8, 1, 4, 2), MFMA_V(8, 1, 8, 2), MFMA_V(8, 2, 8, 2), MFMA_V(8, 1, 16, 1),
+    // direct VALU (no LDS), one and two tokens; _nt: non-temporal weight loads
+    DIRECT_V(1, 16, 1, 4, 1), DIRECT_V(1, 32, 1, 4, 1), DIRECT_V(1, 32, 2, 4, 1), DIRECT_V(1, 64, 1, 4, 1),
+    DIRECT_V(2, 32, 1, 4, 1), DIRECT_V(2, 64, 1, 4, 1), DIRECT_V(1, 32, 1, 4, 2),
+    DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), DIRECT_NT_V(1, 64, 1, 4, 1),
+    DIRECT_NT_V(2, 32, 1, 4, 1), DIRECT_NT_V(2, 64, 1, 4, 1),
+    // LDS VALU, any M (the pages' CUDA-core design)
+    VALU_V(1, 16, 2, 4, 1), VALU_V(8, 16, 2, 4, 1),
+    // MFMA straight from registers (also the fallback past 32-bit buffer offsets)
+    MFMA_V(4, 2, 8, 1), MFMA_V(8, 1, 4, 1), MFMA_V(8, 2, 8, 1),
     // LDS-staged MFMA
-    LMFMA_V(2, 2, 4, 1), LMFMA_V(2, 2, 4, 2), LMFMA_V(4, 2, 4, 1), LMFMA_V(4, 2, 4, 2), LMFMA_V(4, 1, 8, 2),
-    LMFMA_V(4, 2, 8, 1), LMFMA_V(4, 2, 8, 2), LMFMA_V(8, 1, 4, 2), LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 4, 2),
-    LMFMA_V(8, 1, 8, 1), LMFMA_V(8, 1, 8, 2), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 2, 8, 2), LMFMA_V(8, 4, 4, 1),
-    LMFMA_V(8, 4, 4, 2), LMFMA_V(8, 1, 4, 1), LMFMA_V(8, 1, 2, 1), LMFMA_V(8, 2, 2, 1), LMFMA_V(8, 2, 2, 2),
-    LMFMA_V(8, 1, 8, 3), LMFMA_V(8, 1, 16, 1), LMFMA_V(4, 1, 8, 1), LMFMA_V(4, 2, 2, 1), LMFMA_V(4, 1, 4, 1),
-    LMFMA_V(2, 1, 4, 1), LMFMA_V(2, 1, 8, 1),
+    LMFMA_V(2, 2, 4, 1), LMFMA_V(4, 2, 4, 1), LMFMA_V(4, 2, 8, 1), LMFMA_V(8, 1, 4, 1), LMFMA_V(8, 1, 8, 1),
+    LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 2),
+    // direct-to-LDS MFMA (K % 256 == 0)
+    DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
+    DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1075,23 +1241,39 @@ int find_variant(const char* name) {
   return -1;
 }
 
-// Default variant per (M, N, K): the fastest variant of an MI355X sweep over
-// the Qwen3-8B/32B projection and LM-head shapes (back-to-back launches,
-// weights rotated past the Infinity Cache), generalised by N and K.
+// Index of a variant named by a string literal, looked up once per call site.
+#define VARIANT(name) ([] {                   \
+  static const int index_ = find_variant(name); \
+  return index_;                                \
+}())
+
+// Default variant per (M, N, K): the fastest variant of MI355X sweeps over
+// the Qwen3-32B projection shapes (graph-replayed back-to-back launches,
+// weights rotated past the Infinity Cache), generalised by N and K.  The
+// direct-to-LDS kernels need K % 256 == 0; other K fall back to the
+// register-staged MFMA kernel.
 int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
-  const char* name;
-  switch (mt_of(M)) {
-    case 1:
-      name = N >= 16384 ? "direct_m1_g32_r2_w4_p1" : K >= 12288 ? "direct_m1_g64_r1_w4_p1" : "direct_m1_g32_r1_w4_p1";
-      break;
-    case 2:
-      name = N >= 16384 ? "lmfma_m2_r2_w4_p1" : K >= 12288 ? "direct_m2_g64_r1_w4_p1" : "direct_m2_g32_r1_w4_p1";
-      break;
-    case 4: name = K >= 8192 || N >= 65536 ? "lmfma_m4_r2_w8_p1" : "lmfma_m4_r2_w4_p1"; break;
-    default: name = K >= 12288 || N >= 65536 ? "lmfma_m8_r2_w8_p1" : "lmfma_m8_r1_w4_p1"; break;
-  }
-  return find_variant(name);
+  const bool k256 = K % 256 == 0;
+  if (M <= 1)
+    return K >= 8192 ? VARIANT("direct_m1_g64_r1_w4_p1_nt")
+                     : N >= 16384 ? VARIANT("direct_m1_g32_r2_w4_p1_nt") : VARIANT("direct_m1_g32_r1_w4_p1_nt");
+  if (k256 && K >= 12288) return VARIANT("dma_m8_r2_w8_d2");
+  if (k256 && N >= 16384)
+    return M <= 2 ? VARIANT("dma_m2_r2_w4_d3") : M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
+  if (K >= 8192)
+    return M <= 4 ? VARIANT("lmfma_m4_r2_w8_p1") : k256 ? VARIANT("dma_m8_r2_w8_d2") : VARIANT("lmfma_m8_r2_w8_p1");
+  return VARIANT("lmfma_m8_r1_w4_p1");
+}
+
+// NVFP4_GEMV_VARIANT lookup, remembering the last string seen by this thread
+int env_variant(const char* env) {
+  thread_local char last[64] = {0};
+  thread_local int last_index = -1;
+  if (strncmp(env, last, sizeof(last)) == 0) return last_index;
+  last_index = find_variant(env);
+  strncpy(last, env, sizeof(last) - 1);
+  return last_index;
 }
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
@@ -1107,16 +1289,20 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   int vi = -1;
   // the LDS-staged kernel addresses a row tile and the activation with
   // 32-bit buffer offsets
-  auto fits = [&](int i) { return kVariants[i].kind != LMFMA || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31); };
+  auto fits = [&](int i) {
+    if (kVariants[i].kind == DMA && K % 256 != 0) return false;
+    return (kVariants[i].kind != LMFMA && kVariants[i].kind != DMA) || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
+  };
   // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
   // compiled token count covers M
   if (const char* env = getenv("NVFP4_GEMV_VARIANT")) {
-    const int i = find_variant(env);
+    const int i = env_variant(env);
     if (i >= 0 && kVariants[i].mt >= M && fits(i)) vi = i;
   }
   if (vi < 0) vi = default_variant(M, N, K, epi);
-  if (!fits(vi)) vi = find_variant(mt_of(M) <= 2 ? "direct_m2_g64_r1_w4_p1" : mt_of(M) <= 4 ? "mfma_m4_r2_w8_p1"
-                                                                                       : "mfma_m8_r2_w8_p1");
+  if (!fits(vi))
+    vi = mt_of(M) <= 2 ? VARIANT("direct_m2_g64_r1_w4_p1") : mt_of(M) <= 4 ? VARIANT("mfma_m4_r2_w8_p1")
+                                                                           : VARIANT("mfma_m8_r2_w8_p1");
   const Variant& v = kVariants[vi];
   GemvConfig c{};
   c.variant = vi;
@@ -1127,7 +1313,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
-  if (v.kind == MFMA || v.kind == LMFMA) {
+  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA) {
     c.kp = (int)K;
     c.rows_per_wg = (int64_t)16 * v.r;
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
@@ -1135,6 +1321,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     if (v.kind == LMFMA) {
       const int64_t slots = (int64_t)v.nw * (16 * v.r + 8) * (144 + 20);
       if (slots > c.lds_bytes) c.lds_bytes = slots;
+    }
+    if (v.kind == DMA) {
+      const int64_t ring = (int64_t)v.nw * v.p * ((2 * v.r + 1) * 1024 + (v.r + 1) * 256);
+      if (ring > c.lds_bytes) c.lds_bytes = ring;
     }
   } else if (v.kind == VALU) {
     int64_t kp = budget / v.mt / 512 * 512;

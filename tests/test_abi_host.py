@@ -136,3 +136,31 @@ def test_reset_state_and_workspace_helpers(L):
     a = L.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, 8, 151936, 5120)
     b = L.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, 8, 4096, 5120)
     assert a > b > 0
+
+
+def test_launch_table_names_real_variants(L, monkeypatch):
+    """Every shape of the workloads resolves to a compiled variant whose
+    token count covers M and whose K granularity K satisfies (host logic
+    only: no kernel runs)."""
+    import workloads as W
+
+    monkeypatch.delenv("NVFP4_GEMV_VARIANT", raising=False)
+    names = set(F.nvfp4_gemv_variant_names())
+    shapes = [(c.N, c.K) for c in W.qwen3_8b_cases() + W.qwen3_32b_cases()]
+    shapes += [(W.lm_head_case().N, W.lm_head_case().K), (4096, 4096), (4097, 4128), (300, 96), (1, 32)]
+    for (N, K) in shapes:
+        for M in range(1, 9):
+            for lm in (False, True):
+                v = F.nvfp4_gemv_variant(M, N, K, lm)
+                assert v in names, (M, N, K, v)
+                assert F.variant_tokens(v) >= M, (M, N, K, v)
+                assert K % F.variant_k_multiple(v) == 0, (M, N, K, v)
+
+
+def test_forced_variant_falls_back_when_k_does_not_fit(L, monkeypatch):
+    """A direct-to-LDS variant forced on a K that is not a multiple of 256
+    is not launched; the default for that shape is used instead."""
+    monkeypatch.setenv("NVFP4_GEMV_VARIANT", "dma_m8_r2_w4_d3")
+    assert F.nvfp4_gemv_variant(8, 1024, 4096) == "dma_m8_r2_w4_d3"
+    v = F.nvfp4_gemv_variant(8, 1024, 4128)
+    assert v != "dma_m8_r2_w4_d3" and 4128 % F.variant_k_multiple(v) == 0
