@@ -51,8 +51,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "de81e091a9d0ebc5669c0302995e407e1e6db00fa32b3a10b5e3437e7a3a388c",
-    "bytes_per_step": 1117117492,
+    "sha256": "e3e17322910e7b72347542032849994f2ed13f6ebe4e7879094538f64becc259",
+    "bytes_per_step": 1109925348,
 }
 
 
@@ -302,7 +302,8 @@ def main():
                             "FETCH_SIZE / WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes": gemv_bytes,
             "kernel": "gemv kernels, all 16 (projection, M) cases of a step: summed algorithmic bytes / summed "
-                      "average launch durations (back-to-back launches between HIP events)",
+                      "average launch durations (per case: `reps` back-to-back launches captured in a HIP graph, "
+                      "HIP events around its replays on the launch stream)",
         },
         "cpu_baseline": cpu,
         "detail": detail,

@@ -1150,6 +1150,184 @@ __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
   mfma_finish<MT, R, NW, EPI>(p, acc, reinterpret_cast<float*>(lds4), tile0);
 }
 
+// ----------------------------------------------------------------------------
+// LDS-staged VALU kernel (M <= 2, K % 256 == 0)
+// ----------------------------------------------------------------------------
+// The direct kernel's lane mapping and arithmetic (G lanes per weight row,
+// 16 bytes per lane per step, R rows per lane, f16 dot2 block sums), but the
+// activation codes and scales and the block scales of the workgroup's rows
+// are copied into LDS once, with direct-to-LDS loads, before the main loop.
+// The loop then issues one memory instruction per row and step, the
+// non-temporal 16-byte weight load; everything else comes from LDS.
+// Weight loads go through a buffer resource: chunks past K and rows past N
+// read as zero without touching memory, so every lane runs the same steps
+// and no load sits behind a branch (the compiler's wait before step i then
+// counts exactly the loads of steps i+1 .. i+P-1).  Each LDS region is
+// padded to a whole number of 1 KB copies.
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // beyond any buffer resource's num_records
+
+__host__ __device__ constexpr int64_t pad1k(int64_t b) { return (b + 1023) / 1024 * 1024; }
+
+// Copy `bytes` (a multiple of 16) from rsrc into LDS at `lds`: 1 KB per wave
+// instruction, chunks spread over the NW waves.  The whole source offset is
+// in the per-lane operand, so lanes past `bytes` are out of range.
+template <int NW>
+__device__ __forceinline__ void stage_to_lds(const i32x4_t& rsrc, uint32_t lds, int64_t bytes, int wave, int lane) {
+  const int chunks = (int)((bytes + 1023) / 1024);
+  for (int ch = wave; ch < chunks; ch += NW) dma_b128(rsrc, lds + 1024 * ch, 1024 * ch + 16 * lane, 0);
+}
+
+template <int MT, int G, int R, int NW, int P, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_staged_kernel(GemvParams p) {
+  constexpr int RG = 64 / G;
+  constexpr int ROWS = R * NW * RG;
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane % G;
+  const int rg = lane / G;
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * ROWS;
+  const int64_t rows = N - tile0 < ROWS ? N - tile0 : ROWS;
+  const int C = (int)(K / 32);       // 32-element chunks per row
+  const int nmax = (C + G - 1) / G;  // steps of every lane (chunks g, g + G, ...)
+  // LDS regions: activation codes [MT][K/2], activation scales [MT][K/16],
+  // weight scales of this tile [ROWS][K/16]
+  const int64_t acb = pad1k(MT * (K / 2)), asb = pad1k(MT * (K / 16));
+  const uint32_t lbase = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+  stage_to_lds<NW>(raw_rsrc(p.a_codes, (int64_t)M * (K / 2)), lbase, (int64_t)M * (K / 2), wave, lane);
+  stage_to_lds<NW>(raw_rsrc(p.a_scales, (int64_t)M * (K / 16)), lbase + (uint32_t)acb, (int64_t)M * (K / 16), wave,
+                   lane);
+  stage_to_lds<NW>(raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16)), lbase + (uint32_t)(acb + asb),
+                   rows * (K / 16), wave, lane);
+
+  const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  int rloc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rloc[r] = (r * NW + wave) * RG + rg;
+  // a ring of P + 1 register slots, the loop unrolled over the ring: step i
+  // lives in slot i % (P + 1) and the load of step i + P goes to the slot
+  // step i - 1 used, so no slot is reloaded while its contents are live and
+  // the compiler needs no copies (which would wait for the new loads)
+  constexpr int S = P + 1;
+  uint4 wb[S][R];
+  auto load = [&](int slot, int i) {
+    const int c = g + i * G;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t o = c < C ? (uint32_t)(rloc[r] * (int)(K / 2) + 16 * c) : kOutOfRange;
+      wb[slot][r] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(wcr, (int)o, 0, 2 /* non-temporal */));
+    }
+  };
+  // slots filled one after the other (scheduling barriers), so the wait
+  // before a slot counts exactly the later slots' loads
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    load(j, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmcnt<P * R>();  // this wave's staging copies (issued first) have landed
+  asm volatile("s_barrier" ::: "memory");  // ... and every other wave's
+
+  const char* lds = reinterpret_cast<const char*>(lds4);
+  const char* act_s = lds + acb;
+  const char* w_s = lds + acb + asb;
+  float acc[R][MT][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m][0] = acc[r][m][1] = 0.0f;
+
+  for (int i0 = 0; i0 < nmax; i0 += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      const int i = i0 + j;
+      load((j + P) % S, i + P);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < nmax) {
+        // a lane past the row's end has zero weight codes; it reads the last
+        // chunk's activation and scales so that every factor stays finite
+        int c = g + i * G;
+        c = c < C ? c : C - 1;
+        half2_t ah[MT][16];
+        float2_t saf[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int mm = m < M ? m : M - 1;  // tokens >= M reuse a valid row; never stored
+          const uint4 a = *reinterpret_cast<const uint4*>(lds + mm * (K / 2) + 16 * c);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = word_of(a, q);
+            ah[m][4 * q + 0] = fp4x2<0>(word);
+            ah[m][4 * q + 1] = fp4x2<1>(word);
+            ah[m][4 * q + 2] = fp4x2<2>(word);
+            ah[m][4 * q + 3] = fp4x2<3>(word);
+          }
+          saf[m] = __builtin_amdgcn_cvt_pk_f32_fp8(*reinterpret_cast<const uint16_t*>(act_s + mm * (K / 16) + 2 * c),
+                                                   false);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float2_t sw =
+              __builtin_amdgcn_cvt_pk_f32_fp8(*reinterpret_cast<const uint16_t*>(w_s + rloc[r] * (K / 16) + 2 * c), false);
+          half2_t wh[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = word_of(wb[j][r], q);
+            wh[4 * q + 0] = fp4x2<0>(word);
+            wh[4 * q + 1] = fp4x2<1>(word);
+            wh[4 * q + 2] = fp4x2<2>(word);
+            wh[4 * q + 3] = fp4x2<3>(word);
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              t0 = __builtin_amdgcn_fdot2(wh[k], ah[m][k], t0, false);
+              t1 = __builtin_amdgcn_fdot2(wh[8 + k], ah[m][8 + k], t1, false);
+            }
+            acc[r][m][0] = __builtin_fmaf(t0, saf[m][0] * sw[0], acc[r][m][0]);
+            acc[r][m][1] = __builtin_fmaf(t1, saf[m][1] * sw[1], acc[r][m][1]);
+          }
+        }
+      }
+    }
+  }
+
+  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  float out[R * MT];
+  int tok[R * MT];
+  bool ok[R * MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float v = acc[r][m][0] + acc[r][m][1];
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+      const int64_t row = tile0 + rloc[r];
+      out[r * MT + m] = v * scale;
+      tok[r * MT + m] = m;
+      ok[r * MT + m] = g == 0 && row < N && m < M;
+      if (ok[r * MT + m]) p.y[(int64_t)m * N + row] = out[r * MT + m];
+    }
+  if constexpr (EPI) {
+    int rowt[R * MT];
+    bool own[R * MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        rowt[r * MT + m] = rloc[r];
+        own[r * MT + m] = g == 0 && m < M;
+      }
+    lmhead_partials<MT, ROWS, R * MT>(p, out, tok, rowt, own, ok, blockIdx.x);
+  }
+}
+
 __global__ void reset_state_init_kernel(char* state, int M, int window, size_t sbytes) {
   const int m = blockIdx.x;
   if (m >= M) return;
@@ -1169,7 +1347,7 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4 };
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5 };
 
 struct Variant {
   const char* name;
@@ -1208,6 +1386,11 @@ struct Variant {
         gemv_lmfma_kernel<MT, R, NW, P, false, false>, gemv_lmfma_kernel<MT, R, NW, P, false, true>, \
         gemv_lmfma_kernel<MT, R, NW, P, true, false>, gemv_lmfma_kernel<MT, R, NW, P, true, true>    \
   }
+#define STAGED_V(MT, G, R, NW, P)                                                                  \
+  Variant {                                                                                      \
+    "staged_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, STAGED, MT, G, R, NW, P,                   \
+        gemv_staged_kernel<MT, G, R, NW, P, false>, gemv_staged_kernel<MT, G, R, NW, P, true> \
+  }
 #define DMA_V(MT, R, NW, D)                                                          \
   Variant {                                                                        \
     "dma_m" #MT "_r" #R "_w" #NW "_d" #D, DMA, MT, 16, R, NW, D,                   \
@@ -1230,6 +1413,11 @@ const Variant kVariants[] = {
     // direct-to-LDS MFMA (K % 256 == 0)
     DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
     DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
+    // LDS-staged VALU (K % 256 == 0)
+    STAGED_V(1, 32, 1, 4, 1), STAGED_V(1, 32, 2, 4, 1), STAGED_V(1, 64, 1, 4, 1), STAGED_V(1, 32, 1, 4, 2),
+    STAGED_V(1, 32, 2, 4, 2), STAGED_V(1, 64, 1, 4, 2), STAGED_V(1, 64, 2, 4, 1), STAGED_V(1, 32, 4, 4, 1),
+    STAGED_V(1, 32, 2, 8, 1), STAGED_V(1, 64, 1, 8, 2), STAGED_V(2, 32, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
+    STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 64, 1, 4, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1255,12 +1443,19 @@ int find_variant(const char* name) {
 int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
   const bool k256 = K % 256 == 0;
-  if (M <= 1)
+  if (M <= 1) {
+    if (k256)
+      return K >= 12288 ? VARIANT("staged_m1_g64_r1_w4_p2")
+             : K >= 8192 ? VARIANT("staged_m1_g64_r2_w4_p1")
+             : N >= 16384 ? VARIANT("staged_m1_g32_r2_w4_p2")
+                          : VARIANT("staged_m1_g32_r1_w4_p2");
     return K >= 8192 ? VARIANT("direct_m1_g64_r1_w4_p1_nt")
                      : N >= 16384 ? VARIANT("direct_m1_g32_r2_w4_p1_nt") : VARIANT("direct_m1_g32_r1_w4_p1_nt");
+  }
   if (k256 && K >= 12288) return VARIANT("dma_m8_r2_w8_d2");
-  if (k256 && N >= 16384)
-    return M <= 2 ? VARIANT("dma_m2_r2_w4_d3") : M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
+  if (M <= 2 && k256) return N >= 16384 ? VARIANT("staged_m2_g32_r2_w4_p1")
+                             : K >= 8192 ? VARIANT("staged_m2_g64_r1_w4_p1") : VARIANT("lmfma_m8_r1_w4_p1");
+  if (k256 && N >= 16384) return M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
   if (K >= 8192)
     return M <= 4 ? VARIANT("lmfma_m4_r2_w8_p1") : k256 ? VARIANT("dma_m8_r2_w8_d2") : VARIANT("lmfma_m8_r2_w8_p1");
   return VARIANT("lmfma_m8_r1_w4_p1");
@@ -1278,6 +1473,13 @@ int env_variant(const char* env) {
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
+// LDS of the staged kernel: activation codes and scales for MT tokens and
+// the block scales of the workgroup's rows, each padded to whole KB
+int64_t staged_lds_bytes(const Variant& v, int64_t K) {
+  const int64_t rows = (int64_t)v.r * v.nw * (64 / v.g);
+  return pad1k(v.mt * (K / 2)) + pad1k(v.mt * (K / 16)) + pad1k(rows * (K / 16));
+}
+
 }  // namespace
 
 size_t reset_state_bytes(int window) {
@@ -1290,7 +1492,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // the LDS-staged kernel addresses a row tile and the activation with
   // 32-bit buffer offsets
   auto fits = [&](int i) {
-    if (kVariants[i].kind == DMA && K % 256 != 0) return false;
+    if ((kVariants[i].kind == DMA || kVariants[i].kind == STAGED) && K % 256 != 0) return false;
+    if (kVariants[i].kind == STAGED && staged_lds_bytes(kVariants[i], K) > 65536) return false;
     return (kVariants[i].kind != LMFMA && kVariants[i].kind != DMA) || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
   };
   // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
@@ -1338,7 +1541,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.kp = (int)K;
     c.rows_per_wg = (int64_t)v.r * v.nw * (64 / v.g);
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
-    c.lds_bytes = 0;
+    c.lds_bytes = v.kind == STAGED ? staged_lds_bytes(v, K) : 0;
   }
   // workspace (epilogue only): per-workgroup softmax partials
   c.ws_bytes = epi ? align256(c.grid * c.mt * 4 * 4) : 0;

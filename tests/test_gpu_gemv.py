@@ -128,15 +128,22 @@ VARIANT_SHAPES_K256 = [(1, 37, 256), (16, 515, 4352), (16, 300, 5120), (16, 129,
 def test_every_kernel_variant(variant, monkeypatch):
     """Each compiled variant (forced through NVFP4_GEMV_VARIANT) against the
     oracle: ragged row tails, K not a multiple of 128, several K phases, and
-    M below and at the variant's token count."""
+    M below and at the variant's token count.  A variant whose LDS would not
+    fit a shape is not launched there (the default runs instead); every
+    variant runs at least two of the shapes."""
     mt = F.variant_tokens(variant)
     monkeypatch.setenv("NVFP4_GEMV_VARIANT", variant)
     shapes = VARIANT_SHAPES if F.variant_k_multiple(variant) == 32 else VARIANT_SHAPES_K256
+    ran = 0
     for M in sorted({1, max(1, mt - 1), mt}):
         for (nmul, N, K) in shapes:
-            assert F.nvfp4_gemv_variant(M, N, K) == variant
+            if F.nvfp4_gemv_variant(M, N, K) != variant:
+                assert K >= 25600, (variant, M, N, K)  # only the largest K may exceed a variant's LDS
+                continue
+            ran += 1
             w = W.small_random_weights(N + K + M, N, K)
             xb = W.small_random_bf16(3 * N + M, M, K)
             wq, aq, y = _run(M, N, K, w, xb, variant)
             y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
             assert_gemv_close(y, y_ref, ref_abs, what=f"{variant} M={M} N={N} K={K}")
+    assert ran >= 2, variant
