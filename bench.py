@@ -6,13 +6,13 @@ M = 1, 2, 4 and 8 active tokens.  One step = for every M and every
 projection, quantize the bf16 activation on the GPU (the per-layer "Q" step)
 and run the GEMV against the packed NVFP4 weights: 16 quantize launches and
 16 GEMV launches.  Inputs are seeded synthetic tensors (workloads/), resident
-in HBM before timing starts.  Every projection has several packed copies
-that are rotated launch by launch, so no GEMV finds its weights in the
-256 MB Infinity Cache from an earlier launch.
+in HBM before timing starts.  Every projection has enough packed copies
+that its launches cycle through at least 576 MB of distinct weights
+(2 x (256 MB Infinity Cache + 32 MB L2)), so no GEMV finds its weights in a
+cache from an earlier launch.
 
 A step is captured once in a HIP graph (as a decode loop replays it; the
-dispatch choices are fixed at capture) and replayed; one graph per phase of
-the weight-copy rotation.
+dispatch choices are fixed at capture) and replayed.
 
 Prints one JSON line:
   value        effective GB/s over the step = weight+scale bytes streamed per
@@ -51,8 +51,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "e3e17322910e7b72347542032849994f2ed13f6ebe4e7879094538f64becc259",
-    "bytes_per_step": 1109925348,
+    "sha256": "77b261f96fcfd5b4edde803a80d8953fd8bb2336a4308812b159a9f48e92445b",
+    "bytes_per_step": 1108286761,
 }
 
 
@@ -68,6 +68,12 @@ def measured_traffic():
     return GEMV_TRAFFIC["bytes_per_step"]
 
 
+def n_copies(args, c) -> int:
+    """Packed copies of a projection: enough to cycle through args.rotate_mb
+    of distinct weights, and at least 2."""
+    return max(2, math.ceil(args.rotate_mb * 1e6 / weight_bytes(c.N, c.K)))
+
+
 def weight_bytes(N: int, K: int) -> int:
     """Algorithmic bytes of one GEMV: codes + E4M3 scales + global scale."""
     return N * K // 2 + N * K // 16 + 4
@@ -78,7 +84,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--copies", type=int, default=3, help="packed copies per projection (MALL rotation)")
+    ap.add_argument("--rotate-mb", type=float, default=576.0,
+                    help="distinct packed weight bytes (MB) each projection's launches cycle through: at least "
+                         "2 x (256 MB Infinity Cache + 32 MB L2), so no launch reads its weights from a cache")
     ap.add_argument("--reps", type=int, default=30, help="timed launches per (projection, M) for per-kernel times")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle baseline")
@@ -115,12 +123,12 @@ def setup(args):
         base = F.nvfp4_pack_weights(wt)
         del wt
         copies = [base]
-        for _ in range(args.copies - 1):
+        for _ in range(n_copies(args, c) - 1):
             copies.append(F.NvFp4Tensor(base.codes.clone(), base.scales.clone(), base.gscale.clone()))
         wq[c.name] = copies
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        log(args, f"[setup] packed {c.name} {c.N}x{c.K} x{args.copies} in {time.perf_counter() - t0:.1f}s")
+        log(args, f"[setup] packed {c.name} {c.N}x{c.K} x{len(copies)} in {time.perf_counter() - t0:.1f}s")
     acts = {}
     for c in cases:
         for M in M_LIST:
@@ -160,18 +168,21 @@ def main():
 
     def gemv(c, M, copy):
         x, aq, ws, gws, y = acts[(c.name, M)]
-        F.nvfp4_gemv_smallm(aq, wq[c.name][copy % args.copies], y=y, ws=gws, stream=stream)
+        copies = wq[c.name]
+        F.nvfp4_gemv_smallm(aq, copies[copy % len(copies)], y=y, ws=gws, stream=stream)
 
     def quant(c, M):
         x, aq, ws, gws, y = acts[(c.name, M)]
         F.nvfp4_quantize_act(x, ws=ws, out=aq, stream=stream)
 
-    def step(s):
-        # launch i of a projection in the run reads packed copy i % copies
+    def step():
+        # the four launches of a projection in a step read four different
+        # packed copies; between two reads of one copy a whole step (1.1 GB of
+        # other weights) goes by, so a replayed step finds nothing in a cache
         for mi, M in enumerate(M_LIST):
             for c in cases:
                 quant(c, M)
-                gemv(c, M, s * len(M_LIST) + mi)
+                gemv(c, M, mi)
 
     def capture(fn):
         with torch.cuda.stream(stream):
@@ -184,32 +195,31 @@ def main():
         return g
 
     # ---------------- whole-step throughput (graph replay) ----------------
-    period = args.copies // math.gcd(args.copies, len(M_LIST))
-    graphs = [capture(lambda s=s: step(s)) for s in range(period)]
+    g_step = capture(step)
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            graphs[i % period].replay()
+            g_step.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(args.steps):
-            graphs[i % period].replay()
+            g_step.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     bytes_per_step = sum(weight_bytes(c.N, c.K) for c in cases) * len(M_LIST)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log(args, f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s effective (quantization included)")
-    del graphs
+    del g_step
 
     # the same step launched eagerly from Python, for reference (host-bound)
     with torch.cuda.stream(stream):
-        step(0)
+        step()
     torch.cuda.synchronize()
     te = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(10):
-            step(i)
+            step()
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - te) * 1e3 / 10
     log(args, f"[bench] eager Python launches: {eager_ms * 1e3:.1f} us/step")
@@ -288,7 +298,7 @@ def main():
                         "quantization + GEMV for each (projection, M)",
             "global_batch": list(M_LIST),
             "weight_bytes_per_step": bytes_per_step,
-            "weight_copies_rotated": args.copies,
+            "weight_copies_rotated": {c.name: len(wq[c.name]) for c in cases},
             "parallelism": "single-gpu",
         },
         "roofline": {

@@ -1436,28 +1436,24 @@ int find_variant(const char* name) {
 }())
 
 // Default variant per (M, N, K): the fastest variant of MI355X sweeps over
-// the Qwen3-32B projection shapes (graph-replayed back-to-back launches,
-// weights rotated past the Infinity Cache), generalised by N and K.  The
-// direct-to-LDS kernels need K % 256 == 0; other K fall back to the
-// register-staged MFMA kernel.
+// the Qwen3-32B projection shapes (graph-replayed back-to-back launches, each
+// projection's weights rotated over >= 576 MB of copies so that every launch
+// reads HBM), generalised by N and K.  The LDS-copy kernels need
+// K % 256 == 0; other K fall back to the register-staged kernels.
 int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
   const bool k256 = K % 256 == 0;
   if (M <= 1) {
-    if (k256)
-      return K >= 12288 ? VARIANT("staged_m1_g64_r1_w4_p2")
-             : K >= 8192 ? VARIANT("staged_m1_g64_r2_w4_p1")
-             : N >= 16384 ? VARIANT("staged_m1_g32_r2_w4_p2")
-                          : VARIANT("staged_m1_g32_r1_w4_p2");
-    return K >= 8192 ? VARIANT("direct_m1_g64_r1_w4_p1_nt")
-                     : N >= 16384 ? VARIANT("direct_m1_g32_r2_w4_p1_nt") : VARIANT("direct_m1_g32_r1_w4_p1_nt");
+    if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
+    if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
+    return VARIANT("direct_m1_g32_r1_w4_p1_nt");
   }
-  if (k256 && K >= 12288) return VARIANT("dma_m8_r2_w8_d2");
-  if (M <= 2 && k256) return N >= 16384 ? VARIANT("staged_m2_g32_r2_w4_p1")
-                             : K >= 8192 ? VARIANT("staged_m2_g64_r1_w4_p1") : VARIANT("lmfma_m8_r1_w4_p1");
+  if (M <= 2 && k256)
+    return K >= 12288 ? VARIANT("staged_m2_g64_r1_w4_p2")
+           : K >= 8192 && N < 16384 ? VARIANT("staged_m2_g64_r1_w4_p1")
+                                    : VARIANT("staged_m2_g32_r2_w4_p1");
   if (k256 && N >= 16384) return M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
-  if (K >= 8192)
-    return M <= 4 ? VARIANT("lmfma_m4_r2_w8_p1") : k256 ? VARIANT("dma_m8_r2_w8_d2") : VARIANT("lmfma_m8_r2_w8_p1");
+  if (K >= 8192) return M <= 4 ? VARIANT("lmfma_m4_r2_w8_p1") : VARIANT("lmfma_m8_r2_w8_p1");
   return VARIANT("lmfma_m8_r1_w4_p1");
 }
 
