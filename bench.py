@@ -51,8 +51,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "77b261f96fcfd5b4edde803a80d8953fd8bb2336a4308812b159a9f48e92445b",
-    "bytes_per_step": 1108286761,
+    "sha256": "98a7b6ef95f95211de76d3ddda213c9bf67be0d8a3af4b10701c4b98d4589bb4",
+    "bytes_per_step": 1107228786,
 }
 
 

@@ -250,9 +250,9 @@ def variant_tokens(name: str) -> int:
 
 def variant_k_multiple(name: str) -> int:
     """K granularity a variant needs: the direct-to-LDS kernels (``dma_*``,
-    ``staged_*``) copy whole 256-element steps, every other kernel 32-element
-    chunks."""
-    return 256 if name.startswith(("dma_", "staged_")) else 32
+    ``staged_*``, ``fmma_*``) copy whole 256-element steps, every other kernel
+    32-element chunks."""
+    return 256 if name.startswith(("dma_", "staged_", "fmma_")) else 32
 
 
 def nvfp4_reset_state_size(window: int) -> int:

@@ -6,6 +6,8 @@ linked into one shared library.  Flags:
 * ``--offload-arch=gfx950`` only (no other targets, no CUDA);
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops`` keeps the compiler
   from emitting packed-FP32 VALU instructions;
+* ``-mllvm -amdgpu-mfma-vgpr-form``: MFMA results in ordinary VGPRs, so the
+  FP4-MFMA kernel scales them without copying each out of an AGPR first;
 * ``-ffp-contract=off`` so no a*b+c is fused behind the code's back (the
   quantization recipe is a sequence of separately rounded float32 steps;
   the GEMV spells out every FMA it wants);
@@ -35,6 +37,7 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-ffp-contract=off",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-function",

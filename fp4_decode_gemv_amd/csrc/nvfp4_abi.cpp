@@ -177,6 +177,9 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
       overlaps(y, yb, w_codes, wcb) || overlaps(y, yb, w_scales, wsb) || overlaps(y, yb, w_gscale, 4))
     return NVFP4_ERR_ARG;
   const GemvConfig cfg = choose_gemv_config(M, N, K, epi != nullptr);
+  // the epilogue's merge addresses its partials (grid x mt x 16 bytes) with
+  // 32-bit buffer offsets
+  if (epi && cfg.ws_bytes > (int64_t)0x7FFFFF00) return NVFP4_ERR_SHAPE;
   const size_t need = (size_t)cfg.ws_bytes;
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return NVFP4_ERR_ALIGN;

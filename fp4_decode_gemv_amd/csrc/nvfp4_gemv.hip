@@ -72,6 +72,9 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
+// Word 3 of a gfx9-family buffer resource for raw byte-addressed loads.
+constexpr int kBufferWord3 = 0x00020000;
+
 struct GemvParams {
   int M;
   int64_t N, K;
@@ -240,47 +243,84 @@ __device__ __forceinline__ void lmhead_partials(const GemvParams& p, const float
   }
 }
 
-// LM-head epilogue, part 2 (its own launch, one workgroup per token, after
-// the GEMV): merge the token's partials of all row tiles in a fixed order,
-// H = log S - T/S (natural log), then the ReSET update of the token's
-// sequence state and its temperature.
-constexpr int kMergeThreads = 1024;
+// LM-head epilogue, parts 2 and 3 (two launches after the GEMV; no atomics
+// or fences, which on gfx950 cost a write-back of the whole L2 per release):
+//   lmhead_slice_kernel: kMergeGroups workgroups per token each merge a
+//     contiguous slice of the token's row-tile partials in a fixed order and
+//     write one slice partial;
+//   lmhead_merge_kernel: one wave per token merges its kMergeGroups slice
+//     partials in a fixed order, computes H = log S - T/S (natural log) and
+//     runs the ReSET update of the token's sequence state.
+// Workspace: the row-tile partials [ntiles][MT], then [MT][kMergeGroups]
+// slice partials, all float4 {max, S, T, -}.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = 64;
+constexpr int kMergeLoads = 4;  // partials per thread and round, all loads in flight at once
 
-__global__ __launch_bounds__(kMergeThreads) void lmhead_merge_kernel(GemvParams p, int mt, int ntiles) {
-  __shared__ float mred[kMergeThreads], sred[kMergeThreads], tred[kMergeThreads];
+__host__ __device__ constexpr int64_t merge_slices_offset(int64_t ntiles, int mt) {
+  return (ntiles * mt * 16 + 255) / 256 * 256;
+}
+
+// merge the (m, S, T) of the lane `x` places above into this lane's
+__device__ __forceinline__ void merge_from_lane(float& m, float& S, float& T, int x) {
+  const float mb = __shfl_xor(m, x, 64), Sb = __shfl_xor(S, x, 64), Tb = __shfl_xor(T, x, 64);
+  merge_partial(m, S, T, mb, Sb, Tb);
+}
+
+__global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams p, int mt, int ntiles) {
+  __shared__ float wm[kMergeThreads / 64], wS[kMergeThreads / 64], wt[kMergeThreads / 64];
+  const int m = blockIdx.x / kMergeGroups, grp = blockIdx.x % kMergeGroups;
+  if (m >= p.M) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float4_t* slices = reinterpret_cast<float4_t*>(reinterpret_cast<char*>(p.partials) + merge_slices_offset(ntiles, mt));
+  // this workgroup's slice of tiles; thread t takes lo + t, lo + t + NT, ...
+  const int per = (ntiles + kMergeGroups - 1) / kMergeGroups;
+  const int lo = grp * per, hi = lo + per < ntiles ? lo + per : ntiles;
+  // row-tile partials [ntiles][mt] through a buffer resource; tiles outside
+  // the slice take the empty partial (-inf, 0, 0) and no load
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+      p.partials, (short)0, (int)((int64_t)ntiles * mt * 16), kBufferWord3);
+  float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
+  for (int base = lo; base < hi; base += kMergeThreads * kMergeLoads) {  // same trip count for every thread
+    float4_t q[kMergeLoads];
+#pragma unroll
+    for (int j = 0; j < kMergeLoads; ++j) {
+      const int idx = base + j * kMergeThreads + (int)threadIdx.x;
+      const int off = idx < hi ? (int)(((int64_t)idx * mt + m) * 16) : (int)0x7FFFFFF0;
+      q[j] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeLoads; ++j) {
+      const bool in = base + j * kMergeThreads + (int)threadIdx.x < hi;
+      merge_partial(gm, Sm, Tm, in ? q[j][0] : -INFINITY, q[j][1], q[j][2]);
+    }
+  }
+  // across the wave (xor butterfly), then across the waves through LDS
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) merge_from_lane(gm, Sm, Tm, x);
+  if (lane == 0) {
+    wm[wave] = gm;
+    wS[wave] = Sm;
+    wt[wave] = Tm;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  for (int w = 1; w < kMergeThreads / 64; ++w) merge_partial(gm, Sm, Tm, wm[w], wS[w], wt[w]);
+  slices[(int64_t)m * kMergeGroups + grp] = float4_t{gm, Sm, Tm, 0.0f};
+}
+
+__global__ __launch_bounds__(64) void lmhead_merge_kernel(GemvParams p, int mt, int ntiles) {
+  static_assert(kMergeGroups == 64, "one slice partial per lane of a wave");
   const int m = blockIdx.x;
   if (m >= p.M) return;
-  const float4* part = reinterpret_cast<const float4*>(p.partials);
-  // thread t merges tiles t, t + NT, ... in order; then a fixed tree
-  float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
-  int b = threadIdx.x;
-  for (; b + 3 * kMergeThreads < ntiles; b += 4 * kMergeThreads) {
-    float4 q[4];
+  const float4_t* slices =
+      reinterpret_cast<const float4_t*>(reinterpret_cast<const char*>(p.partials) + merge_slices_offset(ntiles, mt));
+  const float4_t sp = slices[(int64_t)m * kMergeGroups + threadIdx.x];
+  float gm = sp[0], Sm = sp[1], Tm = sp[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = part[(int64_t)(b + j * kMergeThreads) * mt + m];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) merge_partial(gm, Sm, Tm, q[j].x, q[j].y, q[j].z);
-  }
-  for (; b < ntiles; b += kMergeThreads) {
-    const float4 q = part[(int64_t)b * mt + m];
-    merge_partial(gm, Sm, Tm, q.x, q.y, q.z);
-  }
-  mred[threadIdx.x] = gm;
-  sred[threadIdx.x] = Sm;
-  tred[threadIdx.x] = Tm;
-  __syncthreads();
-  for (int s = kMergeThreads / 2; s >= 1; s >>= 1) {
-    if (threadIdx.x < s) {
-      float a = mred[threadIdx.x], sa = sred[threadIdx.x], ta = tred[threadIdx.x];
-      merge_partial(a, sa, ta, mred[threadIdx.x + s], sred[threadIdx.x + s], tred[threadIdx.x + s]);
-      mred[threadIdx.x] = a;
-      sred[threadIdx.x] = sa;
-      tred[threadIdx.x] = ta;
-    }
-    __syncthreads();
-  }
+  for (int x = 32; x >= 1; x >>= 1) merge_from_lane(gm, Sm, Tm, x);
   if (threadIdx.x != 0) return;
-  const double Sd = sred[0], Td = tred[0];
+  const double Sd = Sm, Td = Tm;
   const float H = (float)(log(Sd) - Td / Sd);
   p.epi.entropy[m] = H;
   // ---- ReSET update: update with H first, then decide ----
@@ -478,8 +518,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_valu_kernel(GemvParams p) {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 as_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
-// Word 3 of a gfx9-family buffer resource for raw byte-addressed loads.
-constexpr int kBufferWord3 = 0x00020000;
 
 template <bool NT>
 __device__ __forceinline__ uint4 ld_w16(const uint8_t* ptr) {
@@ -1328,6 +1366,273 @@ __global__ __launch_bounds__(NW * 64) void gemv_staged_kernel(GemvParams p) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// FP4 MFMA kernel (M = 1..8, K % 256 == 0): raw E2M1 weights, block-diagonal
+// activation
+// ----------------------------------------------------------------------------
+// gfx950's v_mfma_scale_f32_16x16x128_f8f6f4 multiplies E2M1 operands
+// exactly; its E8M0 scales (one per 32 elements) cannot carry NVFP4's E4M3
+// scales (one per 16), so they are 1 here and the block scales are applied to
+// the results.  For that every result must hold a single 16-element block:
+// the A operand (16 rows) is the activation laid out block-diagonally, row
+// MT*b' + j holding token j's codes of block b' of the MFMA's block group and
+// zeros elsewhere, so D[MT*b' + j][n] is the exact block sum of token j with
+// weight row n.  The B operand is the weight codes exactly as they sit in
+// memory: no per-element decode at all.  A 128-element chunk has 8 blocks;
+// one MFMA covers 16 / MT of them, so a chunk takes MT / 2 MFMAs (MT >= 2).
+// Post-scaling costs two operations per result (scale product, FMA): about
+// MT / 8 lane-operations per weight element, against about 1.5 for decoding
+// the weights to f16.
+//
+// Operand layouts (checked on hardware): A lane l holds row l % 16, elements
+// 32 * (l / 16) .. +31 (element t in bits 4t .. 4t+3 of the 16 bytes); B lane
+// l holds column l % 16 over the same elements; D lane l holds column l % 16,
+// rows 4 * (l / 16) .. +3.
+//
+// Loads are the direct-to-LDS ring of gemv_dma_kernel (same slot layout and
+// swizzle).  Waves split K; each lane accumulates its four results per row
+// tile over the wave's steps, and the final reduction adds, per weight row
+// and token, the lanes and waves that hold that token in a fixed order.
+typedef int v8i32_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float4_t mfma_fp4(const uint4& a, const uint4& b) {
+  const v8i32_t A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i32_t B = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  // formats 4/4: E2M1 both; scales 127 = E8M0 1.0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 4, 4, 0, 127, 0,
+                                                           127);
+}
+
+template <int MT>
+__device__ __forceinline__ uint32_t scale_selector(int kg) {
+  if constexpr (MT == 2) return (uint32_t)(2 * kg) | (uint32_t)(2 * kg + 1) << 8;
+  if constexpr (MT == 4) return (uint32_t)kg | (uint32_t)(4 + kg) << 8;
+  const uint32_t x0 = (uint32_t)(kg >> 1);
+  return x0 | (x0 + 2) << 8 | (x0 + 4) << 16 | (x0 + 6) << 24;
+}
+
+// The scale values a lane needs from a 16-byte record (blocks 0..7 of
+// chunk 0 in its first half, chunk 1 in its second), decoded from E4M3:
+// out[h][x] for chunk h and the lane's x-th block of the chunk.
+template <int MT>
+__device__ __forceinline__ void gather_scales(const uint4& rec, uint32_t sel, float (&out)[2][MT == 8 ? 4 : 2]) {
+  if constexpr (MT == 8) {
+    const uint32_t d0 = __builtin_amdgcn_perm(rec.y, rec.x, sel), d1 = __builtin_amdgcn_perm(rec.w, rec.z, sel);
+    const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(d0, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(d0, true);
+    const float2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(d1, false), e = __builtin_amdgcn_cvt_pk_f32_fp8(d1, true);
+    out[0][0] = a[0], out[0][1] = a[1], out[0][2] = b[0], out[0][3] = b[1];
+    out[1][0] = c[0], out[1][1] = c[1], out[1][2] = e[0], out[1][3] = e[1];
+  } else {
+    // two selected bytes of each half, then both pairs in one word
+    const uint32_t lo = __builtin_amdgcn_perm(rec.y, rec.x, sel), hi = __builtin_amdgcn_perm(rec.w, rec.z, sel);
+    const uint32_t d = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    const float2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(d, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+    out[0][0] = a[0], out[0][1] = a[1];
+    out[1][0] = b[0], out[1][1] = b[1];
+  }
+}
+
+template <int MT, int R, int NW, int D, bool SA, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
+  static_assert(MT == 2 || MT == 4 || MT == 8, "tokens per block row group");
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  // SA: the activation codes and scales and the tile's weight scales are
+  // copied into LDS once, before the loop; a ring slot then holds only the
+  // weight codes of a step
+  constexpr int SLOT = SA ? 2048 * R : dma_slot_bytes<R>();
+  constexpr int L = SA ? 2 * R : 3 * R + 2;  // loads per step
+  constexpr int BPM = 16 / MT;   // blocks per MFMA
+  constexpr int S = MT / 2;      // MFMAs per 128-element chunk and row tile
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, kg = lane >> 4;
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int nsteps = (int)(K / 256);
+  const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
+
+  const int64_t rows = N - tile0 < 16 * R ? N - tile0 : 16 * R;
+  const i32x4_t wcr = raw_rsrc(p.w_codes + tile0 * (K / 2), rows * (K / 2));
+  const i32x4_t wsr = raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16));
+  const i32x4_t acr = raw_rsrc(p.a_codes, (int64_t)M * (K / 2));
+  const i32x4_t asr = raw_rsrc(p.a_scales, (int64_t)M * (K / 16));
+  const int q = lane >> 3, c = lane & 7;
+  int vcode[2 * R], vscale[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) vcode[2 * r + h] = (16 * r + 8 * h + q) * (int)(K / 2) + 16 * (c ^ q ^ h);
+    vscale[r] = (16 * r + (lane >> 2)) * (int)(K / 16) + 4 * (lane & 3);
+  }
+  // staged regions (SA): activation codes [MT][K/2], activation scales
+  // [MT][K/16], the tile's weight scales [16 R][K/16], each padded to whole KB
+  const int64_t acb = SA ? pad1k(MT * (K / 2)) : 0, asb = SA ? pad1k(MT * (K / 16)) : 0;
+  const int64_t staged = SA ? acb + asb + pad1k(16 * R * (K / 16)) : 0;
+  const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+  if constexpr (SA) {
+    stage_to_lds<NW>(acr, lds0, (int64_t)M * (K / 2), wave, lane);
+    stage_to_lds<NW>(asr, lds0 + (uint32_t)acb, (int64_t)M * (K / 16), wave, lane);
+    stage_to_lds<NW>(wsr, lds0 + (uint32_t)(acb + asb), rows * (K / 16), wave, lane);
+  }
+  const uint32_t ring = lds0 + (uint32_t)staged + (uint32_t)(wave * D * SLOT);
+  auto issue = [&](int i) {  // the wave's i-th step into slot i % D
+    const int step = wave + i * NW;
+    const uint32_t s = ring + (uint32_t)((i % D) * SLOT);
+    const int co = step * 128, so = step * 16;
+#pragma unroll
+    for (int b = 0; b < 2 * R; ++b) dma_b128(wcr, s + 1024 * b, vcode[b], co);
+    if constexpr (!SA) {
+      dma_b128(acr, s + 2048 * R, vcode[0], co);
+#pragma unroll
+      for (int r = 0; r < R; ++r) dma_b32(wsr, s + 2048 * R + 1024 + 256 * r, vscale[r], so);
+      dma_b32(asr, s + 2048 * R + 1024 + 256 * R, vscale[0], so);
+    }
+  };
+
+  // A side (this lane as an A row): token j, block b' of the MFMA's group
+  const int ja = li % MT, ba = li / MT;
+  // D side (this lane's four results): row 4*kg + v is token (4kg+v) % MT of
+  // block (4kg+v) / MT of the group
+  const char* lstage = reinterpret_cast<const char*>(lds4);
+  const char* lbase = lstage + staged + wave * D * SLOT;
+  int wro[R][2];  // this lane's B chunk (row li, chunk 4h + kg) in each tile
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int hh = li >> 3, qq = li & 7;
+      wro[r][h] = (2 * r + hh) * 1024 + qq * 128 + 16 * ((4 * h + kg) ^ qq ^ hh);
+    }
+  const int aro[2] = {2048 * R + ja * 128 + 16 * ((kg) ^ ja), 2048 * R + ja * 128 + 16 * ((4 + kg) ^ ja)};
+  const int wso = 2048 * R + 1024 + li * 16;       // + 256 r: this lane's weight row scale record
+  const int aso = 2048 * R + 1024 + 256 * R;       // + 16 j: token j's scale record
+  constexpr int SX = MT == 8 ? 4 : 2;              // scale values per chunk h
+  const uint32_t sel = scale_selector<MT>(kg);
+
+  float acc[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[r][v] = 0.0f;
+
+#pragma unroll
+  for (int jj = 0; jj < D - 1; ++jj)
+    if (jj < n) issue(jj);
+  if constexpr (SA) {
+    // this wave's staging copies (issued before the ring's first steps) have
+    // landed, and after the barrier every other wave's
+    if (n >= D - 1) wait_vmcnt<(D - 1) * L>();
+    else wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+  }
+  for (int i = 0; i < n; ++i) {
+    if (i + D - 1 < n) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the reused slot's reads have returned
+      issue(i + D - 1);
+    }
+    const int later = n - 1 - i;
+    if (later >= D - 1) wait_vmcnt<(D - 1) * L>();
+    else if (D > 3 && later == 2) wait_vmcnt<(D > 3 ? 2 * L : 0)>();
+    else if (D > 2 && later == 1) wait_vmcnt<(D > 2 ? L : 0)>();
+    else wait_vmcnt<0>();
+    const char* sl = lbase + (i % D) * SLOT;
+    const int step = wave + i * NW;
+    // scale records of the step: from the slot, or from the staged copies
+    const char* wrec = SA ? lstage + acb + asb + li * (K / 16) + step * 16 : sl + wso;
+    const int64_t wrec_r = SA ? 16 * (K / 16) : 256;  // to the same row of the next tile
+    const char* arec = SA ? lstage + acb + step * 16 : sl + aso;
+    const int64_t arec_j = SA ? K / 16 : 16;  // to the next token
+    // the scales this lane's results need, gathered from the step's 16-byte
+    // scale records with one byte permute per 4 bytes (selectors fixed per
+    // lane) and decoded: sw[r][h][x] for its weight row, sa[v][h][x] for the
+    // token of result v; x = v / 2 (MT = 2) or the MFMA index s (MT = 4, 8)
+    float sw[R][2][SX], sa[4][2][SX];
+#pragma unroll
+    for (int r = 0; r < R; ++r) gather_scales<MT>(*reinterpret_cast<const uint4*>(wrec + r * wrec_r), sel, sw[r]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (MT == 2 && v >= 2) {  // tokens repeat: v and v - 2 hold the same token
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int x = 0; x < SX; ++x) sa[v][h][x] = sa[v - 2][h][x];
+      } else {
+        gather_scales<MT>(*reinterpret_cast<const uint4*>(arec + ((4 * kg + v) % MT) * arec_j), sel, sa[v]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 wb[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) wb[r] = *reinterpret_cast<const uint4*>(sl + wro[r][h]);
+      const char* aptr = SA ? lstage + ja * (K / 2) + step * 128 + 64 * h + 16 * kg : sl + aro[h];
+      const uint4 av = ja < M ? *reinterpret_cast<const uint4*>(aptr) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int b = s * BPM + ba;  // block (0..7 of the chunk) of this lane's A row
+        const bool keep = kg == (b >> 1);
+        const bool hi = (b & 1) != 0;
+        const uint4 A = make_uint4(keep && !hi ? av.x : 0u, keep && !hi ? av.y : 0u, keep && hi ? av.z : 0u,
+                                   keep && hi ? av.w : 0u);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const float4_t d = mfma_fp4(A, wb[r]);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int x = MT == 2 ? v >> 1 : s;
+            acc[r][v] = __builtin_fmaf(d[v], sw[r][h][x] * sa[v][h][x], acc[r][v]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with its ring before the reduction reuses the LDS
+
+  // reduction: red[wave][r][v][lane], then y[j][row] = sum over waves and
+  // over the lanes (kg) and results (v) that hold token j, in a fixed order
+  float* red = reinterpret_cast<float*>(lds4);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
+  __syncthreads();
+  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  constexpr int OUTS = 16 * R * MT;                     // (row, token) results of the tile
+  constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);  // per thread
+  float out[NV];
+  int tok[NV], rowt[NV];
+  bool ok[NV], own[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int o = (int)threadIdx.x + u * NW * 64;
+    out[u] = 0.0f;
+    tok[u] = 0;
+    rowt[u] = 0;
+    ok[u] = own[u] = false;
+    if (o < OUTS) {
+      const int j = o % MT, rt = o / MT;  // token, row of the tile (16 r + nn)
+      const int r = rt >> 4, nn = rt & 15;
+      float sum = 0.0f;
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if ((4 * g + v) % MT == j) sum += red[((w * R + r) * 4 + v) * 64 + g * 16 + nn];
+      const int64_t row = tile0 + rt;
+      out[u] = sum * scale;
+      tok[u] = j;
+      rowt[u] = rt;
+      own[u] = j < M;
+      ok[u] = j < M && row < N;
+      if (ok[u]) p.y[(int64_t)j * N + row] = out[u];
+    }
+  }
+  if constexpr (EPI) lmhead_partials<MT, 16 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
+}
+
 __global__ void reset_state_init_kernel(char* state, int M, int window, size_t sbytes) {
   const int m = blockIdx.x;
   if (m >= M) return;
@@ -1347,7 +1652,7 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5 };
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7 };
 
 struct Variant {
   const char* name;
@@ -1391,6 +1696,16 @@ struct Variant {
     "staged_m" #MT "_g" #G "_r" #R "_w" #NW "_p" #P, STAGED, MT, G, R, NW, P,                   \
         gemv_staged_kernel<MT, G, R, NW, P, false>, gemv_staged_kernel<MT, G, R, NW, P, true> \
   }
+#define FMMA_V(MT, R, NW, D)                                                                         \
+  Variant {                                                                                        \
+    "fmma_m" #MT "_r" #R "_w" #NW "_d" #D, FMMA, MT, 16, R, NW, D,                                 \
+        gemv_fmma_kernel<MT, R, NW, D, false, false>, gemv_fmma_kernel<MT, R, NW, D, false, true> \
+  }
+#define FMMA_SA_V(MT, R, NW, D)                                                                    \
+  Variant {                                                                                      \
+    "fmma_m" #MT "_r" #R "_w" #NW "_d" #D "_sa", FMMASA, MT, 16, R, NW, D,                       \
+        gemv_fmma_kernel<MT, R, NW, D, true, false>, gemv_fmma_kernel<MT, R, NW, D, true, true> \
+  }
 #define DMA_V(MT, R, NW, D)                                                          \
   Variant {                                                                        \
     "dma_m" #MT "_r" #R "_w" #NW "_d" #D, DMA, MT, 16, R, NW, D,                   \
@@ -1418,6 +1733,13 @@ const Variant kVariants[] = {
     STAGED_V(1, 32, 2, 4, 2), STAGED_V(1, 64, 1, 4, 2), STAGED_V(1, 64, 2, 4, 1), STAGED_V(1, 32, 4, 4, 1),
     STAGED_V(1, 32, 2, 8, 1), STAGED_V(1, 64, 1, 8, 2), STAGED_V(2, 32, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
     STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 64, 1, 4, 2),
+    // FP4 MFMA on raw weight codes (K % 256 == 0)
+    FMMA_V(2, 2, 4, 3), FMMA_V(2, 1, 4, 3), FMMA_V(2, 2, 8, 2), FMMA_V(2, 1, 8, 2), FMMA_V(2, 2, 4, 2),
+    FMMA_V(4, 2, 4, 3), FMMA_V(4, 1, 4, 3), FMMA_V(4, 2, 8, 2), FMMA_V(4, 1, 8, 2), FMMA_V(4, 2, 4, 2),
+    FMMA_V(8, 2, 4, 3), FMMA_V(8, 1, 8, 2),
+    FMMA_SA_V(2, 2, 4, 3), FMMA_SA_V(2, 1, 4, 3), FMMA_SA_V(2, 1, 4, 4), FMMA_SA_V(2, 2, 4, 2),
+    FMMA_SA_V(4, 2, 4, 3), FMMA_SA_V(4, 1, 4, 3), FMMA_SA_V(4, 1, 4, 4), FMMA_SA_V(4, 2, 4, 2),
+    FMMA_SA_V(8, 2, 4, 2), FMMA_SA_V(8, 1, 4, 3), FMMA_SA_V(8, 1, 8, 2), FMMA_SA_V(8, 2, 4, 3),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1429,6 +1751,13 @@ int find_variant(const char* name) {
   return -1;
 }
 
+// LDS of the FP4 MFMA kernel with staged activation: activation codes and
+// scales for MT tokens, the tile's weight scales, then a ring of D weight-code
+// slots per wave
+int64_t fmma_sa_lds_bytes(const Variant& v, int64_t K) {
+  return pad1k(v.mt * (K / 2)) + pad1k(v.mt * (K / 16)) + pad1k(16 * v.r * (K / 16)) + (int64_t)v.nw * v.p * 2048 * v.r;
+}
+
 // Index of a variant named by a string literal, looked up once per call site.
 #define VARIANT(name) ([] {                   \
   static const int index_ = find_variant(name); \
@@ -1436,24 +1765,28 @@ int find_variant(const char* name) {
 }())
 
 // Default variant per (M, N, K): the fastest variant of MI355X sweeps over
-// the Qwen3-32B projection shapes (graph-replayed back-to-back launches, each
-// projection's weights rotated over >= 576 MB of copies so that every launch
-// reads HBM), generalised by N and K.  The LDS-copy kernels need
-// K % 256 == 0; other K fall back to the register-staged kernels.
+// the Qwen3-32B projection and LM-head shapes (graph-replayed back-to-back
+// launches, each projection's weights rotated over >= 576 MB of copies so
+// that every launch reads HBM; candidates interleaved, medians compared),
+// generalised by N and K.  The LDS-copy kernels need K % 256 == 0; other K
+// use the register-staged kernels.
 int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
   const bool k256 = K % 256 == 0;
+  // the FP4 MFMA kernel with the activation in LDS, when that fits
+  auto fmma_sa = [&](int i, int otherwise) { return fmma_sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
   if (M <= 1) {
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
     return VARIANT("direct_m1_g32_r1_w4_p1_nt");
   }
   if (M <= 2 && k256)
-    return K >= 12288 ? VARIANT("staged_m2_g64_r1_w4_p2")
+    return K >= 12288 ? fmma_sa(VARIANT("fmma_m2_r2_w4_d3_sa"), VARIANT("staged_m2_g64_r1_w4_p2"))
            : K >= 8192 && N < 16384 ? VARIANT("staged_m2_g64_r1_w4_p1")
                                     : VARIANT("staged_m2_g32_r2_w4_p1");
   if (k256 && N >= 16384) return M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
-  if (K >= 8192) return M <= 4 ? VARIANT("lmfma_m4_r2_w8_p1") : VARIANT("lmfma_m8_r2_w8_p1");
+  if (M <= 4 && k256 && K >= 12288) return fmma_sa(VARIANT("fmma_m4_r2_w4_d3_sa"), VARIANT("lmfma_m4_r2_w8_p1"));
+  if (K >= 8192) return VARIANT("lmfma_m8_r2_w8_p1");
   return VARIANT("lmfma_m8_r1_w4_p1");
 }
 
@@ -1488,9 +1821,11 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // the LDS-staged kernel addresses a row tile and the activation with
   // 32-bit buffer offsets
   auto fits = [&](int i) {
-    if ((kVariants[i].kind == DMA || kVariants[i].kind == STAGED) && K % 256 != 0) return false;
+    const Kind kd = kVariants[i].kind;
+    if ((kd == DMA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
+    if (kd == FMMASA && fmma_sa_lds_bytes(kVariants[i], K) > 163840) return false;
     if (kVariants[i].kind == STAGED && staged_lds_bytes(kVariants[i], K) > 65536) return false;
-    return (kVariants[i].kind != LMFMA && kVariants[i].kind != DMA) || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
+    return (kd != LMFMA && kd != DMA && kd != FMMA && kd != FMMASA) || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
   };
   // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
   // compiled token count covers M
@@ -1512,7 +1847,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
-  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA) {
+  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == FMMA || v.kind == FMMASA) {
     c.kp = (int)K;
     c.rows_per_wg = (int64_t)16 * v.r;
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
@@ -1521,7 +1856,11 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
       const int64_t slots = (int64_t)v.nw * (16 * v.r + 8) * (144 + 20);
       if (slots > c.lds_bytes) c.lds_bytes = slots;
     }
-    if (v.kind == DMA) {
+    if (v.kind == FMMASA) {
+      const int64_t b = fmma_sa_lds_bytes(v, K);
+      if (b > c.lds_bytes) c.lds_bytes = b;
+    }
+    if (v.kind == DMA || v.kind == FMMA) {
       const int64_t ring = (int64_t)v.nw * v.p * ((2 * v.r + 1) * 1024 + (v.r + 1) * 256);
       if (ring > c.lds_bytes) c.lds_bytes = ring;
     }
@@ -1539,8 +1878,9 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = v.kind == STAGED ? staged_lds_bytes(v, K) : 0;
   }
-  // workspace (epilogue only): per-workgroup softmax partials
-  c.ws_bytes = epi ? align256(c.grid * c.mt * 4 * 4) : 0;
+  // workspace (epilogue only): per-workgroup softmax partials, then the
+  // merge's slice partials
+  c.ws_bytes = epi ? align256(merge_slices_offset(c.grid, c.mt) + (int64_t)c.mt * kMergeGroups * 16) : 0;
   return c;
 }
 
@@ -1581,7 +1921,11 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   if (epi) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(M), dim3(kMergeThreads), 0, stream, p, cfg.mt, (int)cfg.grid);
+    hipLaunchKernelGGL(lmhead_slice_kernel, dim3(M * kMergeGroups), dim3(kMergeThreads), 0, stream, p, cfg.mt,
+                       (int)cfg.grid);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(M), dim3(64), 0, stream, p, cfg.mt, (int)cfg.grid);
   }
   return hipGetLastError();
 }

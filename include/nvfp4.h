@@ -54,7 +54,9 @@ typedef enum {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = -1,      /* a required pointer is NULL                     */
   NVFP4_ERR_SHAPE = -2,     /* M not in [1,8], N < 1, K outside [32, 2^24] or
-                               K % 32 != 0                                    */
+                               K % 32 != 0; with the LM-head epilogue also an
+                               N whose workspace would pass 2 GB (N beyond
+                               about 10^8)                                    */
   NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned        */
   NVFP4_ERR_WORKSPACE = -4, /* ws is NULL or ws_bytes is too small             */
   NVFP4_ERR_DEVICE = -5,    /* the current HIP device is not a gfx950         */

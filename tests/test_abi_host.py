@@ -164,3 +164,15 @@ def test_forced_variant_falls_back_when_k_does_not_fit(L, monkeypatch):
     assert F.nvfp4_gemv_variant(8, 1024, 4096) == "dma_m8_r2_w4_d3"
     v = F.nvfp4_gemv_variant(8, 1024, 4128)
     assert v != "dma_m8_r2_w4_d3" and 4128 % F.variant_k_multiple(v) == 0
+
+
+def test_gemv_epilogue_partials_beyond_2gb_are_a_shape_error(L):
+    """The LM-head merge addresses its per-workgroup partials with 32-bit
+    offsets, so an N whose partials would pass 2 GB is rejected before any
+    HIP call (fake buffers far apart, never dereferenced)."""
+    far = 1 << 44
+    st, ent, tmp, flags = A + 7 * far, A + 8 * far, A + 9 * far, A + 10 * far
+    e = ctypes.byref(F.LmheadEpilogue(0.6, 0.4, 1.0, 0.6, 8, 0, flags, st, ent, tmp))
+    M, N, K = 8, 1 << 32, 32
+    assert L.nvfp4_gemv_smallm(M, N, K, A, A + far, A + 2 * far, A + 3 * far, A + 4 * far, A + 5 * far,
+                               A + 6 * far, e, A + 11 * far, 1 << 40, None) == F.NVFP4_ERR_SHAPE

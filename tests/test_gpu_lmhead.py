@@ -134,3 +134,52 @@ def test_full_lm_head_sequence(M):
         ar = (ar[0], ar[1], np.float32(ar[2] * np.float32(2.0 ** u[t])))
         y_ref, ref_abs = O.gemv_ref(ar, wr)
         assert_gemv_close(logits[t][:, rows], y_ref, ref_abs, what=f"lm head t={t}")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_epilogue_graph_replays_match_eager(M):
+    """The LM-head call (GEMV, partials, multi-workgroup merge with its
+    self-resetting counters) captured in a HIP graph and replayed several
+    times, with eager work in between, gives the eager entropies every time;
+    the ReSET state advances once per replay exactly as eager calls do."""
+    dev = torch.device("cuda:0")
+    N, K = 20000, 1024
+    print(f"[lmhead graph] M={M} N={N} K={K}", flush=True)
+    w = W.small_random_weights(77, N, K, scale=0.2)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    aq = F.nvfp4_quantize_act(bf16_dev(W.small_random_bf16(78, M, K)))
+    ws = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, N, K), dev)
+    flags = torch.zeros(M, dtype=torch.uint8, device=dev)
+    ent, tmp = torch.empty(M, device=dev), torch.empty(M, device=dev)
+    y = torch.empty((M, N), device=dev)
+    s = torch.cuda.Stream()
+
+    def call(st):
+        epi = F.Epilogue(step_start=flags, state=st, entropy=ent, temperature=tmp, window=4)
+        F.nvfp4_gemv_smallm(aq, wq, y=y, epi=epi, ws=ws, stream=torch.cuda.current_stream())
+
+    # eager reference: four calls on a fresh state
+    st_e = F.new_reset_state(M, 4, dev)
+    ref_H, ref_T = [], []
+    for _ in range(4):
+        call(st_e)
+        torch.cuda.synchronize()
+        ref_H.append(ent.cpu().numpy().copy())
+        ref_T.append(tmp.cpu().numpy().copy())
+    # graph: capture one call on a second state, replay it four times
+    st_g = F.new_reset_state(M, 4, dev)
+    st_w = F.new_reset_state(M, 4, dev)
+    with torch.cuda.stream(s):
+        call(st_w)  # warm-up outside the capture, on a scratch state
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(st_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(ent.cpu().numpy(), ref_H[r]), (r, ent.cpu().numpy(), ref_H[r])
+        assert np.array_equal(tmp.cpu().numpy(), ref_T[r]), (r, tmp.cpu().numpy(), ref_T[r])
+        y.zero_()  # eager work between replays
+        torch.cuda.synchronize()
