@@ -19,6 +19,9 @@ Sources:
 * Two temperatures (project page rule; reading notes, section 4.3): T_low
   when H_t is below the threshold, T_high otherwise; T_base is the model
   default and is used only when ReSET is switched off.
+* The fixed-threshold rule (reading notes, section 3.1, formula (1)): the
+  same two temperatures with the threshold held at tau0 for every token,
+  the token-level baseline that SAT replaces.
 
 Readings taken where the pages are silent or garbled (listed in the design
 notes): natural log, softmax at temperature 1 over all logits; update first,
@@ -57,7 +60,7 @@ class ResetParams:
     t_high: float = 1.0
     t_base: float = 0.6
     window: int = 8
-    mode: int = 0          # 0 = ReSET, 1 = BASE (always t_base)
+    mode: int = 0          # 0 = ReSET, 1 = BASE (always t_base), 2 = fixed threshold tau0
 
 
 @dataclass
@@ -95,6 +98,8 @@ def reset_sequence(H, step_start, p: ResetParams) -> ResetTrace:
         Hstep[t] = win if step_len <= p.window else in_step
         unc[t] = Hstep[t] > Hbar[t]
         tau[t] = Hstep[t] if unc[t] else p.tau0
+        if p.mode == 2:          # formula (1): the threshold is tau0 whatever the step
+            tau[t] = p.tau0
         if p.mode == 1:
             T[t] = p.t_base
         else:
