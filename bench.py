@@ -23,6 +23,9 @@ Prints one JSON line:
                its replay on the launch stream), against the 8 TB/s HBM peak
   cpu_baseline the CPU oracle (quantize + dequantize + fp64 GEMV) on a
                bounded row sample of the same projections, same byte formula
+  extra        the LM head (N=151936) with the entropy / ReSET epilogue and
+               the top-p = 0.95 draw at the epilogue's temperatures, and the
+               64-layer decode chain captured in one graph
 """
 
 from __future__ import annotations
@@ -51,8 +54,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "98a7b6ef95f95211de76d3ddda213c9bf67be0d8a3af4b10701c4b98d4589bb4",
-    "bytes_per_step": 1107228786,
+    "sha256": "2fda5f80918e41ef2489ffec2958d237af25a320390720e86c6d54e7bc21277d",
+    "bytes_per_step": 1107150050,
 }
 
 
@@ -358,7 +361,9 @@ def _graph_us(fn, reps, stream):
 
 def bench_lm_head(args, stream):
     """LM head N=151936 K=5120 at M = 1 and 8: quantization + GEMV with the
-    fused entropy / ReSET epilogue, and the plain GEMV for comparison."""
+    fused entropy / ReSET epilogue, the plain GEMV for comparison, and the
+    top-p = 0.95 draw at the epilogue's temperatures (alone and as the tail
+    of the decode step)."""
     import torch
 
     import fp4_decode_gemv_amd as F
@@ -386,6 +391,18 @@ def bench_lm_head(args, stream):
         ews = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, case.N, case.K), dev)
         gn = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, case.N, case.K)
         gws = F.new_workspace(gn, dev) if gn else None
+        uni = torch.from_numpy(W.sampler_uniforms(3500, 1, M)[0]).to(dev)
+        tok = torch.empty(M, dtype=torch.int32, device=dev)
+        nuc = torch.empty(M, dtype=torch.int32, device=dev)
+        sws = torch.empty(F.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, M, case.N, 0), dtype=torch.uint8, device=dev)
+
+        def sample(i):
+            F.nvfp4_sample_top_p(y, epi.temperature, 0.95, uni, tokens=tok, nucleus=nuc, ws=sws, stream=stream)
+
+        def decode_tail(i):
+            F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
+            F.nvfp4_gemv_smallm(aq, copies[i % 2], y=y, epi=epi, ws=ews, stream=stream)
+            sample(i)
 
         def with_epi(i):
             F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
@@ -400,13 +417,17 @@ def bench_lm_head(args, stream):
         t_all = _graph_us(with_epi, args.reps, stream)
         t_epi = _graph_us(epi_only, args.reps, stream)
         t_plain = _graph_us(plain, args.reps, stream)
+        t_tail = _graph_us(decode_tail, args.reps, stream)
+        t_samp = _graph_us(sample, args.reps, stream)  # logits and temperatures of the last step
         out.append({"M": M, "N": case.N, "K": case.K, "weight_bytes": wb,
                     "variant": F.nvfp4_gemv_variant(M, case.N, case.K, True),
                     "quant_gemv_epilogue_us": round(t_all, 2), "gemv_epilogue_us": round(t_epi, 2),
                     "gemv_plain_us": round(t_plain, 2), "gemv_epilogue_gbs": round(wb / t_epi / 1e3, 1),
-                    "epilogue_overhead_us": round(t_epi - t_plain, 2)})
+                    "epilogue_overhead_us": round(t_epi - t_plain, 2),
+                    "sample_top_p_us": round(t_samp, 2), "quant_gemv_epilogue_sample_us": round(t_tail, 2)})
         log(args, f"[lmhead] M={M} quant+gemv+epilogue {t_all:.2f} us, gemv+epilogue {t_epi:.2f} us "
-                  f"({wb / t_epi / 1e3:.0f} GB/s), plain gemv {t_plain:.2f} us")
+                  f"({wb / t_epi / 1e3:.0f} GB/s), plain gemv {t_plain:.2f} us, top-p draw {t_samp:.2f} us, "
+                  f"whole tail {t_tail:.2f} us")
     del copies, base
     torch.cuda.empty_cache()
     return out

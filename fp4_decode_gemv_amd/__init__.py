@@ -12,6 +12,8 @@ Functions keep the C names:
 * ``nvfp4_quantize_act(x_bf16, gscale=None)`` -> ``(codes, scales, gscale)``
 * ``nvfp4_gemv_smallm(a, w, ...)`` -> ``y`` (optionally with the LM-head
   epilogue)
+* ``nvfp4_sample_top_p(logits, temperature, top_p, uniforms)`` ->
+  ``(tokens, nucleus)``
 * ``nvfp4_workspace_size``, ``nvfp4_workspace_init``,
   ``nvfp4_reset_state_size``, ``nvfp4_reset_state_init``,
   ``nvfp4_status_str``.
@@ -42,6 +44,7 @@ NVFP4_OP_PACK = 0
 NVFP4_OP_QUANT = 1
 NVFP4_OP_GEMV = 2
 NVFP4_OP_GEMV_LMHEAD = 3
+NVFP4_OP_SAMPLE = 4
 
 EXPORTED = (
     "nvfp4_status_str",
@@ -54,6 +57,7 @@ EXPORTED = (
     "nvfp4_gemv_smallm",
     "nvfp4_gemv_variant",
     "nvfp4_gemv_variant_name",
+    "nvfp4_sample_top_p",
 )
 
 
@@ -116,6 +120,8 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_gemv_smallm.restype = c_int
     L.nvfp4_gemv_smallm.argtypes = [c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(LmheadEpilogue), vp, sz, vp]
+    L.nvfp4_sample_top_p.restype = c_int
+    L.nvfp4_sample_top_p.argtypes = [c_int, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -284,7 +290,7 @@ class Epilogue:
     t_high: float = 1.0
     t_base: float = 0.6
     window: int = 8
-    mode: int = 0
+    mode: int = 0            # 0 = ReSET, 1 = BASE (t_base), 2 = fixed threshold tau0
 
     def as_c(self) -> LmheadEpilogue:
         return LmheadEpilogue(self.tau0, self.t_low, self.t_high, self.t_base, self.window, self.mode,
@@ -313,3 +319,33 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
                                    None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,
                                    _stream(stream)), "nvfp4_gemv_smallm")
     return y
+
+
+def nvfp4_sample_top_p(logits, temperature, top_p: float, uniforms, tokens=None, nucleus=None, ws=None,
+                       stream=None):
+    """One top-p draw per row of ``logits`` [M][N] fp32 at ``temperature``
+    [M] fp32 with the caller's ``uniforms`` [M] fp32 in [0, 1).  ``ws``: a
+    workspace of nvfp4_workspace_size(NVFP4_OP_SAMPLE, M, N, 0) bytes
+    (allocated here when not given; no zero-fill needed).  Returns
+    (tokens int32 [M], nucleus sizes int32 [M])."""
+    import torch
+
+    M, N = logits.shape
+    dev = logits.device
+    need = nvfp4_workspace_size(NVFP4_OP_SAMPLE, M, N, 0)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if tokens is None:
+        tokens = torch.empty(M, dtype=torch.int32, device=dev)
+    if nucleus is None:
+        nucleus = torch.empty(M, dtype=torch.int32, device=dev)
+    for t, dt in ((logits, torch.float32), (temperature, torch.float32), (uniforms, torch.float32),
+                  (tokens, torch.int32), (nucleus, torch.int32)):
+        if not t.is_contiguous() or t.dtype != dt or t.device != dev:
+            raise ValueError(f"nvfp4_sample_top_p needs contiguous {dt} tensors on {dev}")
+    if temperature.numel() != M or uniforms.numel() != M or tokens.numel() != M or nucleus.numel() != M:
+        raise ValueError("temperature, uniforms, tokens and nucleus hold one value per row")
+    _check(lib().nvfp4_sample_top_p(M, N, _ptr(logits), _ptr(temperature), float(top_p), _ptr(uniforms),
+                                    _ptr(tokens), _ptr(nucleus), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)), "nvfp4_sample_top_p")
+    return tokens, nucleus

@@ -29,7 +29,7 @@ LIB = os.path.join(LIBDIR, "libnvfp4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 
-SOURCES = ["nvfp4_abi.cpp", "nvfp4_quant.hip", "nvfp4_gemv.hip"]
+SOURCES = ["nvfp4_abi.cpp", "nvfp4_quant.hip", "nvfp4_gemv.hip", "nvfp4_sample.hip"]
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950",

@@ -19,6 +19,7 @@ namespace {
 using namespace nvfp4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   if (!a || !b || an == 0 || bn == 0) return false;
@@ -63,8 +64,10 @@ const char* nvfp4_status_str(int status) {
   switch (status) {
     case NVFP4_OK: return "NVFP4_OK";
     case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
-    case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: need 1<=M<=8, N>=1, 32<=K<=2^24, K%32==0";
-    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case NVFP4_ERR_SHAPE:
+      return "NVFP4_ERR_SHAPE: a size is out of range (GEMV and quantization: 1<=M<=8, N>=1, 32<=K<=2^24, "
+             "K%32==0; sampler: 1<=M<=65535, 1<=N<2^24)";
+    case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a pointer is not aligned (16 bytes; 4 for the sampler)";
     case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
     case NVFP4_ERR_DEVICE: return "NVFP4_ERR_DEVICE: the current device is not a gfx950";
     case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP: a HIP call or kernel launch failed";
@@ -87,6 +90,9 @@ size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K) {
     case NVFP4_OP_GEMV_LMHEAD:
       if (!shape_ok(M, N, K)) return 0;
       return gemv_workspace_bytes(M, N, K, true);
+    case NVFP4_OP_SAMPLE:
+      if (M < 1 || M > kSampleMaxM || N < 1 || N > kSampleMaxN) return 0;
+      return sample_workspace_bytes(M, N);
   }
   return 0;
 }
@@ -190,7 +196,7 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
   EpilogueArgs ea{};
   if (epi) {
     if (!epi->step_start || !epi->state || !epi->entropy || !epi->temperature) return NVFP4_ERR_NULL;
-    if (epi->window < 1 || epi->window > kResetMaxWindow || (epi->mode != 0 && epi->mode != 1))
+    if (epi->window < 1 || epi->window > kResetMaxWindow || (epi->mode < 0 || epi->mode > 2))
       return NVFP4_ERR_ARG;
     if (!aligned16(epi->state)) return NVFP4_ERR_ALIGN;
     const size_t stb = (size_t)M * reset_state_bytes(epi->window);
@@ -224,5 +230,33 @@ const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead) {
 }
 
 const char* nvfp4_gemv_variant_name(int index) { return gemv_variant_by_index(index); }
+
+int nvfp4_sample_top_p(int M, int64_t N, const float* logits, const float* temperature, float top_p,
+                       const float* uniforms, int32_t* tokens, int32_t* nucleus, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (M < 1 || M > kSampleMaxM || N < 1 || N > kSampleMaxN) return NVFP4_ERR_SHAPE;
+  if (!logits || !temperature || !uniforms || !tokens) return NVFP4_ERR_NULL;
+  if (!aligned4(logits) || !aligned4(temperature) || !aligned4(uniforms) || !aligned4(tokens) ||
+      (nucleus && !aligned4(nucleus)))
+    return NVFP4_ERR_ALIGN;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return NVFP4_ERR_ARG;
+  const size_t need = sample_workspace_bytes(M, N);
+  if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NVFP4_ERR_ALIGN;
+  const size_t lb = (size_t)M * (size_t)N * 4, vb = (size_t)M * 4;
+  const void* outs[3] = {tokens, nucleus, ws};
+  const size_t outb[3] = {vb, nucleus ? vb : 0, need};
+  for (int k = 0; k < 3; ++k) {
+    if (overlaps(outs[k], outb[k], logits, lb) || overlaps(outs[k], outb[k], temperature, vb) ||
+        overlaps(outs[k], outb[k], uniforms, vb))
+      return NVFP4_ERR_ARG;
+    for (int l = k + 1; l < 3; ++l)
+      if (overlaps(outs[k], outb[k], outs[l], outb[l])) return NVFP4_ERR_ARG;
+  }
+  const int d = check_device();
+  if (d != NVFP4_OK) return d;
+  return hip_status(launch_sample_top_p(M, N, logits, temperature, top_p, uniforms, tokens, nucleus, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
 
 }  // extern "C"

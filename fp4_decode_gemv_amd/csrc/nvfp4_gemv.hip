@@ -347,8 +347,9 @@ __global__ __launch_bounds__(64) void lmhead_merge_kernel(GemvParams p, int mt, 
   const double hstep = st->step_len <= w ? wsum / (double)nwin : st->step_sum / (double)st->step_len;
   const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
   float T_t;
-  if (p.epi.mode == 1) T_t = p.epi.t_base;
-  else T_t = h < tau ? p.epi.t_low : p.epi.t_high;
+  if (p.epi.mode == 1) T_t = p.epi.t_base;                                   // BASE
+  else if (p.epi.mode == 2) T_t = h < (double)p.epi.tau0 ? p.epi.t_low : p.epi.t_high;  // fixed threshold
+  else T_t = h < tau ? p.epi.t_low : p.epi.t_high;                           // ReSET
   p.epi.temperature[m] = T_t;
 }
 

@@ -79,4 +79,15 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
 
 hipError_t launch_reset_state_init(void* state, int M, int window, hipStream_t stream);
 
+// ----------------------------------------------------------------- sampler --
+
+constexpr int64_t kSampleMaxN = ((int64_t)1 << 24) - 1;  // fixed-point mass sums fit 64 bits
+constexpr int kSampleMaxM = 65535;
+constexpr int64_t kSampleChunk = 4096;  // elements per workgroup of the wide launches
+
+size_t sample_workspace_bytes(int M, int64_t N);
+hipError_t launch_sample_top_p(int M, int64_t N, const float* logits, const float* temperature, float top_p,
+                               const float* uniforms, int32_t* tokens, int32_t* nucleus, void* ws,
+                               hipStream_t stream);
+
 }  // namespace nvfp4

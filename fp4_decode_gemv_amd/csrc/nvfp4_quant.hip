@@ -364,10 +364,20 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint
     hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x, nelem,
                        partials);
   }
-  // workgroup size: small tensors spread over more CUs
-  const int threads = nelem <= 16384 ? 64 : nelem <= 65536 ? 256 : 1024;
+  // workgroup size, from graph-replayed timings of every decode shape: when
+  // every workgroup reads the whole tensor for the amax (GS_SELF), larger
+  // tensors want fewer, larger workgroups; otherwise each workgroup reads
+  // only its own chunk and 64 threads spread the divisions over the most CUs
+  const int threads = mode != GS_SELF  ? 64
+                      : nelem <= 8192  ? 64
+                      : nelem <= 16384 ? 128
+                      : nelem <= 32768 ? 256
+                                       : 512;
   const int64_t grid = (nelem + (int64_t)threads * 8 - 1) / ((int64_t)threads * 8);
-  auto fn = threads == 64 ? quantize_act_kernel<64> : threads == 256 ? quantize_act_kernel<256> : quantize_act_kernel<1024>;
+  auto fn = threads == 64    ? quantize_act_kernel<64>
+            : threads == 128 ? quantize_act_kernel<128>
+            : threads == 256 ? quantize_act_kernel<256>
+                             : quantize_act_kernel<512>;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, stream, x, nelem, codes, scales, gscale, (int)mode,
                      partials, n_parts);
   return hipGetLastError();

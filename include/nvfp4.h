@@ -29,8 +29,10 @@
  *   - Arguments are validated on the host BEFORE any HIP call.  A negative
  *     status means nothing was launched and no output was touched.
  *   - Device pointers must be 16-byte aligned (NVFP4_ERR_ALIGN otherwise),
- *     except scalars (global scales, entropy/temperature outputs, flags).
- *   - Shapes: 1 <= M <= 8, N >= 1, 32 <= K <= 2^24, K % 32 == 0.
+ *     except scalars (global scales, entropy/temperature outputs, flags)
+ *     and the sampler's arrays (4 bytes).
+ *   - Shapes: 1 <= M <= 8, N >= 1, 32 <= K <= 2^24, K % 32 == 0 (the
+ *     sampler: 1 <= M <= 65535, 1 <= N < 2^24).
  *   - Outputs must not overlap inputs (NVFP4_ERR_ARG).
  *   - Non-finite inputs give undefined (but memory-safe) results.
  *   - Workspace `ws` is caller-owned device scratch of at least
@@ -56,8 +58,9 @@ typedef enum {
   NVFP4_ERR_SHAPE = -2,     /* M not in [1,8], N < 1, K outside [32, 2^24] or
                                K % 32 != 0; with the LM-head epilogue also an
                                N whose workspace would pass 2 GB (N beyond
-                               about 10^8)                                    */
-  NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned        */
+                               about 10^8); sampler sizes out of range        */
+  NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned (the
+                               sampler's: not 4-byte aligned)                 */
   NVFP4_ERR_WORKSPACE = -4, /* ws is NULL or ws_bytes is too small             */
   NVFP4_ERR_DEVICE = -5,    /* the current HIP device is not a gfx950         */
   NVFP4_ERR_HIP = -6,       /* a HIP runtime call or kernel launch failed     */
@@ -69,13 +72,14 @@ typedef enum {
 enum { NVFP4_GS_DYNAMIC = 0, NVFP4_GS_STATIC = 1 };
 
 /* ops for nvfp4_workspace_size */
-enum { NVFP4_OP_PACK = 0, NVFP4_OP_QUANT = 1, NVFP4_OP_GEMV = 2, NVFP4_OP_GEMV_LMHEAD = 3 };
+enum { NVFP4_OP_PACK = 0, NVFP4_OP_QUANT = 1, NVFP4_OP_GEMV = 2, NVFP4_OP_GEMV_LMHEAD = 3, NVFP4_OP_SAMPLE = 4 };
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* nvfp4_status_str(int status);
 
 /* Bytes of workspace the op needs for this shape (0 = none; M is ignored
- * for NVFP4_OP_PACK, where N x K is the weight).  Pure host function. */
+ * for NVFP4_OP_PACK, where N x K is the weight; K is ignored for
+ * NVFP4_OP_SAMPLE, where N is the vocabulary).  Pure host function. */
 size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K);
 
 /* Zero-fill a workspace with a kernel on `stream` (graph-capturable; no
@@ -132,12 +136,17 @@ int nvfp4_reset_state_init(void* state, int M, int window, void* stream);
  *           step is at most `window` positions long, else the step's mean;
  *   tau   = Hstep if Hstep > Hbar (uncertain step) else tau0;
  *   T     = t_low if H_t < tau else t_high      (mode 0, ReSET)
- *   T     = t_base                              (mode 1, ReSET off).
+ *   T     = t_base                              (mode 1, ReSET off)
+ *   T     = t_low if H_t < tau0 else t_high     (mode 2, the fixed-threshold
+ *           rule of the reading notes, section 3.1, formula (1): the
+ *           token-level baseline ReSET improves on).
+ * The state is updated in every mode, so a sequence may switch modes.
+ * Any other mode is NVFP4_ERR_ARG.
  */
 typedef struct {
   float tau0, t_low, t_high, t_base;
   int window;                 /* must equal the window the states were initialised with */
-  int mode;                   /* 0 = ReSET, 1 = BASE                                     */
+  int mode;                   /* 0 = ReSET, 1 = BASE, 2 = fixed threshold tau0           */
   const uint8_t* step_start;  /* [M] device: 1 = this position starts a new step          */
   void* state;                /* [M] device states (nvfp4_reset_state_size(window) each) */
   float* entropy;             /* [M] device out, nats                                    */
@@ -172,6 +181,36 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K,
  * of the process, so a captured graph replays the same kernels.
  */
 const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead);
+
+/*
+ * Top-p (nucleus) sampling of one token per sequence from the logits
+ * [M][N] fp32 (row-major, e.g. the y of an LM-head nvfp4_gemv_smallm), at
+ * the per-sequence temperature temperature[M] (e.g. the epilogue's output).
+ * The decode loop of the ReSET reading notes samples with top-p = 0.95
+ * (section 6.1) at the temperature chosen per token (section 4.3); nucleus
+ * sampling as published by Holtzman et al. (ICLR 2020):
+ *   p = softmax(z / T); order = decreasing logit, equal logits by
+ *   increasing index; the nucleus is the shortest prefix of the order whose
+ *   mass is >= top_p; the token is the first of the order whose cumulative
+ *   mass exceeds u * (nucleus mass), with u = uniforms[m] in [0, 1) drawn
+ *   by the caller (values outside are clamped into it).
+ * Out: tokens[M] int32; nucleus[M] int32 = nucleus size (may be NULL).
+ * Probabilities are float32 exponentials summed in 2^-40 fixed point, so the
+ * cut points agree with exact arithmetic to within a few 1e-6 of the row's
+ * mass; repeated calls give identical tokens.  Logits must be finite; a row
+ * whose temperature is not positive and finite gets token -1, nucleus 0.
+ * Array pointers are device pointers, 4-byte aligned.  Workspace: ws (16-byte
+ * aligned) of nvfp4_workspace_size(NVFP4_OP_SAMPLE, M, N, 0) bytes; it
+ * needs no zero-fill (every call clears what it accumulates into) and holds
+ * nothing between calls.  Outputs and ws must not overlap inputs or each
+ * other.  Three launches on `stream`.
+ * Errors: NVFP4_ERR_SHAPE (M outside [1, 65535], N outside [1, 2^24 - 1]),
+ * NVFP4_ERR_NULL, NVFP4_ERR_ALIGN, NVFP4_ERR_WORKSPACE, NVFP4_ERR_ARG
+ * (top_p outside (0, 1], overlap), NVFP4_ERR_DEVICE, NVFP4_ERR_HIP.
+ */
+int nvfp4_sample_top_p(int M, int64_t N, const float* logits, const float* temperature, float top_p,
+                       const float* uniforms, int32_t* tokens, int32_t* nucleus, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Name of compiled kernel variant `index` (0-based), NULL past the end.
  * Setting the environment variable NVFP4_GEMV_VARIANT to one of these

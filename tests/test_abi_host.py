@@ -176,3 +176,36 @@ def test_gemv_epilogue_partials_beyond_2gb_are_a_shape_error(L):
     M, N, K = 8, 1 << 32, 32
     assert L.nvfp4_gemv_smallm(M, N, K, A, A + far, A + 2 * far, A + 3 * far, A + 4 * far, A + 5 * far,
                                A + 6 * far, e, A + 11 * far, 1 << 40, None) == F.NVFP4_ERR_SHAPE
+
+
+def test_sample_top_p_errors(L):
+    s = L.nvfp4_sample_top_p
+    z, T, u, tok, nuc, ws = A, A + BIG, A + 2 * BIG, A + 3 * BIG, A + 4 * BIG, A + 5 * BIG
+    need = L.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, 2, 100, 0)
+    assert need > 0
+    assert L.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, 8, 151936, 0) > L.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, 1, 151936, 0)
+    assert L.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, 0, 100, 0) == 0
+
+    def call(M=2, N=100, z=z, T=T, p=0.95, u=u, tok=tok, nuc=nuc, ws=ws, wsb=need):
+        return s(M, N, z, T, p, u, tok, nuc, ws, wsb, None)
+
+    assert call(M=0) == F.NVFP4_ERR_SHAPE
+    assert call(M=65536) == F.NVFP4_ERR_SHAPE
+    assert call(N=0) == F.NVFP4_ERR_SHAPE
+    assert call(N=1 << 24) == F.NVFP4_ERR_SHAPE
+    assert call(z=None) == F.NVFP4_ERR_NULL
+    assert call(T=None) == F.NVFP4_ERR_NULL
+    assert call(u=None) == F.NVFP4_ERR_NULL
+    assert call(tok=None) == F.NVFP4_ERR_NULL
+    assert call(z=z + 2) == F.NVFP4_ERR_ALIGN
+    assert call(tok=tok + 1) == F.NVFP4_ERR_ALIGN
+    for p in (0.0, -0.5, 1.0001, float("nan")):
+        assert call(p=p) == F.NVFP4_ERR_ARG, p
+    assert call(ws=None) == F.NVFP4_ERR_WORKSPACE
+    assert call(wsb=need - 1) == F.NVFP4_ERR_WORKSPACE
+    assert call(ws=ws + 8) == F.NVFP4_ERR_ALIGN
+    assert call(tok=z + 40) == F.NVFP4_ERR_ARG        # tokens inside the logits
+    assert call(nuc=tok + 4) == F.NVFP4_ERR_ARG       # nucleus overlapping tokens
+    assert call(tok=T) == F.NVFP4_ERR_ARG             # output over an input
+    assert call(ws=z + 256) == F.NVFP4_ERR_ARG        # workspace over the logits
+    assert call(ws=tok - 256) == F.NVFP4_ERR_ARG      # workspace over an output

@@ -48,7 +48,7 @@ def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None):
     return logits, np.array(Hs), np.array(Ts)
 
 
-@pytest.mark.parametrize("mode,M,N,K", [(0, 4, 3000, 512), (1, 4, 3000, 512), (0, 1, 2500, 1024),
+@pytest.mark.parametrize("mode,M,N,K", [(0, 4, 3000, 512), (1, 4, 3000, 512), (2, 4, 3000, 512), (0, 1, 2500, 1024),
                                          (0, 8, 2000, 8192), (0, 2, 4099, 256)])
 def test_small_vocab_sequence(mode, M, N, K):
     P = 60
@@ -72,6 +72,10 @@ def test_small_vocab_sequence(mode, M, N, K):
         assert ok.all(), (m, np.nonzero(~ok))
         if mode == 1:
             assert np.all(T[:, m] == np.float32(0.6))
+        if mode == 2:
+            Hm = H[:, m].astype(np.float64)
+            clear = np.abs(Hm - p.tau0) >= BAND
+            assert np.all(T[clear, m] == np.where(Hm[clear] < p.tau0, np.float32(p.t_low), np.float32(p.t_high)))
     # logits of the last step against the oracle
     wr = O.quantize_nvfp4(w)
     ar = O.quantize_act_bf16(xs[-1])

@@ -39,3 +39,11 @@ def test_step_flags_and_cases():
     cases = W.qwen3_32b_cases()
     assert [(c.N, c.K) for c in cases] == [(10240, 5120), (5120, 8192), (51200, 5120), (5120, 25600)]
     assert W.qwen3_8b_cases()[3].swiglu
+
+
+def test_sampler_uniforms():
+    u = W.sampler_uniforms(3500, 4, 8)
+    assert u.shape == (4, 8) and u.dtype == np.float32
+    assert np.all((u >= 0) & (u < 1))
+    assert np.array_equal(W.sampler_uniforms(3500, 4, 3), u[:, :3])   # fewer sequences: a prefix
+    assert not np.array_equal(W.sampler_uniforms(3501, 4, 8), u)

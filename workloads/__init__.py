@@ -257,6 +257,13 @@ def step_flags(seed: int, positions: int, seqs: int = 8, p: float = 0.02) -> np.
     return f
 
 
+def sampler_uniforms(seed: int, positions: int, seqs: int = 8) -> np.ndarray:
+    """float32 [positions][seqs] in [0, 1): the caller's random numbers for
+    the top-p draws (the sampler itself draws none)."""
+    rng = np.random.default_rng(seed)
+    return rng.random((positions, 8), dtype=np.float32)[:, :seqs].copy()
+
+
 def pow2_exponents(seed: int, positions: int, hi: int = 6) -> np.ndarray:
     """Integers u ~ U{0..hi} per position (activations scaled by 2**u)."""
     return np.random.default_rng(seed).integers(0, hi + 1, positions)
