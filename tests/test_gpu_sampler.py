@@ -109,6 +109,24 @@ def test_near_flat_logits_refine_by_key_bits():
     _check(z, T, 0.3, u)
 
 
+def test_large_bucket_inside_the_collected_list():
+    """600 near-equal logits (one bucket) hold most of the mass: the list of
+    collected elements does not overflow, but the cut's bucket is larger than
+    the directly ranked set, so the cut takes the passes over the row."""
+    rng = np.random.default_rng(16)
+    M, N = 8, 20000
+    z = np.full((M, N), -30.0, dtype=np.float32)
+    for m in range(M):
+        idx = rng.choice(N, 603, replace=False)
+        z[m, idx[:600]] = (0.005 * rng.random(600)).astype(np.float32)
+        z[m, idx[600:]] = np.array([1.0, 2.0, 3.0], dtype=np.float32)
+    T = np.full(M, 1.0, dtype=np.float32)
+    u = rng.random(M).astype(np.float32)
+    for top_p in (0.95, 0.5):
+        tok, nuc, exact = _check(z, T, top_p, u)
+        assert exact >= M // 2, exact
+
+
 def test_few_distinct_values_with_many_ties():
     rng = np.random.default_rng(10)
     M, N = 8, 12000
