@@ -1090,11 +1090,26 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int MT, int R, int NW, int D, bool EPI>
+__host__ __device__ constexpr int64_t pad1k(int64_t b) { return (b + 1023) / 1024 * 1024; }
+
+// Copy `bytes` (a multiple of 16) from rsrc into LDS at `lds`: 1 KB per wave
+// instruction, chunks spread over the NW waves.  The whole source offset is
+// in the per-lane operand, so lanes past `bytes` are out of range.
+template <int NW>
+__device__ __forceinline__ void stage_to_lds(const i32x4_t& rsrc, uint32_t lds, int64_t bytes, int wave, int lane) {
+  const int chunks = (int)((bytes + 1023) / 1024);
+  for (int ch = wave; ch < chunks; ch += NW) dma_b128(rsrc, lds + 1024 * ch, 1024 * ch + 16 * lane, 0);
+}
+
+template <int MT, int R, int NW, int D, bool SA, bool EPI>
 __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
   static_assert(D >= 2 && D <= 4, "ring depth");
-  constexpr int SLOT = dma_slot_bytes<R>();
-  constexpr int L = 3 * R + 2;  // loads per step
+  // SA: the activation codes and scales and the tile's weight scales are
+  // copied into LDS once, before the loop (as in gemv_fmma_kernel); a ring
+  // slot then holds only the weight codes of a step, two 1 KB loads per row
+  // tile instead of 3 R + 2 loads
+  constexpr int SLOT = SA ? 2048 * R : dma_slot_bytes<R>();
+  constexpr int L = SA ? 2 * R : 3 * R + 2;  // loads per step
   extern __shared__ uint4 lds4[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: step offsets go to SGPRs
@@ -1122,22 +1137,34 @@ __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
     vscale[r] = (16 * r + (lane >> 2)) * (int)(K / 16) + 4 * (lane & 3);
   }
 
-  const uint32_t ring = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4)) +
-                        (uint32_t)(wave * D * SLOT);
+  // staged regions (SA): activation codes [MT][K/2], activation scales
+  // [MT][K/16], the tile's weight scales [16 R][K/16], each padded to whole KB
+  const int64_t acb = SA ? pad1k(MT * (K / 2)) : 0, asb = SA ? pad1k(MT * (K / 16)) : 0;
+  const int64_t staged = SA ? acb + asb + pad1k(16 * R * (K / 16)) : 0;
+  const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+  if constexpr (SA) {
+    stage_to_lds<NW>(acr, lds0, (int64_t)M * (K / 2), wave, lane);
+    stage_to_lds<NW>(asr, lds0 + (uint32_t)acb, (int64_t)M * (K / 16), wave, lane);
+    stage_to_lds<NW>(wsr, lds0 + (uint32_t)(acb + asb), rows * (K / 16), wave, lane);
+  }
+  const uint32_t ring = lds0 + (uint32_t)staged + (uint32_t)(wave * D * SLOT);
   auto issue = [&](int i) {  // the wave's i-th step into slot i % D
     const int step = wave + i * NW;
     const uint32_t s = ring + (uint32_t)((i % D) * SLOT);
     const int co = step * 128, so = step * 16;
 #pragma unroll
     for (int b = 0; b < 2 * R; ++b) dma_b128(wcr, s + 1024 * b, vcode[b], co);
-    dma_b128(acr, s + 2048 * R, vcode[0], co);
+    if constexpr (!SA) {
+      dma_b128(acr, s + 2048 * R, vcode[0], co);
 #pragma unroll
-    for (int r = 0; r < R; ++r) dma_b32(wsr, s + 2048 * R + 1024 + 256 * r, vscale[r], so);
-    dma_b32(asr, s + 2048 * R + 1024 + 256 * R, vscale[0], so);
+      for (int r = 0; r < R; ++r) dma_b32(wsr, s + 2048 * R + 1024 + 256 * r, vscale[r], so);
+      dma_b32(asr, s + 2048 * R + 1024 + 256 * R, vscale[0], so);
+    }
   };
 
   const int btok = li < M ? li : M - 1;
-  const char* lbase = reinterpret_cast<const char*>(lds4) + wave * D * SLOT;
+  const char* lstage = reinterpret_cast<const char*>(lds4);
+  const char* lbase = lstage + staged + wave * D * SLOT;
   // operand read offsets within a slot
   int wro[R][2];
 #pragma unroll
@@ -1159,6 +1186,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
 #pragma unroll
   for (int j = 0; j < D - 1; ++j)
     if (j < n) issue(j);
+  if constexpr (SA) {
+    // this wave's staging copies (issued before the ring's first steps) have
+    // landed, and after the barrier every other wave's
+    if (n >= D - 1) wait_vmcnt<(D - 1) * L>();
+    else wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+  }
+  // staged operand offsets (SA), without the step term: token btok's codes
+  // and scale word, and this lane's weight row's scale word in tile 0
+  const char* sa_codes = lstage + btok * (K / 2) + 32 * kg;
+  const char* sa_scale = lstage + acb + btok * (K / 16) + 4 * kg;
+  const char* sw_scale = lstage + acb + asb + li * (K / 16) + 4 * kg;
   for (int i = 0; i < n; ++i) {
     if (i + D - 1 < n) {
       // into the slot of step i - 1: its operand reads must have returned
@@ -1172,17 +1211,22 @@ __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
     else if (D > 2 && later == 1) wait_vmcnt<(D > 2 ? L : 0)>();
     else wait_vmcnt<0>();
     const char* sl = lbase + (i % D) * SLOT;
+    const int step = wave + i * NW;
     uint4 w[R][2];
     uint32_t sw[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       w[r][0] = *reinterpret_cast<const uint4*>(sl + wro[r][0]);
       w[r][1] = *reinterpret_cast<const uint4*>(sl + wro[r][1]);
-      sw[r] = *reinterpret_cast<const uint32_t*>(sl + sro + 256 * r);
+      sw[r] = SA ? *reinterpret_cast<const uint32_t*>(sw_scale + 16 * r * (K / 16) + step * 16)
+                 : *reinterpret_cast<const uint32_t*>(sl + sro + 256 * r);
     }
-    const uint4 a0 = *reinterpret_cast<const uint4*>(sl + aro0);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(sl + aro1);
-    const uint32_t sa = *reinterpret_cast<const uint32_t*>(sl + asro);
+    const uint4 a0 = SA ? *reinterpret_cast<const uint4*>(sa_codes + step * 128)
+                        : *reinterpret_cast<const uint4*>(sl + aro0);
+    const uint4 a1 = SA ? *reinterpret_cast<const uint4*>(sa_codes + step * 128 + 16)
+                        : *reinterpret_cast<const uint4*>(sl + aro1);
+    const uint32_t sa = SA ? *reinterpret_cast<const uint32_t*>(sa_scale + step * 16)
+                           : *reinterpret_cast<const uint32_t*>(sl + asro);
     mfma_step<R>(w, sw, a0, a1, sa, acc);
   }
   __syncthreads();  // every wave is done with its ring before the reduction reuses the LDS
@@ -1204,17 +1248,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
 // counts exactly the loads of steps i+1 .. i+P-1).  Each LDS region is
 // padded to a whole number of 1 KB copies.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;  // beyond any buffer resource's num_records
-
-__host__ __device__ constexpr int64_t pad1k(int64_t b) { return (b + 1023) / 1024 * 1024; }
-
-// Copy `bytes` (a multiple of 16) from rsrc into LDS at `lds`: 1 KB per wave
-// instruction, chunks spread over the NW waves.  The whole source offset is
-// in the per-lane operand, so lanes past `bytes` are out of range.
-template <int NW>
-__device__ __forceinline__ void stage_to_lds(const i32x4_t& rsrc, uint32_t lds, int64_t bytes, int wave, int lane) {
-  const int chunks = (int)((bytes + 1023) / 1024);
-  for (int ch = wave; ch < chunks; ch += NW) dma_b128(rsrc, lds + 1024 * ch, 1024 * ch + 16 * lane, 0);
-}
 
 template <int MT, int G, int R, int NW, int P, bool EPI>
 __global__ __launch_bounds__(NW * 64) void gemv_staged_kernel(GemvParams p) {
@@ -1653,7 +1686,7 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7 };
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8 };
 
 struct Variant {
   const char* name;
@@ -1707,10 +1740,15 @@ struct Variant {
     "fmma_m" #MT "_r" #R "_w" #NW "_d" #D "_sa", FMMASA, MT, 16, R, NW, D,                       \
         gemv_fmma_kernel<MT, R, NW, D, true, false>, gemv_fmma_kernel<MT, R, NW, D, true, true> \
   }
-#define DMA_V(MT, R, NW, D)                                                          \
-  Variant {                                                                        \
-    "dma_m" #MT "_r" #R "_w" #NW "_d" #D, DMA, MT, 16, R, NW, D,                   \
-        gemv_dma_kernel<MT, R, NW, D, false>, gemv_dma_kernel<MT, R, NW, D, true> \
+#define DMA_V(MT, R, NW, D)                                                                        \
+  Variant {                                                                                      \
+    "dma_m" #MT "_r" #R "_w" #NW "_d" #D, DMA, MT, 16, R, NW, D,                                 \
+        gemv_dma_kernel<MT, R, NW, D, false, false>, gemv_dma_kernel<MT, R, NW, D, false, true> \
+  }
+#define DMA_SA_V(MT, R, NW, D)                                                                   \
+  Variant {                                                                                    \
+    "dma_m" #MT "_r" #R "_w" #NW "_d" #D "_sa", DMASA, MT, 16, R, NW, D,                       \
+        gemv_dma_kernel<MT, R, NW, D, true, false>, gemv_dma_kernel<MT, R, NW, D, true, true> \
   }
 
 const Variant kVariants[] = {
@@ -1729,6 +1767,9 @@ const Variant kVariants[] = {
     // direct-to-LDS MFMA (K % 256 == 0)
     DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
     DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
+    // direct-to-LDS MFMA, activation and the tile's weight scales staged once (K % 256 == 0)
+    DMA_SA_V(4, 2, 4, 3), DMA_SA_V(4, 2, 4, 2), DMA_SA_V(4, 1, 4, 3), DMA_SA_V(8, 2, 4, 3), DMA_SA_V(8, 2, 4, 2),
+    DMA_SA_V(8, 1, 4, 3), DMA_SA_V(8, 1, 4, 4), DMA_SA_V(8, 1, 8, 2), DMA_SA_V(8, 2, 8, 2), DMA_SA_V(8, 1, 4, 2),
     // LDS-staged VALU (K % 256 == 0)
     STAGED_V(1, 32, 1, 4, 1), STAGED_V(1, 32, 2, 4, 1), STAGED_V(1, 64, 1, 4, 1), STAGED_V(1, 32, 1, 4, 2),
     STAGED_V(1, 32, 2, 4, 2), STAGED_V(1, 64, 1, 4, 2), STAGED_V(1, 64, 2, 4, 1), STAGED_V(1, 32, 4, 4, 1),
@@ -1752,10 +1793,10 @@ int find_variant(const char* name) {
   return -1;
 }
 
-// LDS of the FP4 MFMA kernel with staged activation: activation codes and
-// scales for MT tokens, the tile's weight scales, then a ring of D weight-code
-// slots per wave
-int64_t fmma_sa_lds_bytes(const Variant& v, int64_t K) {
+// LDS of the direct-to-LDS kernels with staged activation (f16 and FP4
+// MFMA): activation codes and scales for MT tokens, the tile's weight scales,
+// then a ring of D weight-code slots per wave
+int64_t sa_lds_bytes(const Variant& v, int64_t K) {
   return pad1k(v.mt * (K / 2)) + pad1k(v.mt * (K / 16)) + pad1k(16 * v.r * (K / 16)) + (int64_t)v.nw * v.p * 2048 * v.r;
 }
 
@@ -1775,7 +1816,7 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
-  auto fmma_sa = [&](int i, int otherwise) { return fmma_sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
+  auto fmma_sa = [&](int i, int otherwise) { return sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
   if (M <= 1) {
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
@@ -1785,7 +1826,12 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
     return K >= 12288 ? fmma_sa(VARIANT("fmma_m2_r2_w4_d3_sa"), VARIANT("staged_m2_g64_r1_w4_p2"))
            : K >= 8192 && N < 16384 ? VARIANT("staged_m2_g64_r1_w4_p1")
                                     : VARIANT("staged_m2_g32_r2_w4_p1");
-  if (k256 && N >= 16384) return M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
+  // M = 5..8: the staged-activation form when two workgroups still fit a
+  // CU's LDS (with one per CU it is slower than the plain ring)
+  if (k256 && N >= 16384)
+    return M <= 4 ? VARIANT("dma_m4_r2_w4_d3")
+           : sa_lds_bytes(kVariants[VARIANT("dma_m8_r2_w4_d2_sa")], K) <= 81920 ? VARIANT("dma_m8_r2_w4_d2_sa")
+                                                                                 : VARIANT("dma_m8_r2_w4_d3");
   if (M <= 4 && k256 && K >= 12288) return fmma_sa(VARIANT("fmma_m4_r2_w4_d3_sa"), VARIANT("lmfma_m4_r2_w8_p1"));
   if (K >= 8192) return VARIANT("lmfma_m8_r2_w8_p1");
   return VARIANT("lmfma_m8_r1_w4_p1");
@@ -1823,10 +1869,11 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // 32-bit buffer offsets
   auto fits = [&](int i) {
     const Kind kd = kVariants[i].kind;
-    if ((kd == DMA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
-    if (kd == FMMASA && fmma_sa_lds_bytes(kVariants[i], K) > 163840) return false;
+    if ((kd == DMA || kd == DMASA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
+    if ((kd == FMMASA || kd == DMASA) && sa_lds_bytes(kVariants[i], K) > 163840) return false;
     if (kVariants[i].kind == STAGED && staged_lds_bytes(kVariants[i], K) > 65536) return false;
-    return (kd != LMFMA && kd != DMA && kd != FMMA && kd != FMMASA) || (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
+    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA) ||
+           (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
   };
   // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
   // compiled token count covers M
@@ -1848,7 +1895,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
-  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == FMMA || v.kind == FMMASA) {
+  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA) {
     c.kp = (int)K;
     c.rows_per_wg = (int64_t)16 * v.r;
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
@@ -1857,8 +1904,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
       const int64_t slots = (int64_t)v.nw * (16 * v.r + 8) * (144 + 20);
       if (slots > c.lds_bytes) c.lds_bytes = slots;
     }
-    if (v.kind == FMMASA) {
-      const int64_t b = fmma_sa_lds_bytes(v, K);
+    if (v.kind == FMMASA || v.kind == DMASA) {
+      const int64_t b = sa_lds_bytes(v, K);
       if (b > c.lds_bytes) c.lds_bytes = b;
     }
     if (v.kind == DMA || v.kind == FMMA) {
