@@ -90,6 +90,10 @@ struct GemvParams {
   EpilogueArgs epi;
   float* partials;         // epilogue: [row tiles][MT][4] = {max, S, T, -}
   size_t state_bytes;      // bytes per ReSET state
+  // weight rows per workgroup of the MFMA kernels (<= 16 R): workgroup b
+  // owns rows [b * tile_rows, (b + 1) * tile_rows); rows of its 16 R-row
+  // tile past that range read as zeros and are never stored
+  int tile_rows;
 };
 
 // ReSET per-sequence state (device).  Followed by float ring[window].
@@ -748,6 +752,7 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
     for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
   __syncthreads();
   const float scale = (*p.a_gscale) * (*p.w_gscale);
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;  // rows this workgroup owns
   // wave w finalizes the (r, v) register slots w, w + NW, ...; D layout:
   // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token li
   constexpr int NV = (R * 4 + NW - 1) / NW;
@@ -769,7 +774,7 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
       out[u] = sum * scale;
       rowt[u] = 16 * r + 4 * kg + v;
       own[u] = li < M;
-      ok[u] = li < M && row < N;
+      ok[u] = li < M && rowt[u] < rows;
       if (ok[u]) p.y[(int64_t)li * N + row] = out[u];
     }
   }
@@ -908,17 +913,17 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
   const int sq = lane >> 2, sp = lane & 3;   // scale loads: row, 4-byte part
   const int64_t N = p.N, K = p.K;
   const int M = p.M;
-  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
   const int nsteps = (int)((K + 255) / 256);
   const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
   (void)MT;
 
-  // Buffer resources over this tile's weight rows and over the activation:
-  // rows past N or M lie outside num_records and load as zeros, so no load
-  // is predicated.  Code chunks past K (last step only) load bytes of the
+  // Buffer resources over this workgroup's weight rows and over the
+  // activation: rows past them (or past M) lie outside num_records and load
+  // as zeros, so no load is predicated.  Code chunks past K (last step only) load bytes of the
   // next row; their block scales are masked to zero below, which makes the
   // decoded values zero (E2M1 codes are always finite).
-  const int64_t rows = N - tile0 < 16 * R ? N - tile0 : 16 * R;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
   const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
   const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
@@ -1116,12 +1121,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_dma_kernel(GemvParams p) {
   const int li = lane & 15, kg = lane >> 4;  // operand layout
   const int64_t N = p.N, K = p.K;
   const int M = p.M;
-  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
   const int nsteps = (int)(K / 256);
   const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
   (void)MT;
 
-  const int64_t rows = N - tile0 < 16 * R ? N - tile0 : 16 * R;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
   const i32x4_t wcr = raw_rsrc(p.w_codes + tile0 * (K / 2), rows * (K / 2));
   const i32x4_t wsr = raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16));
   const i32x4_t acr = raw_rsrc(p.a_codes, (int64_t)M * (K / 2));
@@ -1483,11 +1488,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
   const int li = lane & 15, kg = lane >> 4;
   const int64_t N = p.N, K = p.K;
   const int M = p.M;
-  const int64_t tile0 = (int64_t)blockIdx.x * (16 * R);
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
   const int nsteps = (int)(K / 256);
   const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
 
-  const int64_t rows = N - tile0 < 16 * R ? N - tile0 : 16 * R;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
   const i32x4_t wcr = raw_rsrc(p.w_codes + tile0 * (K / 2), rows * (K / 2));
   const i32x4_t wsr = raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16));
   const i32x4_t acr = raw_rsrc(p.a_codes, (int64_t)M * (K / 2));
@@ -1660,7 +1665,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
       tok[u] = j;
       rowt[u] = rt;
       own[u] = j < M;
-      ok[u] = j < M && row < N;
+      ok[u] = j < M && rt < rows;
       if (ok[u]) p.y[(int64_t)j * N + row] = out[u];
     }
   }
@@ -1810,8 +1815,10 @@ int64_t sa_lds_bytes(const Variant& v, int64_t K) {
 // the Qwen3-32B projection and LM-head shapes (graph-replayed back-to-back
 // launches, each projection's weights rotated over >= 576 MB of copies so
 // that every launch reads HBM; candidates interleaved, medians compared),
-// generalised by N and K.  The LDS-copy kernels need K % 256 == 0; other K
-// use the register-staged kernels.
+// generalised by N and K, with the MFMA kernels' rows dealt out evenly over
+// the CUs where whole tiles would leave some idle (tile_rows_for).  The
+// LDS-copy kernels need K % 256 == 0; other K use the register-staged
+// kernels.
 int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
   const bool k256 = K % 256 == 0;
@@ -1823,16 +1830,17 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
     return VARIANT("direct_m1_g32_r1_w4_p1_nt");
   }
   if (M <= 2 && k256)
-    return K >= 12288 ? fmma_sa(VARIANT("fmma_m2_r2_w4_d3_sa"), VARIANT("staged_m2_g64_r1_w4_p2"))
+    return K >= 12288 ? fmma_sa(VARIANT("fmma_m2_r1_w4_d3_sa"), VARIANT("staged_m2_g64_r1_w4_p2"))
            : K >= 8192 && N < 16384 ? VARIANT("staged_m2_g64_r1_w4_p1")
                                     : VARIANT("staged_m2_g32_r2_w4_p1");
-  // M = 5..8: the staged-activation form when two workgroups still fit a
-  // CU's LDS (with one per CU it is slower than the plain ring)
+  // N >= 16384: the plain ring at M = 3..4; at M = 5..8 the staged-activation
+  // form when two workgroups still fit a CU's LDS (with one per CU it is
+  // slower than the plain ring)
   if (k256 && N >= 16384)
     return M <= 4 ? VARIANT("dma_m4_r2_w4_d3")
            : sa_lds_bytes(kVariants[VARIANT("dma_m8_r2_w4_d2_sa")], K) <= 81920 ? VARIANT("dma_m8_r2_w4_d2_sa")
                                                                                  : VARIANT("dma_m8_r2_w4_d3");
-  if (M <= 4 && k256 && K >= 12288) return fmma_sa(VARIANT("fmma_m4_r2_w4_d3_sa"), VARIANT("lmfma_m4_r2_w8_p1"));
+  if (M <= 4 && k256 && K >= 12288) return VARIANT("fmma_m4_r2_w4_d3");
   if (K >= 8192) return VARIANT("lmfma_m8_r2_w8_p1");
   return VARIANT("lmfma_m8_r1_w4_p1");
 }
@@ -1848,6 +1856,25 @@ int env_variant(const char* env) {
 }
 
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// Rows per workgroup of the MFMA tile kernels.  A workgroup streams its rows
+// at a rate set by the loads it keeps in flight, so a grid of N / (16 R)
+// workgroups that leaves CUs idle (N = 5120: 160 or 320 tiles on 256 CUs)
+// runs at the speed of the busiest CU.  When the tiles fill the CUs at most
+// twice over, the rows are instead dealt out evenly: ceil(N / (256 k))
+// rows per workgroup for the smallest k that fits a 16 R-row tile, so that
+// every CU streams the same number of rows.  NVFP4_GEMV_BALANCE=0 keeps
+// whole tiles (for timing comparisons).
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+int64_t tile_rows_for(int64_t N, int64_t tile) {
+  const char* env = getenv("NVFP4_GEMV_BALANCE");
+  if (env && env[0] == '0') return tile;
+  const int64_t k = (N + tile * kComputeUnits - 1) / (tile * kComputeUnits);
+  if (k > 2) return tile;
+  const int64_t rows = (N + kComputeUnits * k - 1) / (kComputeUnits * k);
+  return rows < tile ? rows : tile;
+}
 
 // LDS of the staged kernel: activation codes and scales for MT tokens and
 // the block scales of the workgroup's rows, each padded to whole KB
@@ -1897,7 +1924,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   const int64_t budget = epi ? 24576 : 32768;
   if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA) {
     c.kp = (int)K;
-    c.rows_per_wg = (int64_t)16 * v.r;
+    c.rows_per_wg = v.kind == MFMA ? (int64_t)16 * v.r : tile_rows_for(N, (int64_t)16 * v.r);
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = (int64_t)v.nw * v.r * 4 * 64 * 4;  // partial tiles of the final reduction
     if (v.kind == LMFMA) {
@@ -1956,6 +1983,7 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   p.w_scales = w_scales;
   p.w_gscale = w_gscale;
   p.y = y;
+  p.tile_rows = (int)cfg.rows_per_wg;
   char* wsb = reinterpret_cast<char*>(ws);
   if (epi) {
     p.epi = *epi;

@@ -147,3 +147,26 @@ def test_every_kernel_variant(variant, monkeypatch):
             y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
             assert_gemv_close(y, y_ref, ref_abs, what=f"{variant} M={M} N={N} K={K}")
     assert ran >= 2, variant
+
+
+# Row mapping of the MFMA tile kernels: whole 16R-row tiles (forced with
+# NVFP4_GEMV_BALANCE=0) against rows dealt out evenly over the CUs (the
+# default where whole tiles would leave CUs idle; N = 5120 gives 20 or 10
+# rows per workgroup).  N = 4099 leaves a ragged last tile in both mappings;
+# N = 5120 - 3 a ragged last workgroup of the even deal.
+ROW_MAP_CASES = [("lmfma_m8_r2_w8_p1", 8, 4099, 2048), ("lmfma_m8_r1_w4_p1", 5, 5117, 1280),
+                 ("dma_m8_r2_w4_d3", 8, 5117, 1024), ("dma_m8_r2_w4_d2_sa", 7, 4099, 2048),
+                 ("fmma_m4_r2_w4_d3", 4, 5117, 1024), ("fmma_m2_r1_w4_d3_sa", 2, 4099, 1024)]
+
+
+@pytest.mark.parametrize("balance", ["0", "1"])
+@pytest.mark.parametrize("variant,M,N,K", ROW_MAP_CASES)
+def test_row_mapping(variant, M, N, K, balance, monkeypatch):
+    monkeypatch.setenv("NVFP4_GEMV_VARIANT", variant)
+    monkeypatch.setenv("NVFP4_GEMV_BALANCE", balance)
+    assert F.nvfp4_gemv_variant(M, N, K) == variant
+    w = W.small_random_weights(N + 5 * K, N, K)
+    xb = W.small_random_bf16(N + M, M, K)
+    wq, aq, y = _run(M, N, K, w, xb, f"{variant} balance={balance}")
+    y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+    assert_gemv_close(y, y_ref, ref_abs, what=f"{variant} balance={balance} M={M} N={N} K={K}")
