@@ -54,8 +54,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "2fda5f80918e41ef2489ffec2958d237af25a320390720e86c6d54e7bc21277d",
-    "bytes_per_step": 1107150050,
+    "sha256": "8a33e8e189b4d647d733a85fd9bec658a94e27143639836bc8dfb7c25cf2d0fa",
+    "bytes_per_step": 1107293706,
 }
 
 
