@@ -172,8 +172,9 @@ _WS_SIZES: dict = {}
 
 
 def nvfp4_workspace_size(op: int, M: int, N: int, K: int) -> int:
-    # remembered per shape (and per forced kernel variant, which can change it)
-    key = (op, M, N, K, os.environ.get("NVFP4_GEMV_VARIANT"))
+    # remembered per shape (and per forced kernel variant and row mapping,
+    # which can change it)
+    key = (op, M, N, K, os.environ.get("NVFP4_GEMV_VARIANT"), os.environ.get("NVFP4_GEMV_BALANCE"))
     n = _WS_SIZES.get(key)
     if n is None:
         n = _WS_SIZES[key] = int(lib().nvfp4_workspace_size(op, M, N, K))

@@ -215,7 +215,11 @@ int nvfp4_sample_top_p(int M, int64_t N, const float* logits, const float* tempe
 /* Name of compiled kernel variant `index` (0-based), NULL past the end.
  * Setting the environment variable NVFP4_GEMV_VARIANT to one of these
  * names makes nvfp4_gemv_smallm launch that variant for every M it covers
- * (for tuning and testing; read on each call). */
+ * (for tuning and testing; read on each call).  NVFP4_GEMV_BALANCE=0 makes
+ * the MFMA kernels keep whole 16-row tiles per workgroup instead of dealing
+ * the rows of small-N shapes out evenly over the CUs (also read on each
+ * call; it changes the LM-head workspace size, which must then be queried
+ * again). */
 const char* nvfp4_gemv_variant_name(int index);
 
 #ifdef __cplusplus
