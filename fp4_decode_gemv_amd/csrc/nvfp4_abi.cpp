@@ -29,7 +29,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 bool shape_ok_k(int64_t K) { return K >= 32 && K % 32 == 0 && K <= ((int64_t)1 << 24); }
 bool shape_ok(int M, int64_t N, int64_t K) {
-  return M >= 1 && M <= 8 && N >= 1 && N <= ((int64_t)1 << 40) && shape_ok_k(K);
+  return M >= 1 && M <= kMaxTokens && N >= 1 && N <= ((int64_t)1 << 40) && shape_ok_k(K);
 }
 
 // Device check, cached per device ordinal (1 = gfx950, 2 = other).
@@ -82,7 +82,7 @@ size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K) {
       if (N < 1 || !shape_ok_k(K)) return 0;
       return quant_ws_bytes(N * K, true);
     case NVFP4_OP_QUANT:
-      if (M < 1 || M > 8 || !shape_ok_k(K)) return 0;
+      if (M < 1 || M > kMaxTokens || !shape_ok_k(K)) return 0;
       return quant_ws_bytes((int64_t)M * K, (int64_t)M * K > kActSelfAmaxMaxElems);
     case NVFP4_OP_GEMV:
       if (!shape_ok(M, N, K)) return 0;
@@ -128,7 +128,7 @@ int nvfp4_pack_weights(const float* w, int64_t N, int64_t K, uint8_t* codes, uin
 
 int nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, uint8_t* codes, uint8_t* scales,
                        float* gscale, int flags, void* ws, size_t ws_bytes, void* stream) {
-  if (M < 1 || M > 8 || !shape_ok_k(K)) return NVFP4_ERR_SHAPE;
+  if (M < 1 || M > kMaxTokens || !shape_ok_k(K)) return NVFP4_ERR_SHAPE;
   if (!x_bf16 || !codes || !scales || !gscale) return NVFP4_ERR_NULL;
   if (flags != NVFP4_GS_DYNAMIC && flags != NVFP4_GS_STATIC) return NVFP4_ERR_ARG;
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
@@ -158,7 +158,7 @@ size_t nvfp4_reset_state_size(int window) {
 }
 
 int nvfp4_reset_state_init(void* state, int M, int window, void* stream) {
-  if (M < 1 || M > 8) return NVFP4_ERR_SHAPE;
+  if (M < 1 || M > kMaxTokens) return NVFP4_ERR_SHAPE;
   if (window < 1 || window > kResetMaxWindow) return NVFP4_ERR_ARG;
   if (!state) return NVFP4_ERR_NULL;
   if (!aligned16(state)) return NVFP4_ERR_ALIGN;

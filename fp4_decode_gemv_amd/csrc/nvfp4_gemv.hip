@@ -49,6 +49,12 @@
 //
 // Every kernel multiplies by the two global scales once at the end.
 //
+// The register-staged MFMA kernel (gemv_lmfma_kernel) also has 16-token
+// instantiations, for M = 9..16, where every token column of the MFMA tile
+// is in use; they stage two activation row groups per step.  The MFMA tile
+// kernels deal the rows of small-N shapes out evenly over the CUs
+// (tile_rows_for).
+//
 // Optional LM-head epilogue (ReSET project page, "Step-aware temperature
 // scaling"; reading notes sections 3.1, 4.1-4.3): each workgroup also
 // writes per-token softmax partials (max, sum e^(z-max), sum e^(z-max)(z-max))
@@ -884,15 +890,21 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(GemvParams p) {
 constexpr int kLdsCodeRow = 144;  // LDS bytes per 128-byte row of codes
 constexpr int kLdsScaleRow = 20;  // LDS bytes per 16-byte row of scales
 
-template <int R>
+// activation rows in a slot: 8 for up to 8 tokens, 16 for up to 16
+template <int MT>
+constexpr int lmfma_act_rows() {
+  return MT > 8 ? 16 : 8;
+}
+
+template <int R, int MT>
 constexpr int lmfma_slot_bytes() {
-  return (16 * R + 8) * (kLdsCodeRow + kLdsScaleRow);
+  return (16 * R + lmfma_act_rows<MT>()) * (kLdsCodeRow + kLdsScaleRow);
 }
 
 template <int R>
 struct LmfmaStep {
   uint4 w[R][2];    // weight codes: rows 8h + lane/8 of tile r, 16 bytes at 16*(lane%8)
-  uint4 a;          // activation codes: row lane/8, 16 bytes at 16*(lane%8)
+  uint4 a[2];       // activation codes: rows lane/8 and 8 + lane/8 (16 tokens only), 16 bytes at 16*(lane%8)
   uint32_t ws[R];   // weight scales: row lane/4 of tile r, bytes 4*(lane%4) .. +3 (or +1)
   uint32_t wsh[R];  // bytes 4*(lane%4) + 2, +3 when the word is loaded in halves
   uint32_t as, ash; // activation scales: row lane/4, the same bytes
@@ -916,7 +928,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
   const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
   const int nsteps = (int)((K + 255) / 256);
   const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
-  (void)MT;
+  constexpr int AR = lmfma_act_rows<MT>();  // activation rows staged per step
 
   // Buffer resources over this workgroup's weight rows and over the
   // activation: rows past them (or past M) lie outside num_records and load
@@ -943,7 +955,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
       for (int h = 0; h < 2; ++h)
         st.w[r][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(
             wcr, code_off + (16 * r + 8 * h) * (int)(K / 2) + cstep, 0, 0));
-    st.a = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + cstep, 0, 0));
+    st.a[0] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + cstep, 0, 0));
+    if constexpr (AR > 8)
+      st.a[1] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + 8 * (int)(K / 2) + cstep, 0, 0));
     // four block scales (64 elements).  With K % 64 == 0 (K64) every 4-byte
     // word is aligned and wholly inside its row; otherwise rows are 2-byte
     // aligned and the last word of a row is half outside, so the word is
@@ -974,8 +988,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
     return es + 32 < K ? w : es < K ? (w & 0xFFFFu) : 0u;
   };
 
-  char* slot = reinterpret_cast<char*>(lds4) + wave * lmfma_slot_bytes<R>();
-  char* scl = slot + (16 * R + 8) * kLdsCodeRow;
+  char* slot = reinterpret_cast<char*>(lds4) + wave * lmfma_slot_bytes<R, MT>();
+  char* scl = slot + (16 * R + AR) * kLdsCodeRow;
   // operand-layout read addresses (activation columns >= M read row M - 1; ignored)
   const int btok = li < M ? li : M - 1;
 
@@ -1014,8 +1028,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
           *reinterpret_cast<uint32_t*>(scl + (16 * r + sq) * kLdsScaleRow + 4 * sp) =
               scale_word(buf[j].ws[r], buf[j].wsh[r], si);
         }
-        *reinterpret_cast<uint4*>(slot + (16 * R + lq) * kLdsCodeRow + 16 * lc) = buf[j].a;
-        if (sq < 8)
+        *reinterpret_cast<uint4*>(slot + (16 * R + lq) * kLdsCodeRow + 16 * lc) = buf[j].a[0];
+        if constexpr (AR > 8)
+          *reinterpret_cast<uint4*>(slot + (16 * R + 8 + lq) * kLdsCodeRow + 16 * lc) = buf[j].a[1];
+        if (sq < AR)
           *reinterpret_cast<uint32_t*>(scl + (16 * R + sq) * kLdsScaleRow + 4 * sp) =
               scale_word(buf[j].as, buf[j].ash, si);
         wave_lds_fence();
@@ -1769,6 +1785,8 @@ const Variant kVariants[] = {
     // LDS-staged MFMA
     LMFMA_V(2, 2, 4, 1), LMFMA_V(4, 2, 4, 1), LMFMA_V(4, 2, 8, 1), LMFMA_V(8, 1, 4, 1), LMFMA_V(8, 1, 8, 1),
     LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 2),
+    // ... for 9..16 tokens (every column of the 16-token MFMA tile in use)
+    LMFMA_V(16, 1, 4, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(16, 1, 8, 1), LMFMA_V(16, 2, 8, 1),
     // direct-to-LDS MFMA (K % 256 == 0)
     DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
     DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
@@ -1790,7 +1808,7 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 
 int find_variant(const char* name) {
   for (int i = 0; i < kNumVariants; ++i)
@@ -1824,6 +1842,8 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
   auto fmma_sa = [&](int i, int otherwise) { return sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
+  // 9..16 tokens: the register-staged MFMA kernel with all 16 token columns
+  if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
   if (M <= 1) {
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
@@ -1910,8 +1930,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   }
   if (vi < 0) vi = default_variant(M, N, K, epi);
   if (!fits(vi))
-    vi = mt_of(M) <= 2 ? VARIANT("direct_m2_g64_r1_w4_p1") : mt_of(M) <= 4 ? VARIANT("mfma_m4_r2_w8_p1")
-                                                                           : VARIANT("mfma_m8_r2_w8_p1");
+    vi = mt_of(M) <= 2   ? VARIANT("direct_m2_g64_r1_w4_p1")
+         : mt_of(M) <= 4 ? VARIANT("mfma_m4_r2_w8_p1")
+         : mt_of(M) <= 8 ? VARIANT("mfma_m8_r2_w8_p1")
+                         : VARIANT("lmfma_m16_r1_w4_p1");
   const Variant& v = kVariants[vi];
   GemvConfig c{};
   c.variant = vi;
@@ -1928,7 +1950,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = (int64_t)v.nw * v.r * 4 * 64 * 4;  // partial tiles of the final reduction
     if (v.kind == LMFMA) {
-      const int64_t slots = (int64_t)v.nw * (16 * v.r + 8) * (144 + 20);
+      const int64_t slots = (int64_t)v.nw * (16 * v.r + (v.mt > 8 ? 16 : 8)) * (144 + 20);
       if (slots > c.lds_bytes) c.lds_bytes = slots;
     }
     if (v.kind == FMMASA || v.kind == DMASA) {

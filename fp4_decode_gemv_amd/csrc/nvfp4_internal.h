@@ -36,6 +36,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 // -------------------------------------------------------------------- gemv --
 
+// Tokens (M) a GEMV, an activation quantization and a ReSET state set serve
+// per call: 1..kMaxTokens.
+constexpr int kMaxTokens = 16;
+
 struct EpilogueArgs {
   float tau0, t_low, t_high, t_base;
   int window, mode;

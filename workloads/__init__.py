@@ -250,9 +250,10 @@ def lm_head_positions_bf16(seed: int, positions: int, M: int, K: int) -> np.ndar
 
 
 def step_flags(seed: int, positions: int, seqs: int = 8, p: float = 0.02) -> np.ndarray:
-    """uint8 [positions][seqs]: 1 where a new reasoning step starts."""
+    """uint8 [positions][seqs]: 1 where a new reasoning step starts (drawn
+    for max(8, seqs) sequences, so the first 8 never depend on seqs)."""
     rng = np.random.default_rng(seed)
-    f = (rng.random((positions, 8)) < p).astype(np.uint8)[:, :seqs]
+    f = (rng.random((positions, max(8, seqs))) < p).astype(np.uint8)[:, :seqs]
     f[0, :] = 1
     return f
 
@@ -261,7 +262,7 @@ def sampler_uniforms(seed: int, positions: int, seqs: int = 8) -> np.ndarray:
     """float32 [positions][seqs] in [0, 1): the caller's random numbers for
     the top-p draws (the sampler itself draws none)."""
     rng = np.random.default_rng(seed)
-    return rng.random((positions, 8), dtype=np.float32)[:, :seqs].copy()
+    return rng.random((positions, max(8, seqs)), dtype=np.float32)[:, :seqs].copy()
 
 
 def pow2_exponents(seed: int, positions: int, hi: int = 6) -> np.ndarray:
