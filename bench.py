@@ -57,8 +57,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "8a33e8e189b4d647d733a85fd9bec658a94e27143639836bc8dfb7c25cf2d0fa",
-    "bytes_per_step": 1107293706,
+    "sha256": "66d841e06341855febd4b7e0a64b532c98533cff82f2466d42bab3e2f3b003d0",
+    "bytes_per_step": 1107265424,
 }
 
 
