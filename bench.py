@@ -23,8 +23,8 @@ Prints one JSON line:
                its replay on the launch stream), against the 8 TB/s HBM peak
   cpu_baseline the CPU oracle (quantize + dequantize + fp64 GEMV) on a
                bounded row sample of the same projections, same byte formula
-  extra        the four projections at M = 16 (beyond the metric's M range;
-               per-kernel times only), the LM head (N=151936) with the
+  extra        the four projections at M = 16 and 32 (beyond the metric's M
+               range; per-kernel times only), the LM head (N=151936) with the
                entropy / ReSET epilogue and the top-p = 0.95 draw at the
                epilogue's temperatures, and the 64-layer decode chain
                captured in one graph
@@ -48,7 +48,7 @@ if ROOT not in sys.path:
 METRIC = "µs and effective HBM GB/s per NVFP4 GEMV at M=1/2/4/8; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
 M_LIST = (1, 2, 4, 8)
-M_WIDE = 16  # beyond the metric's M = 1..8: reported under extra.m16 only
+M_WIDE = (16, 32)  # beyond the metric's M = 1..8: reported under extra.wide only
 CPU_ROWS = 2048
 
 # Measured HBM traffic of the 16 GEMV launches of one step: rocprofv3
@@ -98,7 +98,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle baseline")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head + ReSET epilogue figures")
     ap.add_argument("--no-chain", action="store_true", help="skip the 64-layer hipGraph chain figures")
-    ap.add_argument("--no-wide", action="store_true", help="skip the M = 16 projection figures (extra.m16)")
+    ap.add_argument("--no-wide", action="store_true", help="skip the M = 16 and 32 projection figures (extra.wide)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="at the end, fill and copy a buffer of this many MiB three times: a plain copy of "
                          "known size to calibrate hardware byte counters against")
@@ -138,7 +138,7 @@ def setup(args):
         log(args, f"[setup] packed {c.name} {c.N}x{c.K} x{len(copies)} in {time.perf_counter() - t0:.1f}s")
     acts = {}
     for c in cases:
-        for M in M_LIST + ((M_WIDE,) if not args.no_wide else ()):
+        for M in M_LIST + (M_WIDE if not args.no_wide else ()):
             acts[(c.name, M)] = make_activation(c, M, dev)
     torch.cuda.synchronize()
     return cases, wq, acts, samples
@@ -277,19 +277,20 @@ def main():
 
     extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4)}
     if not args.no_wide:
-        # 16 tokens, every token column of the MFMA tile in use: the same
-        # per-kernel timing, outside the step and the roofline figures
+        # 16 and 32 tokens (one or two full 16-token MFMA column tiles): the
+        # same per-kernel timing, outside the step and the roofline figures
         wide = []
-        for c in cases:
-            gus = b2b(lambda i: gemv(c, M_WIDE, i))
-            qus = b2b(lambda i: quant(c, M_WIDE))
-            wb = weight_bytes(c.N, c.K)
-            wide.append({"proj": c.name, "M": M_WIDE, "N": c.N, "K": c.K,
-                         "variant": F.nvfp4_gemv_variant(M_WIDE, c.N, c.K), "gemv_us": round(gus, 3),
-                         "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1), "quant_us": round(qus, 3)})
-            log(args, f"[kern] {c.name:18s} M={M_WIDE} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s  "
-                      f"quant {qus:6.2f} us")
-        extra["m16"] = wide
+        for Mw in M_WIDE:
+            for c in cases:
+                gus = b2b(lambda i: gemv(c, Mw, i))
+                qus = b2b(lambda i: quant(c, Mw))
+                wb = weight_bytes(c.N, c.K)
+                wide.append({"proj": c.name, "M": Mw, "N": c.N, "K": c.K,
+                             "variant": F.nvfp4_gemv_variant(Mw, c.N, c.K), "gemv_us": round(gus, 3),
+                             "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1), "quant_us": round(qus, 3)})
+                log(args, f"[kern] {c.name:18s} M={Mw} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s  "
+                          f"quant {qus:6.2f} us")
+        extra["wide"] = wide
     if not args.no_lmhead:
         extra["lm_head"] = bench_lm_head(args, stream)
     if not args.no_chain:

@@ -51,9 +51,11 @@
 //
 // The register-staged MFMA kernel (gemv_lmfma_kernel) also has 16-token
 // instantiations, for M = 9..16, where every token column of the MFMA tile
-// is in use; they stage two activation row groups per step.  The MFMA tile
-// kernels deal the rows of small-N shapes out evenly over the CUs
-// (tile_rows_for).
+// is in use (two activation row groups staged per step), and 32-token ones,
+// for M = 17..32, with two 16-token column tiles: each decoded weight
+// operand feeds one MFMA per column tile, so the weight bytes and their
+// decode are shared by all 32 tokens.  The MFMA tile kernels deal the rows
+// of small-N shapes out evenly over the CUs (tile_rows_for).
 //
 // Optional LM-head epilogue (ReSET project page, "Step-aware temperature
 // scaling"; reading notes sections 3.1, 4.1-4.3): each workgroup also
@@ -744,8 +746,10 @@ __device__ __forceinline__ void mfma_step(const uint4 (&w)[R][2], const uint32_t
 // Add the NW waves' partial tiles in a fixed order (through LDS; every wave
 // must have left its main loop), scale by the global scales, store y and run
 // the optional epilogue.
-template <int MT, int R, int NW, bool EPI>
-__device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t (&acc)[R], float* red,
+// CT column tiles of 16 tokens each: acc[r * CT + ct] holds row tile r,
+// tokens 16 ct .. 16 ct + 15.
+template <int MT, int R, int NW, bool EPI, int CT = 1>
+__device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t (&acc)[R * CT], float* red,
                                             int64_t tile0) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -753,15 +757,15 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
   const int64_t N = p.N;
   const int M = p.M;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int rc = 0; rc < R * CT; ++rc)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
+    for (int v = 0; v < 4; ++v) red[((wave * R * CT + rc) * 4 + v) * 64 + lane] = acc[rc][v];
   __syncthreads();
   const float scale = (*p.a_gscale) * (*p.w_gscale);
   const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;  // rows this workgroup owns
-  // wave w finalizes the (r, v) register slots w, w + NW, ...; D layout:
-  // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token li
-  constexpr int NV = (R * 4 + NW - 1) / NW;
+  // wave w finalizes the (r, ct, v) register slots w, w + NW, ...; D layout:
+  // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token 16 ct + li
+  constexpr int NV = (R * CT * 4 + NW - 1) / NW;
   float out[NV];
   int tok[NV], rowt[NV];
   bool ok[NV], own[NV];
@@ -772,16 +776,18 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
     tok[u] = li < MT ? li : 0;
     rowt[u] = 0;
     ok[u] = own[u] = false;
-    if (rv < R * 4) {
-      const int r = rv >> 2, v = rv & 3;
+    if (rv < R * CT * 4) {
+      const int rc = rv >> 2, v = rv & 3;
+      const int r = rc / CT, t = 16 * (rc % CT) + li;  // row tile, token
       float sum = 0.0f;
-      for (int w = 0; w < NW; ++w) sum += red[((w * R + r) * 4 + v) * 64 + lane];
+      for (int w = 0; w < NW; ++w) sum += red[((w * R * CT + rc) * 4 + v) * 64 + lane];
       const int64_t row = tile0 + 16 * r + 4 * kg + v;
       out[u] = sum * scale;
+      tok[u] = t < MT ? t : 0;
       rowt[u] = 16 * r + 4 * kg + v;
-      own[u] = li < M;
-      ok[u] = li < M && rowt[u] < rows;
-      if (ok[u]) p.y[(int64_t)li * N + row] = out[u];
+      own[u] = t < M;
+      ok[u] = t < M && rowt[u] < rows;
+      if (ok[u]) p.y[(int64_t)t * N + row] = out[u];
     }
   }
   if constexpr (EPI) lmhead_partials<MT, 16 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
@@ -890,10 +896,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_mfma_kernel(GemvParams p) {
 constexpr int kLdsCodeRow = 144;  // LDS bytes per 128-byte row of codes
 constexpr int kLdsScaleRow = 20;  // LDS bytes per 16-byte row of scales
 
-// activation rows in a slot: 8 for up to 8 tokens, 16 for up to 16
+// activation rows in a slot: 8 for up to 8 tokens, else the token count
+// (16 or 32)
 template <int MT>
 constexpr int lmfma_act_rows() {
-  return MT > 8 ? 16 : 8;
+  return MT > 8 ? MT : 8;
 }
 
 template <int R, int MT>
@@ -904,11 +911,52 @@ constexpr int lmfma_slot_bytes() {
 template <int R>
 struct LmfmaStep {
   uint4 w[R][2];    // weight codes: rows 8h + lane/8 of tile r, 16 bytes at 16*(lane%8)
-  uint4 a[2];       // activation codes: rows lane/8 and 8 + lane/8 (16 tokens only), 16 bytes at 16*(lane%8)
+  uint4 a[4];       // activation codes: rows 8 g + lane/8 (g < activation rows / 8), 16 bytes at 16*(lane%8)
   uint32_t ws[R];   // weight scales: row lane/4 of tile r, bytes 4*(lane%4) .. +3 (or +1)
   uint32_t wsh[R];  // bytes 4*(lane%4) + 2, +3 when the word is loaded in halves
-  uint32_t as, ash; // activation scales: row lane/4, the same bytes
+  uint32_t as[2], ash[2];  // activation scales: rows 16 s + lane/4, the same bytes
 };
+
+// One 256-element step for CT column tiles of 16 tokens: as mfma_step, but
+// each decoded weight operand feeds the CT tiles' MFMAs.  a0/a1/sa[ct] hold
+// the lane's token 16 ct + li; acc[r * CT + ct].
+template <int R, int CT>
+__device__ __forceinline__ void mfma_step_ct(const uint4 (&w)[R][2], const uint32_t (&s)[R], const uint4 (&a0)[CT],
+                                             const uint4 (&a1)[CT], const uint32_t (&sa)[CT], float4_t (&acc)[R * CT]) {
+  half2_t ha[CT][4];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const float2_t sa01 = __builtin_amdgcn_cvt_pk_f32_fp8(sa[ct], false);
+    const float2_t sa23 = __builtin_amdgcn_cvt_pk_f32_fp8(sa[ct], true);
+    ha[ct][0] = as_half2(pack_f16x2(sa01[0], sa01[0]));
+    ha[ct][1] = as_half2(pack_f16x2(sa01[1], sa01[1]));
+    ha[ct][2] = as_half2(pack_f16x2(sa23[0], sa23[0]));
+    ha[ct][3] = as_half2(pack_f16x2(sa23[1], sa23[1]));
+  }
+  half2_t hw[R][4];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float2_t sw01 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], false);
+    const float2_t sw23 = __builtin_amdgcn_cvt_pk_f32_fp8(s[r], true);
+    hw[r][0] = as_half2(pack_f16x2(sw01[0], sw01[0]));
+    hw[r][1] = as_half2(pack_f16x2(sw01[1], sw01[1]));
+    hw[r][2] = as_half2(pack_f16x2(sw23[0], sw23[0]));
+    hw[r][3] = as_half2(pack_f16x2(sw23[1], sw23[1]));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    half8_t b[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) b[ct] = wdecode8_scaled(word_of(j < 4 ? a0[ct] : a1[ct], j & 3), ha[ct][j >> 1]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const half8_t a = wdecode8_scaled(word_of(w[r][j >> 2], j & 3), hw[r][j >> 1]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        acc[r * CT + ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[ct], acc[r * CT + ct], 0, 0, 0);
+    }
+  }
+}
 
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -929,6 +977,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
   const int nsteps = (int)((K + 255) / 256);
   const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
   constexpr int AR = lmfma_act_rows<MT>();  // activation rows staged per step
+  constexpr int AG = AR / 8;                 // activation code loads per step (8 rows each)
+  constexpr int SG = AR > 16 ? 2 : 1;        // activation scale loads per step (16 rows each)
+  constexpr int CT = AR > 16 ? AR / 16 : 1;  // 16-token column tiles
 
   // Buffer resources over this workgroup's weight rows and over the
   // activation: rows past them (or past M) lie outside num_records and load
@@ -955,9 +1006,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
       for (int h = 0; h < 2; ++h)
         st.w[r][h] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(
             wcr, code_off + (16 * r + 8 * h) * (int)(K / 2) + cstep, 0, 0));
-    st.a[0] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + cstep, 0, 0));
-    if constexpr (AR > 8)
-      st.a[1] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + 8 * (int)(K / 2) + cstep, 0, 0));
+#pragma unroll
+    for (int g = 0; g < AG; ++g)
+      st.a[g] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(acr, code_off + 8 * g * (int)(K / 2) + cstep, 0, 0));
     // four block scales (64 elements).  With K % 64 == 0 (K64) every 4-byte
     // word is aligned and wholly inside its row; otherwise rows are 2-byte
     // aligned and the last word of a row is half outside, so the word is
@@ -968,7 +1019,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
         st.ws[r] = __builtin_amdgcn_raw_buffer_load_b32(wsr, scale_off + 16 * r * (int)(K / 16) + sstep, 0, 0);
-      st.as = __builtin_amdgcn_raw_buffer_load_b32(asr, scale_off + sstep, 0, 0);
+#pragma unroll
+      for (int g = 0; g < SG; ++g)
+        st.as[g] = __builtin_amdgcn_raw_buffer_load_b32(asr, scale_off + 16 * g * (int)(K / 16) + sstep, 0, 0);
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -976,8 +1029,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
         st.ws[r] = __builtin_amdgcn_raw_buffer_load_b16(wsr, o, 0, 0);
         st.wsh[r] = __builtin_amdgcn_raw_buffer_load_b16(wsr, o + 2, 0, 0);
       }
-      st.as = __builtin_amdgcn_raw_buffer_load_b16(asr, scale_off + sstep, 0, 0);
-      st.ash = __builtin_amdgcn_raw_buffer_load_b16(asr, scale_off + sstep + 2, 0, 0);
+#pragma unroll
+      for (int g = 0; g < SG; ++g) {
+        const int o = scale_off + 16 * g * (int)(K / 16) + sstep;
+        st.as[g] = __builtin_amdgcn_raw_buffer_load_b16(asr, o, 0, 0);
+        st.ash[g] = __builtin_amdgcn_raw_buffer_load_b16(asr, o + 2, 0, 0);
+      }
     }
   };
   // the staged scale word of a lane: its loaded bytes with the blocks past K
@@ -990,12 +1047,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
 
   char* slot = reinterpret_cast<char*>(lds4) + wave * lmfma_slot_bytes<R, MT>();
   char* scl = slot + (16 * R + AR) * kLdsCodeRow;
-  // operand-layout read addresses (activation columns >= M read row M - 1; ignored)
-  const int btok = li < M ? li : M - 1;
-
-  float4_t acc[R];
+  // operand-layout read addresses: token 16 ct + li of each column tile
+  // (tokens >= M read row M - 1; ignored)
+  int btok[CT];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int ct = 0; ct < CT; ++ct) btok[ct] = 16 * ct + li < M ? 16 * ct + li : M - 1;
+
+  float4_t acc[R * CT];
+#pragma unroll
+  for (int rc = 0; rc < R * CT; ++rc) acc[rc] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // P register buffers in a ring: the loads of steps i+1 .. i+P-1 stay in
   // flight while step i is staged and computed; a buffer is refilled right
@@ -1028,12 +1088,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
           *reinterpret_cast<uint32_t*>(scl + (16 * r + sq) * kLdsScaleRow + 4 * sp) =
               scale_word(buf[j].ws[r], buf[j].wsh[r], si);
         }
-        *reinterpret_cast<uint4*>(slot + (16 * R + lq) * kLdsCodeRow + 16 * lc) = buf[j].a[0];
-        if constexpr (AR > 8)
-          *reinterpret_cast<uint4*>(slot + (16 * R + 8 + lq) * kLdsCodeRow + 16 * lc) = buf[j].a[1];
-        if (sq < AR)
-          *reinterpret_cast<uint32_t*>(scl + (16 * R + sq) * kLdsScaleRow + 4 * sp) =
-              scale_word(buf[j].as, buf[j].ash, si);
+#pragma unroll
+        for (int g = 0; g < AG; ++g)
+          *reinterpret_cast<uint4*>(slot + (16 * R + 8 * g + lq) * kLdsCodeRow + 16 * lc) = buf[j].a[g];
+#pragma unroll
+        for (int g = 0; g < SG; ++g)
+          if (16 * g + sq < AR)
+            *reinterpret_cast<uint32_t*>(scl + (16 * R + 16 * g + sq) * kLdsScaleRow + 4 * sp) =
+                scale_word(buf[j].as[g], buf[j].ash[g], si);
         wave_lds_fence();
         __builtin_amdgcn_sched_barrier(0);
         load(buf[j], wave + (i + P < n ? i + P : n - 1) * NW);
@@ -1048,16 +1110,21 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
             w[r][1] = *reinterpret_cast<const uint4*>(slot + (16 * r + li) * kLdsCodeRow + 32 * kg + 16);
             sw[r] = *reinterpret_cast<const uint32_t*>(scl + (16 * r + li) * kLdsScaleRow + 4 * kg);
           }
-          const uint4 a0 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg);
-          const uint4 a1 = *reinterpret_cast<const uint4*>(slot + (16 * R + btok) * kLdsCodeRow + 32 * kg + 16);
-          const uint32_t sa = *reinterpret_cast<const uint32_t*>(scl + (16 * R + btok) * kLdsScaleRow + 4 * kg);
-          mfma_step<R>(w, sw, a0, a1, sa, acc);
+          uint4 a0[CT], a1[CT];
+          uint32_t sa[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            a0[ct] = *reinterpret_cast<const uint4*>(slot + (16 * R + btok[ct]) * kLdsCodeRow + 32 * kg);
+            a1[ct] = *reinterpret_cast<const uint4*>(slot + (16 * R + btok[ct]) * kLdsCodeRow + 32 * kg + 16);
+            sa[ct] = *reinterpret_cast<const uint32_t*>(scl + (16 * R + btok[ct]) * kLdsScaleRow + 4 * kg);
+          }
+          mfma_step_ct<R, CT>(w, sw, a0, a1, sa, acc);
         }
       }
     }
   }
   __syncthreads();  // every wave is done with its slot before the reduction reuses the LDS
-  mfma_finish<MT, R, NW, EPI>(p, acc, reinterpret_cast<float*>(lds4), tile0);
+  mfma_finish<MT, R, NW, EPI, CT>(p, acc, reinterpret_cast<float*>(lds4), tile0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1787,6 +1854,8 @@ const Variant kVariants[] = {
     LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 2),
     // ... for 9..16 tokens (every column of the 16-token MFMA tile in use)
     LMFMA_V(16, 1, 4, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(16, 1, 8, 1), LMFMA_V(16, 2, 8, 1),
+    // ... for 17..32 tokens (two 16-token column tiles per decoded weight operand)
+    LMFMA_V(32, 1, 4, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(32, 1, 8, 1), LMFMA_V(32, 2, 8, 1),
     // direct-to-LDS MFMA (K % 256 == 0)
     DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
     DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
@@ -1808,7 +1877,7 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
 
 int find_variant(const char* name) {
   for (int i = 0; i < kNumVariants; ++i)
@@ -1842,7 +1911,9 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
   auto fmma_sa = [&](int i, int otherwise) { return sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
-  // 9..16 tokens: the register-staged MFMA kernel with all 16 token columns
+  // 17..32 tokens: two 16-token column tiles; 9..16: all 16 token columns
+  // of one tile (the register-staged MFMA kernel)
+  if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
   if (M <= 1) {
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
@@ -1932,8 +2003,9 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   if (!fits(vi))
     vi = mt_of(M) <= 2   ? VARIANT("direct_m2_g64_r1_w4_p1")
          : mt_of(M) <= 4 ? VARIANT("mfma_m4_r2_w8_p1")
-         : mt_of(M) <= 8 ? VARIANT("mfma_m8_r2_w8_p1")
-                         : VARIANT("lmfma_m16_r1_w4_p1");
+         : mt_of(M) <= 8  ? VARIANT("mfma_m8_r2_w8_p1")
+         : mt_of(M) <= 16 ? VARIANT("lmfma_m16_r1_w4_p1")
+                          : VARIANT("lmfma_m32_r1_w4_p1");
   const Variant& v = kVariants[vi];
   GemvConfig c{};
   c.variant = vi;
@@ -1948,9 +2020,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.kp = (int)K;
     c.rows_per_wg = v.kind == MFMA ? (int64_t)16 * v.r : tile_rows_for(N, (int64_t)16 * v.r);
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
-    c.lds_bytes = (int64_t)v.nw * v.r * 4 * 64 * 4;  // partial tiles of the final reduction
+    const int ct = v.mt > 16 ? v.mt / 16 : 1;              // 16-token column tiles
+    c.lds_bytes = (int64_t)v.nw * v.r * ct * 4 * 64 * 4;  // partial tiles of the final reduction
     if (v.kind == LMFMA) {
-      const int64_t slots = (int64_t)v.nw * (16 * v.r + (v.mt > 8 ? 16 : 8)) * (144 + 20);
+      const int64_t slots = (int64_t)v.nw * (16 * v.r + (v.mt > 8 ? v.mt : 8)) * (144 + 20);
       if (slots > c.lds_bytes) c.lds_bytes = slots;
     }
     if (v.kind == FMMASA || v.kind == DMASA) {
