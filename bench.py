@@ -57,8 +57,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "66d841e06341855febd4b7e0a64b532c98533cff82f2466d42bab3e2f3b003d0",
-    "bytes_per_step": 1107265424,
+    "sha256": "fb1ddebf4cb61c231b3bb71b96ea010db65803137ee7ea10a7cf08051fd73d86",
+    "bytes_per_step": 1108220552,
 }
 
 
