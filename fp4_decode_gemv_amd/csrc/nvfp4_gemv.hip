@@ -51,10 +51,10 @@
 //
 // The register-staged MFMA kernel (gemv_lmfma_kernel) also has 16-token
 // instantiations, for M = 9..16, where every token column of the MFMA tile
-// is in use (two activation row groups staged per step), and 32-token ones,
-// for M = 17..32, with two 16-token column tiles: each decoded weight
-// operand feeds one MFMA per column tile, so the weight bytes and their
-// decode are shared by all 32 tokens.  The MFMA tile kernels deal the rows
+// is in use (two activation row groups staged per step), and 32- and
+// 64-token ones, for M = 17..64, with two or four 16-token column tiles:
+// each decoded weight operand feeds one MFMA per column tile, so the weight
+// bytes and their decode are shared by all the tokens.  The MFMA tile kernels deal the rows
 // of small-N shapes out evenly over the CUs (tile_rows_for).
 //
 // Optional LM-head epilogue (ReSET project page, "Step-aware temperature
@@ -897,7 +897,7 @@ constexpr int kLdsCodeRow = 144;  // LDS bytes per 128-byte row of codes
 constexpr int kLdsScaleRow = 20;  // LDS bytes per 16-byte row of scales
 
 // activation rows in a slot: 8 for up to 8 tokens, else the token count
-// (16 or 32)
+// (16, 32 or 64)
 template <int MT>
 constexpr int lmfma_act_rows() {
   return MT > 8 ? MT : 8;
@@ -911,10 +911,10 @@ constexpr int lmfma_slot_bytes() {
 template <int R>
 struct LmfmaStep {
   uint4 w[R][2];    // weight codes: rows 8h + lane/8 of tile r, 16 bytes at 16*(lane%8)
-  uint4 a[4];       // activation codes: rows 8 g + lane/8 (g < activation rows / 8), 16 bytes at 16*(lane%8)
+  uint4 a[8];       // activation codes: rows 8 g + lane/8 (g < activation rows / 8), 16 bytes at 16*(lane%8)
   uint32_t ws[R];   // weight scales: row lane/4 of tile r, bytes 4*(lane%4) .. +3 (or +1)
   uint32_t wsh[R];  // bytes 4*(lane%4) + 2, +3 when the word is loaded in halves
-  uint32_t as[2], ash[2];  // activation scales: rows 16 s + lane/4, the same bytes
+  uint32_t as[4], ash[4];  // activation scales: rows 16 s + lane/4, the same bytes
 };
 
 // One 256-element step for CT column tiles of 16 tokens: as mfma_step, but
@@ -978,7 +978,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_lmfma_kernel(GemvParams p) {
   const int n = wave < nsteps ? (nsteps - wave + NW - 1) / NW : 0;  // steps wave, wave + NW, ...
   constexpr int AR = lmfma_act_rows<MT>();  // activation rows staged per step
   constexpr int AG = AR / 8;                 // activation code loads per step (8 rows each)
-  constexpr int SG = AR > 16 ? 2 : 1;        // activation scale loads per step (16 rows each)
+  constexpr int SG = AR > 16 ? AR / 16 : 1;  // activation scale loads per step (16 rows each)
   constexpr int CT = AR > 16 ? AR / 16 : 1;  // 16-token column tiles
 
   // Buffer resources over this workgroup's weight rows and over the
@@ -1854,8 +1854,10 @@ const Variant kVariants[] = {
     LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 2),
     // ... for 9..16 tokens (every column of the 16-token MFMA tile in use)
     LMFMA_V(16, 1, 4, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(16, 1, 8, 1), LMFMA_V(16, 2, 8, 1),
-    // ... for 17..32 tokens (two 16-token column tiles per decoded weight operand)
+    // ... for 17..32 and 33..64 tokens (two or four 16-token column tiles per
+    // decoded weight operand)
     LMFMA_V(32, 1, 4, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(32, 1, 8, 1), LMFMA_V(32, 2, 8, 1),
+    LMFMA_V(64, 1, 4, 1), LMFMA_V(64, 2, 4, 1), LMFMA_V(64, 1, 8, 1), LMFMA_V(64, 2, 8, 1),
     // direct-to-LDS MFMA (K % 256 == 0)
     DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
     DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
@@ -1877,7 +1879,7 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32; }
+int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64; }
 
 int find_variant(const char* name) {
   for (int i = 0; i < kNumVariants; ++i)
@@ -1911,8 +1913,9 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
   auto fmma_sa = [&](int i, int otherwise) { return sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
-  // 17..32 tokens: two 16-token column tiles; 9..16: all 16 token columns
-  // of one tile (the register-staged MFMA kernel)
+  // 33..64 tokens: four 16-token column tiles; 17..32: two; 9..16: all 16
+  // token columns of one tile (the register-staged MFMA kernel)
+  if (M > 32) return K >= 16384 ? VARIANT("lmfma_m64_r2_w8_p1") : VARIANT("lmfma_m64_r2_w4_p1");
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
   if (M <= 1) {
@@ -2005,7 +2008,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
          : mt_of(M) <= 4 ? VARIANT("mfma_m4_r2_w8_p1")
          : mt_of(M) <= 8  ? VARIANT("mfma_m8_r2_w8_p1")
          : mt_of(M) <= 16 ? VARIANT("lmfma_m16_r1_w4_p1")
-                          : VARIANT("lmfma_m32_r1_w4_p1");
+         : mt_of(M) <= 32 ? VARIANT("lmfma_m32_r1_w4_p1")
+                          : VARIANT("lmfma_m64_r1_w4_p1");
   const Variant& v = kVariants[vi];
   GemvConfig c{};
   c.variant = vi;

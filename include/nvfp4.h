@@ -31,7 +31,7 @@
  *   - Device pointers must be 16-byte aligned (NVFP4_ERR_ALIGN otherwise),
  *     except scalars (global scales, entropy/temperature outputs, flags)
  *     and the sampler's arrays (4 bytes).
- *   - Shapes: 1 <= M <= 32, N >= 1, 32 <= K <= 2^24, K % 32 == 0 (the
+ *   - Shapes: 1 <= M <= 64, N >= 1, 32 <= K <= 2^24, K % 32 == 0 (the
  *     sampler: 1 <= M <= 65535, 1 <= N < 2^24).
  *   - Outputs must not overlap inputs (NVFP4_ERR_ARG).
  *   - Non-finite inputs give undefined (but memory-safe) results.
