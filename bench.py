@@ -57,8 +57,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "fb1ddebf4cb61c231b3bb71b96ea010db65803137ee7ea10a7cf08051fd73d86",
-    "bytes_per_step": 1108220552,
+    "sha256": "315f67bfa44cbac5c7ab225e2f35d82954b8bc7ef87d05cbf1f9bb55b4e0f700",
+    "bytes_per_step": 1108192062,
 }
 
 
