@@ -2,8 +2,9 @@
  * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 small-M decode projection.
  *
  * The operation (ReSET project page, "Core contribution -- the nvfp4r
- * CUDA-core kernel"): y = A . W^T for a small number M (1..8) of active
- * decode tokens, where both the activation A [M][K] and the weight W [N][K]
+ * CUDA-core kernel"): y = A . W^T for a small number M (1..8 on the pages;
+ * up to 64 here) of active decode tokens, where both the activation A [M][K]
+ * and the weight W [N][K]
  * are NVFP4 tensors (ReSET reading notes, section 2.1 and section 6.1):
  *
  *   - every element is a 4-bit E2M1 float, two per byte, element 2j in the
