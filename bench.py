@@ -23,7 +23,7 @@ Prints one JSON line:
                its replay on the launch stream), against the 8 TB/s HBM peak
   cpu_baseline the CPU oracle (quantize + dequantize + fp64 GEMV) on a
                bounded row sample of the same projections, same byte formula
-  extra        the four projections at M = 16, 32 and 64 (beyond the metric's M
+  extra        the four projections at M = 16, 32, 64 and 128 (beyond the metric's M
                range; per-kernel times only), the LM head (N=151936) with the
                entropy / ReSET epilogue and the top-p = 0.95 draw at the
                epilogue's temperatures, and the 64-layer decode chain
@@ -48,7 +48,7 @@ if ROOT not in sys.path:
 METRIC = "µs and effective HBM GB/s per NVFP4 GEMV at M=1/2/4/8; % of HBM peak"
 HBM_PEAK_GBS = 8000.0
 M_LIST = (1, 2, 4, 8)
-M_WIDE = (16, 32, 64)  # beyond the metric's M = 1..8: reported under extra.wide only
+M_WIDE = (16, 32, 64, 128)  # beyond the metric's M = 1..8: reported under extra.wide only
 CPU_ROWS = 2048
 
 # Measured HBM traffic of the 16 GEMV launches of one step: rocprofv3
@@ -98,7 +98,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU budget of the oracle baseline")
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head + ReSET epilogue figures")
     ap.add_argument("--no-chain", action="store_true", help="skip the 64-layer hipGraph chain figures")
-    ap.add_argument("--no-wide", action="store_true", help="skip the M = 16, 32 and 64 projection figures (extra.wide)")
+    ap.add_argument("--no-wide", action="store_true", help="skip the M = 16, 32, 64 and 128 projection figures (extra.wide)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="at the end, fill and copy a buffer of this many MiB three times: a plain copy of "
                          "known size to calibrate hardware byte counters against")
@@ -277,7 +277,7 @@ def main():
 
     extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4)}
     if not args.no_wide:
-        # 16, 32 and 64 tokens (one, two or four 16-token MFMA column tiles): the
+        # 16, 32, 64 and 128 tokens (1, 2, 4 or 8 16-token MFMA column tiles): the
         # same per-kernel timing, outside the step and the roofline figures
         wide = []
         for Mw in M_WIDE:

@@ -51,8 +51,8 @@
 //
 // The register-staged MFMA kernel (gemv_lmfma_kernel) also has 16-token
 // instantiations, for M = 9..16, where every token column of the MFMA tile
-// is in use (two activation row groups staged per step), and 32- and
-// 64-token ones, for M = 17..64, with two or four 16-token column tiles:
+// is in use (two activation row groups staged per step), and 32-, 64- and
+// 128-token ones, for M = 17..128, with 2, 4 or 8 16-token column tiles:
 // each decoded weight operand feeds one MFMA per column tile, so the weight
 // bytes and their decode are shared by all the tokens.  The MFMA tile kernels deal the rows
 // of small-N shapes out evenly over the CUs (tile_rows_for).
@@ -897,7 +897,7 @@ constexpr int kLdsCodeRow = 144;  // LDS bytes per 128-byte row of codes
 constexpr int kLdsScaleRow = 20;  // LDS bytes per 16-byte row of scales
 
 // activation rows in a slot: 8 for up to 8 tokens, else the token count
-// (16, 32 or 64)
+// (16, 32, 64 or 128)
 template <int MT>
 constexpr int lmfma_act_rows() {
   return MT > 8 ? MT : 8;
@@ -911,10 +911,10 @@ constexpr int lmfma_slot_bytes() {
 template <int R>
 struct LmfmaStep {
   uint4 w[R][2];    // weight codes: rows 8h + lane/8 of tile r, 16 bytes at 16*(lane%8)
-  uint4 a[8];       // activation codes: rows 8 g + lane/8 (g < activation rows / 8), 16 bytes at 16*(lane%8)
+  uint4 a[16];      // activation codes: rows 8 g + lane/8 (g < activation rows / 8), 16 bytes at 16*(lane%8)
   uint32_t ws[R];   // weight scales: row lane/4 of tile r, bytes 4*(lane%4) .. +3 (or +1)
   uint32_t wsh[R];  // bytes 4*(lane%4) + 2, +3 when the word is loaded in halves
-  uint32_t as[4], ash[4];  // activation scales: rows 16 s + lane/4, the same bytes
+  uint32_t as[8], ash[8];  // activation scales: rows 16 s + lane/4, the same bytes
 };
 
 // One 256-element step for CT column tiles of 16 tokens: as mfma_step, but
@@ -945,15 +945,34 @@ __device__ __forceinline__ void mfma_step_ct(const uint4 (&w)[R][2], const uint3
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    half8_t b[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) b[ct] = wdecode8_scaled(word_of(j < 4 ? a0[ct] : a1[ct], j & 3), ha[ct][j >> 1]);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const half8_t a = wdecode8_scaled(word_of(w[r][j >> 2], j & 3), hw[r][j >> 1]);
+    if constexpr (CT <= 2) {
+      // activation operands first (CT of them live), then one weight
+      // operand at a time
+      half8_t b[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        acc[r * CT + ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[ct], acc[r * CT + ct], 0, 0, 0);
+        b[ct] = wdecode8_scaled(word_of(j < 4 ? a0[ct] : a1[ct], j & 3), ha[ct][j >> 1]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const half8_t a = wdecode8_scaled(word_of(w[r][j >> 2], j & 3), hw[r][j >> 1]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          acc[r * CT + ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[ct], acc[r * CT + ct], 0, 0, 0);
+      }
+    } else {
+      // weight operands first (R of them live), then one column tile's
+      // activation operand at a time, so the live registers grow with R,
+      // not CT
+      half8_t a[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) a[r] = wdecode8_scaled(word_of(w[r][j >> 2], j & 3), hw[r][j >> 1]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const half8_t b = wdecode8_scaled(word_of(j < 4 ? a0[ct] : a1[ct], j & 3), ha[ct][j >> 1]);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          acc[r * CT + ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], b, acc[r * CT + ct], 0, 0, 0);
+      }
     }
   }
 }
@@ -1854,10 +1873,11 @@ const Variant kVariants[] = {
     LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 2),
     // ... for 9..16 tokens (every column of the 16-token MFMA tile in use)
     LMFMA_V(16, 1, 4, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(16, 1, 8, 1), LMFMA_V(16, 2, 8, 1),
-    // ... for 17..32 and 33..64 tokens (two or four 16-token column tiles per
-    // decoded weight operand)
+    // ... for 17..32, 33..64 and 65..128 tokens (2, 4 or 8 16-token column
+    // tiles per decoded weight operand)
     LMFMA_V(32, 1, 4, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(32, 1, 8, 1), LMFMA_V(32, 2, 8, 1),
     LMFMA_V(64, 1, 4, 1), LMFMA_V(64, 2, 4, 1), LMFMA_V(64, 1, 8, 1), LMFMA_V(64, 2, 8, 1),
+    LMFMA_V(128, 1, 4, 1), LMFMA_V(128, 2, 4, 1), LMFMA_V(128, 1, 2, 1),
     // direct-to-LDS MFMA (K % 256 == 0)
     DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
     DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
@@ -1879,7 +1899,9 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64; }
+int mt_of(int M) {
+  return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128;
+}
 
 int find_variant(const char* name) {
   for (int i = 0; i < kNumVariants; ++i)
@@ -1913,8 +1935,9 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
   auto fmma_sa = [&](int i, int otherwise) { return sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
-  // 33..64 tokens: four 16-token column tiles; 17..32: two; 9..16: all 16
-  // token columns of one tile (the register-staged MFMA kernel)
+  // 65..128 tokens: eight 16-token column tiles; 33..64: four; 17..32: two;
+  // 9..16: all 16 token columns of one tile (the register-staged MFMA kernel)
+  if (M > 64) return VARIANT("lmfma_m128_r2_w4_p1");
   if (M > 32) return K >= 16384 ? VARIANT("lmfma_m64_r2_w8_p1") : VARIANT("lmfma_m64_r2_w4_p1");
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
@@ -2009,7 +2032,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
          : mt_of(M) <= 8  ? VARIANT("mfma_m8_r2_w8_p1")
          : mt_of(M) <= 16 ? VARIANT("lmfma_m16_r1_w4_p1")
          : mt_of(M) <= 32 ? VARIANT("lmfma_m32_r1_w4_p1")
-                          : VARIANT("lmfma_m64_r1_w4_p1");
+         : mt_of(M) <= 64 ? VARIANT("lmfma_m64_r1_w4_p1")
+                          : VARIANT("lmfma_m128_r1_w4_p1");
   const Variant& v = kVariants[vi];
   GemvConfig c{};
   c.variant = vi;

@@ -38,7 +38,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 
 // Tokens (M) a GEMV, an activation quantization and a ReSET state set serve
 // per call: 1..kMaxTokens.
-constexpr int kMaxTokens = 64;
+constexpr int kMaxTokens = 128;
 
 struct EpilogueArgs {
   float tau0, t_low, t_high, t_base;

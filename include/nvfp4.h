@@ -3,7 +3,7 @@
  *
  * The operation (ReSET project page, "Core contribution -- the nvfp4r
  * CUDA-core kernel"): y = A . W^T for a small number M (1..8 on the pages;
- * up to 64 here) of active decode tokens, where both the activation A [M][K]
+ * up to 128 here) of active decode tokens, where both the activation A [M][K]
  * and the weight W [N][K]
  * are NVFP4 tensors (ReSET reading notes, section 2.1 and section 6.1):
  *
@@ -32,7 +32,7 @@
  *   - Device pointers must be 16-byte aligned (NVFP4_ERR_ALIGN otherwise),
  *     except scalars (global scales, entropy/temperature outputs, flags)
  *     and the sampler's arrays (4 bytes).
- *   - Shapes: 1 <= M <= 64, N >= 1, 32 <= K <= 2^24, K % 32 == 0 (the
+ *   - Shapes: 1 <= M <= 128, N >= 1, 32 <= K <= 2^24, K % 32 == 0 (the
  *     sampler: 1 <= M <= 65535, 1 <= N < 2^24).
  *   - Outputs must not overlap inputs (NVFP4_ERR_ARG).
  *   - Non-finite inputs give undefined (but memory-safe) results.

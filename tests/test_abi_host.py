@@ -51,7 +51,7 @@ def _gemv(L, M=1, N=64, K=64, a=A, asc=A + BIG, ag=A + 2 * BIG, w=A + 3 * BIG, w
 
 
 def test_gemv_shape_errors(L):
-    for M, N, K in [(0, 64, 64), (65, 64, 64), (1, 0, 64), (1, 64, 16), (1, 64, 48), (1, 64, 0), (-1, 64, 64)]:
+    for M, N, K in [(0, 64, 64), (129, 64, 64), (1, 0, 64), (1, 64, 16), (1, 64, 48), (1, 64, 0), (-1, 64, 64)]:
         assert _gemv(L, M, N, K) == F.NVFP4_ERR_SHAPE, (M, N, K)
 
 
@@ -87,7 +87,7 @@ def test_quantize_act_errors(L):
     q = L.nvfp4_quantize_act
     x, c, s, g = A, A + BIG, A + 2 * BIG, A + 3 * BIG
     assert q(x, 0, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
-    assert q(x, 65, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
+    assert q(x, 129, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
     assert q(x, 1, 40, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_SHAPE
     assert q(None, 1, 64, c, s, g, 0, None, 0, None) == F.NVFP4_ERR_NULL
     assert q(x, 1, 64, c, s, None, 0, None, 0, None) == F.NVFP4_ERR_NULL
@@ -124,7 +124,7 @@ def test_reset_state_and_workspace_helpers(L):
         sz = L.nvfp4_reset_state_size(w)
         assert sz % 16 == 0 and sz >= 4 * w + 32
     assert L.nvfp4_reset_state_init(A, 0, 8, None) == F.NVFP4_ERR_SHAPE
-    assert L.nvfp4_reset_state_init(A, 65, 8, None) == F.NVFP4_ERR_SHAPE
+    assert L.nvfp4_reset_state_init(A, 129, 8, None) == F.NVFP4_ERR_SHAPE
     assert L.nvfp4_reset_state_init(A, 1, 0, None) == F.NVFP4_ERR_ARG
     assert L.nvfp4_reset_state_init(None, 1, 8, None) == F.NVFP4_ERR_NULL
     assert L.nvfp4_reset_state_init(A + 8, 1, 8, None) == F.NVFP4_ERR_ALIGN
@@ -150,7 +150,7 @@ def test_launch_table_names_real_variants(L, monkeypatch):
     shapes = [(c.N, c.K) for c in W.qwen3_8b_cases() + W.qwen3_32b_cases()]
     shapes += [(W.lm_head_case().N, W.lm_head_case().K), (4096, 4096), (4097, 4128), (300, 96), (1, 32)]
     for (N, K) in shapes:
-        for M in range(1, 65):
+        for M in range(1, 129):
             for lm in (False, True):
                 v = F.nvfp4_gemv_variant(M, N, K, lm)
                 assert v in names, (M, N, K, v)

@@ -28,7 +28,8 @@ SMALL = [(1, 1, 32), (1, 100, 64), (2, 257, 96), (3, 33, 160), (4, 1000, 512), (
          (6, 129, 4128), (7, 70, 8192), (8, 500, 5120), (8, 17, 12288), (8, 300, 25600), (1, 4097, 4096),
          (9, 300, 5120), (11, 1000, 512), (12, 129, 4128), (16, 37, 96), (16, 515, 8192), (16, 70, 25600),
          (17, 300, 5120), (24, 129, 4128), (31, 1000, 512), (32, 37, 96), (32, 515, 8192), (32, 70, 25600),
-         (33, 300, 5120), (48, 129, 4128), (64, 37, 96), (64, 515, 8192), (64, 70, 25600)]
+         (33, 300, 5120), (48, 129, 4128), (64, 37, 96), (64, 515, 8192), (64, 70, 25600),
+         (65, 300, 5120), (100, 129, 4128), (128, 37, 96), (128, 515, 2048), (128, 70, 25600)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
@@ -83,7 +84,7 @@ def test_qwen3_8b_projections(case):
 
 @pytest.mark.parametrize("case", W.qwen3_32b_cases(), ids=lambda c: c.name)
 def test_qwen3_32b_projections(case):
-    _full_size(case, (1, 2, 4, 8, 16, 32, 64))
+    _full_size(case, (1, 2, 4, 8, 16, 32, 64, 128))
 
 
 def test_lm_head_projection():
@@ -161,6 +162,7 @@ ROW_MAP_CASES = [("lmfma_m8_r2_w8_p1", 8, 4099, 2048), ("lmfma_m8_r1_w4_p1", 5, 
                  ("lmfma_m16_r2_w8_p1", 16, 5117, 2048), ("lmfma_m16_r1_w4_p1", 10, 4099, 1312),
                  ("lmfma_m32_r2_w8_p1", 32, 5117, 2048), ("lmfma_m32_r1_w4_p1", 20, 4099, 1312),
                  ("lmfma_m64_r1_w8_p1", 64, 5117, 2048), ("lmfma_m64_r2_w4_p1", 40, 4099, 1312),
+                 ("lmfma_m128_r1_w4_p1", 128, 5117, 1024), ("lmfma_m128_r2_w4_p1", 90, 4099, 1312),
                  ("dma_m8_r2_w4_d3", 8, 5117, 1024), ("dma_m8_r2_w4_d2_sa", 7, 4099, 2048),
                  ("fmma_m4_r2_w4_d3", 4, 5117, 1024), ("fmma_m2_r1_w4_d3_sa", 2, 4099, 1024)]
 

@@ -23,7 +23,7 @@ def _act_case(bits, what, gscale=None):
 
 
 @pytest.mark.parametrize("K", [4096, 5120, 8192, 12288, 25600])
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 32, 64, 128])
 def test_activation_workloads(M, K):
     _act_case(W.activations_bf16(101 + K, K, M), f"act M={M} K={K}")
 
