@@ -57,8 +57,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "315f67bfa44cbac5c7ab225e2f35d82954b8bc7ef87d05cbf1f9bb55b4e0f700",
-    "bytes_per_step": 1108192062,
+    "sha256": "b0d492f2440a8b276681f499d8e114bae00de462a062fade2c202d0bca2fa62e",
+    "bytes_per_step": 1108170582,
 }
 
 
