@@ -39,6 +39,8 @@ NVFP4_ERR_ARG = -7
 
 NVFP4_GS_DYNAMIC = 0
 NVFP4_GS_STATIC = 1
+NVFP4_GS_TOKEN_DYNAMIC = 2
+NVFP4_GS_TOKEN_STATIC = 3
 
 NVFP4_OP_PACK = 0
 NVFP4_OP_QUANT = 1
@@ -55,6 +57,7 @@ EXPORTED = (
     "nvfp4_reset_state_size",
     "nvfp4_reset_state_init",
     "nvfp4_gemv_smallm",
+    "nvfp4_gemv_smallm_token_scales",
     "nvfp4_gemv_variant",
     "nvfp4_gemv_variant_name",
     "nvfp4_sample_top_p",
@@ -120,6 +123,8 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_gemv_smallm.restype = c_int
     L.nvfp4_gemv_smallm.argtypes = [c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(LmheadEpilogue), vp, sz, vp]
+    L.nvfp4_gemv_smallm_token_scales.restype = c_int
+    L.nvfp4_gemv_smallm_token_scales.argtypes = L.nvfp4_gemv_smallm.argtypes
     L.nvfp4_sample_top_p.restype = c_int
     L.nvfp4_sample_top_p.argtypes = [c_int, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     _lib = L
@@ -213,19 +218,25 @@ def nvfp4_pack_weights(w, ws=None, out: NvFp4Tensor | None = None, stream=None) 
     return out
 
 
-def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, stream=None) -> NvFp4Tensor:
+def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, stream=None,
+                       per_token: bool = False) -> NvFp4Tensor:
     """Quantize x bf16 [M][K] (device, contiguous).  ``gscale=None``: dynamic
-    global scale (written into out.gscale); else a device fp32 [1] tensor
-    holding a static scale (used as out.gscale)."""
+    global scale (written into out.gscale); else a device fp32 tensor holding
+    a static scale (used as out.gscale).  ``per_token``: one global scale per
+    row (out.gscale [M]) instead of one for the tensor ([1])."""
     import torch
 
     M, K = int(x.shape[0]), int(x.shape[1])
-    flags = NVFP4_GS_DYNAMIC if gscale is None else NVFP4_GS_STATIC
+    if per_token:
+        flags = NVFP4_GS_TOKEN_DYNAMIC if gscale is None else NVFP4_GS_TOKEN_STATIC
+    else:
+        flags = NVFP4_GS_DYNAMIC if gscale is None else NVFP4_GS_STATIC
     if out is None:
         out = NvFp4Tensor(torch.empty((M, K // 2), dtype=torch.uint8, device=x.device),
                           torch.empty((M, K // 16), dtype=torch.uint8, device=x.device),
-                          gscale if gscale is not None else torch.empty(1, dtype=torch.float32, device=x.device))
-    need = nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K)
+                          gscale if gscale is not None else
+                          torch.empty(M if per_token else 1, dtype=torch.float32, device=x.device))
+    need = 0 if per_token else nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K)
     if need and ws is None:
         ws = new_workspace(need, x.device, stream)
     _check(lib().nvfp4_quantize_act(_ptr(x), M, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
@@ -315,10 +326,11 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
     if need and ws is None:
         ws = new_workspace(need, w.codes.device, stream)
     ws_bytes = 0 if ws is None else ws.numel()
-    _check(lib().nvfp4_gemv_smallm(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale),
-                                   _ptr(w.codes), _ptr(w.scales), _ptr(w.gscale), _ptr(y),
-                                   None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,
-                                   _stream(stream)), "nvfp4_gemv_smallm")
+    # an activation with one global scale per row goes to the per-token entry point
+    fn = lib().nvfp4_gemv_smallm_token_scales if a.gscale.numel() > 1 else lib().nvfp4_gemv_smallm
+    _check(fn(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale), _ptr(w.codes), _ptr(w.scales),
+              _ptr(w.gscale), _ptr(y), None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,
+              _stream(stream)), "nvfp4_gemv_smallm")
     return y
 
 

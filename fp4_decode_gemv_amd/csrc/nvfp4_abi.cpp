@@ -130,7 +130,11 @@ int nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, uint8_t* codes,
                        float* gscale, int flags, void* ws, size_t ws_bytes, void* stream) {
   if (M < 1 || M > kMaxTokens || !shape_ok_k(K)) return NVFP4_ERR_SHAPE;
   if (!x_bf16 || !codes || !scales || !gscale) return NVFP4_ERR_NULL;
-  if (flags != NVFP4_GS_DYNAMIC && flags != NVFP4_GS_STATIC) return NVFP4_ERR_ARG;
+  if (flags != NVFP4_GS_DYNAMIC && flags != NVFP4_GS_STATIC && flags != NVFP4_GS_TOKEN_DYNAMIC &&
+      flags != NVFP4_GS_TOKEN_STATIC)
+    return NVFP4_ERR_ARG;
+  const bool per_token = flags == NVFP4_GS_TOKEN_DYNAMIC || flags == NVFP4_GS_TOKEN_STATIC;
+  if (flags == NVFP4_GS_TOKEN_DYNAMIC && K > kTokenScaleMaxK) return NVFP4_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
   const int64_t elems = (int64_t)M * K;
   const bool two = flags == NVFP4_GS_DYNAMIC && elems > kActSelfAmaxMaxElems;
@@ -138,17 +142,20 @@ int nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, uint8_t* codes,
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return NVFP4_ERR_ALIGN;
   const size_t xb = (size_t)elems * 2, cb = (size_t)elems / 2, sb = (size_t)elems / 16;
-  if (overlaps(x_bf16, xb, codes, cb) || overlaps(x_bf16, xb, scales, sb) || overlaps(x_bf16, xb, gscale, 4) ||
-      overlaps(codes, cb, scales, sb) || overlaps(codes, cb, gscale, 4) || overlaps(scales, sb, gscale, 4) ||
+  const size_t gb = per_token ? (size_t)M * 4 : 4;
+  if (overlaps(x_bf16, xb, codes, cb) || overlaps(x_bf16, xb, scales, sb) || overlaps(x_bf16, xb, gscale, gb) ||
+      overlaps(codes, cb, scales, sb) || overlaps(codes, cb, gscale, gb) || overlaps(scales, sb, gscale, gb) ||
       (need > 0 && (overlaps(ws, need, x_bf16, xb) || overlaps(ws, need, codes, cb) ||
-                    overlaps(ws, need, scales, sb) || overlaps(ws, need, gscale, 4))))
+                    overlaps(ws, need, scales, sb) || overlaps(ws, need, gscale, gb))))
     return NVFP4_ERR_ARG;
   const int d = check_device();
   if (d != NVFP4_OK) return d;
-  const GsMode mode = flags == NVFP4_GS_STATIC ? GS_STATIC : (two ? GS_FROM_PARTIALS : GS_SELF);
+  const GsMode mode = flags == NVFP4_GS_STATIC || flags == NVFP4_GS_TOKEN_STATIC ? GS_STATIC
+                      : two                                                    ? GS_FROM_PARTIALS
+                                                                               : GS_SELF;
   return hip_status(launch_quantize_bf16(x_bf16, M, K, codes, scales, gscale, mode,
                                          two ? static_cast<float*>(ws) : nullptr,
-                                         two ? amax_partial_count(elems) : 0,
+                                         two ? amax_partial_count(elems) : 0, per_token,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -167,10 +174,13 @@ int nvfp4_reset_state_init(void* state, int M, int window, void* stream) {
   return hip_status(launch_reset_state_init(state, M, window, static_cast<hipStream_t>(stream)));
 }
 
-int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
-                      const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
-                      const float* w_gscale, float* y, const nvfp4_lmhead_epilogue_t* epi, void* ws,
-                      size_t ws_bytes, void* stream) {
+namespace {
+
+// nvfp4_gemv_smallm and its per-token-scale form: a_gscale holds 1 or M floats
+int gemv_entry(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+               const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+               float* y, const nvfp4_lmhead_epilogue_t* epi, void* ws, size_t ws_bytes, void* stream,
+               bool per_token) {
   if (!shape_ok(M, N, K)) return NVFP4_ERR_SHAPE;
   if (!a_codes || !a_scales || !a_gscale || !w_codes || !w_scales || !w_gscale || !y) return NVFP4_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
@@ -179,7 +189,8 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
   const size_t yb = (size_t)M * N * 4;
   const size_t acb = (size_t)M * K / 2, asb = (size_t)M * K / 16;
   const size_t wcb = (size_t)N * K / 2, wsb = (size_t)N * K / 16;
-  if (overlaps(y, yb, a_codes, acb) || overlaps(y, yb, a_scales, asb) || overlaps(y, yb, a_gscale, 4) ||
+  const size_t agb = per_token ? (size_t)M * 4 : 4;
+  if (overlaps(y, yb, a_codes, acb) || overlaps(y, yb, a_scales, asb) || overlaps(y, yb, a_gscale, agb) ||
       overlaps(y, yb, w_codes, wcb) || overlaps(y, yb, w_scales, wsb) || overlaps(y, yb, w_gscale, 4))
     return NVFP4_ERR_ARG;
   const GemvConfig cfg = choose_gemv_config(M, N, K, epi != nullptr);
@@ -190,7 +201,7 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
   if (need > 0 && !aligned16(ws)) return NVFP4_ERR_ALIGN;
   if (need > 0 && (overlaps(ws, need, y, yb) || overlaps(ws, need, a_codes, acb) || overlaps(ws, need, a_scales, asb) ||
-                   overlaps(ws, need, a_gscale, 4) || overlaps(ws, need, w_codes, wcb) ||
+                   overlaps(ws, need, a_gscale, agb) || overlaps(ws, need, w_codes, wcb) ||
                    overlaps(ws, need, w_scales, wsb) || overlaps(ws, need, w_gscale, 4)))
     return NVFP4_ERR_ARG;
   EpilogueArgs ea{};
@@ -221,7 +232,25 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const
   const int d = check_device();
   if (d != NVFP4_OK) return d;
   return hip_status(launch_gemv(cfg, M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y,
-                                epi ? &ea : nullptr, ws, static_cast<hipStream_t>(stream)));
+                                epi ? &ea : nullptr, ws, per_token, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int nvfp4_gemv_smallm(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                      const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                      const float* w_gscale, float* y, const nvfp4_lmhead_epilogue_t* epi, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return gemv_entry(M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y, epi, ws, ws_bytes, stream,
+                    false);
+}
+
+int nvfp4_gemv_smallm_token_scales(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                                   const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                                   const float* w_gscale, float* y, const nvfp4_lmhead_epilogue_t* epi, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return gemv_entry(M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y, epi, ws, ws_bytes, stream,
+                    true);
 }
 
 const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead) {

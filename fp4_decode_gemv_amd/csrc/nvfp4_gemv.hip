@@ -90,6 +90,7 @@ struct GemvParams {
   const uint8_t* a_codes;
   const uint8_t* a_scales;
   const float* a_gscale;
+  int a_gs_stride;  // 0: one activation global scale; 1: one per token (a_gscale[M])
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   const float* w_gscale;
@@ -103,6 +104,13 @@ struct GemvParams {
   // tile past that range read as zeros and are never stored
   int tile_rows;
 };
+
+// Product of the two global scales for token t (< M): the activation's scale
+// is shared by all tokens or, with per-token scales, the token's own.
+__device__ __forceinline__ float token_scale(const GemvParams& p, int t) {
+  return p.a_gscale[t * p.a_gs_stride] * (*p.w_gscale);
+}
+
 
 // ReSET per-sequence state (device).  Followed by float ring[window].
 struct ResetState {
@@ -490,7 +498,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_valu_kernel(GemvParams p) {
   }
 
   // reduce the G lanes of each row-group
-  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  float scale[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) scale[m] = token_scale(p, m < M ? m : 0);
   float out[R * MT];
   int tok[R * MT];
   bool ok[R * MT];
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_valu_kernel(GemvParams p) {
       float v = acc[r][m][0] + acc[r][m][1];
 #pragma unroll
       for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-      out[r * MT + m] = v * scale;
+      out[r * MT + m] = v * scale[m];
       tok[r * MT + m] = m;
       ok[r * MT + m] = g == 0 && row[r] < N && m < M;
     }
@@ -671,7 +681,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
     }
   }
 
-  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  float scale[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) scale[m] = token_scale(p, m < M ? m : 0);
   float out[R * MT];
   int tok[R * MT];
   bool ok[R * MT];
@@ -682,7 +694,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_direct_kernel(GemvParams p) {
       float v = acc[r][m][0] + acc[r][m][1];
 #pragma unroll
       for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-      out[r * MT + m] = v * scale;
+      out[r * MT + m] = v * scale[m];
       tok[r * MT + m] = m;
       ok[r * MT + m] = g == 0 && row[r] < N && m < M;
     }
@@ -761,7 +773,6 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[((wave * R * CT + rc) * 4 + v) * 64 + lane] = acc[rc][v];
   __syncthreads();
-  const float scale = (*p.a_gscale) * (*p.w_gscale);
   const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;  // rows this workgroup owns
   // wave w finalizes the (r, ct, v) register slots w, w + NW, ...; D layout:
   // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token 16 ct + li
@@ -782,7 +793,7 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
       float sum = 0.0f;
       for (int w = 0; w < NW; ++w) sum += red[((w * R * CT + rc) * 4 + v) * 64 + lane];
       const int64_t row = tile0 + 16 * r + 4 * kg + v;
-      out[u] = sum * scale;
+      out[u] = sum * token_scale(p, t < M ? t : 0);
       tok[u] = t < MT ? t : 0;
       rowt[u] = 16 * r + 4 * kg + v;
       own[u] = t < M;
@@ -1476,7 +1487,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_staged_kernel(GemvParams p) {
     }
   }
 
-  const float scale = (*p.a_gscale) * (*p.w_gscale);
+  float scale[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) scale[m] = token_scale(p, m < M ? m : 0);
   float out[R * MT];
   int tok[R * MT];
   bool ok[R * MT];
@@ -1488,7 +1501,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_staged_kernel(GemvParams p) {
 #pragma unroll
       for (int o = G / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
       const int64_t row = tile0 + rloc[r];
-      out[r * MT + m] = v * scale;
+      out[r * MT + m] = v * scale[m];
       tok[r * MT + m] = m;
       ok[r * MT + m] = g == 0 && row < N && m < M;
       if (ok[r * MT + m]) p.y[(int64_t)m * N + row] = out[r * MT + m];
@@ -1739,7 +1752,6 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[((wave * R + r) * 4 + v) * 64 + lane] = acc[r][v];
   __syncthreads();
-  const float scale = (*p.a_gscale) * (*p.w_gscale);
   constexpr int OUTS = 16 * R * MT;                     // (row, token) results of the tile
   constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);  // per thread
   float out[NV];
@@ -1763,7 +1775,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
           for (int v = 0; v < 4; ++v)
             if ((4 * g + v) % MT == j) sum += red[((w * R + r) * 4 + v) * 64 + g * 16 + nn];
       const int64_t row = tile0 + rt;
-      out[u] = sum * scale;
+      out[u] = sum * token_scale(p, j < M ? j : 0);
       tok[u] = j;
       rowt[u] = rt;
       own[u] = j < M;
@@ -2092,7 +2104,7 @@ size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi) {
 hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_gscale, const uint8_t* w_codes,
                        const uint8_t* w_scales, const float* w_gscale, float* y,
-                       const EpilogueArgs* epi, void* ws, hipStream_t stream) {
+                       const EpilogueArgs* epi, void* ws, bool per_token, hipStream_t stream) {
   if (cfg.variant < 0 || cfg.variant >= kNumVariants) return hipErrorInvalidConfiguration;
   GemvParams p{};
   p.M = M;
@@ -2102,6 +2114,7 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   p.a_codes = a_codes;
   p.a_scales = a_scales;
   p.a_gscale = a_gscale;
+  p.a_gs_stride = per_token ? 1 : 0;
   p.w_codes = w_codes;
   p.w_scales = w_scales;
   p.w_gscale = w_gscale;

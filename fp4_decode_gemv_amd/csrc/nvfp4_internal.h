@@ -28,7 +28,10 @@ constexpr int64_t kActSelfAmaxMaxElems = 131072;
 // Launchers (no validation: the C-ABI layer has done it).
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
                                 uint8_t* scales, float* gscale, GsMode mode, float* partials,
-                                int n_parts, hipStream_t stream);
+                                int n_parts, bool per_token, hipStream_t stream);
+// largest K of a per-token dynamic quantization (one launch, every
+// workgroup of a row reads the whole row for its amax)
+constexpr int64_t kTokenScaleMaxK = 131072;
 hipError_t launch_quantize_f32(const float* x, int64_t rows, int64_t K, uint8_t* codes,
                                uint8_t* scales, float* gscale, float* partials, int n_parts,
                                hipStream_t stream);
@@ -79,7 +82,7 @@ constexpr int kResetMaxWindow = 1024;
 hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const uint8_t* a_scales, const float* a_gscale, const uint8_t* w_codes,
                        const uint8_t* w_scales, const float* w_gscale, float* y,
-                       const EpilogueArgs* epi, void* ws, hipStream_t stream);
+                       const EpilogueArgs* epi, void* ws, bool per_token, hipStream_t stream);
 
 hipError_t launch_reset_state_init(void* state, int M, int window, hipStream_t stream);
 

@@ -278,6 +278,13 @@ __global__ __launch_bounds__(T) void quantize_act_kernel(
     uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode,
     const float* __restrict__ partials, int n_parts) {
   __shared__ __align__(16) uint32_t red[T / 64];
+  // segment blockIdx.y of nelem elements: the whole tensor (gridDim.y == 1),
+  // or one row with its own global scale (per-token scales, gridDim.y == M)
+  const int64_t seg = blockIdx.y;
+  x += seg * nelem;
+  codes += seg * (nelem / 2);
+  scales += seg * (nelem / 16);
+  gscale += seg;
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, (int)(nelem * 2), kBufferWord3);
   const int mine = ((int)blockIdx.x * T + (int)threadIdx.x) * 8;  // first element of this thread
@@ -357,8 +364,11 @@ int amax_partial_count(int64_t elems) {
 
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
                                 uint8_t* scales, float* gscale, GsMode mode, float* partials,
-                                int n_parts, hipStream_t stream) {
-  const int64_t nelem = rows * K;
+                                int n_parts, bool per_token, hipStream_t stream) {
+  // per-token scales: one segment (and one global scale) per row
+  const int64_t nelem = per_token ? K : rows * K;
+  const unsigned segs = per_token ? (unsigned)rows : 1u;
+  if (per_token && mode == GS_FROM_PARTIALS) return hipErrorInvalidValue;
   if (mode == GS_SELF && nelem > kActSelfElems) return hipErrorInvalidValue;
   if (mode == GS_FROM_PARTIALS) {
     hipLaunchKernelGGL(amax_partials_kernel<uint16_t>, dim3(n_parts), dim3(kThreads), 0, stream, x, nelem,
@@ -378,8 +388,8 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint
             : threads == 128 ? quantize_act_kernel<128>
             : threads == 256 ? quantize_act_kernel<256>
                              : quantize_act_kernel<512>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, stream, x, nelem, codes, scales, gscale, (int)mode,
-                     partials, n_parts);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid, segs), dim3(threads), 0, stream, x, nelem, codes, scales, gscale,
+                     (int)mode, partials, n_parts);
   return hipGetLastError();
 }
 

@@ -69,8 +69,9 @@ typedef enum {
                                overlapping input/output buffers               */
 } nvfp4_status_t;
 
-/* nvfp4_quantize_act flags */
-enum { NVFP4_GS_DYNAMIC = 0, NVFP4_GS_STATIC = 1 };
+/* nvfp4_quantize_act flags: one activation global scale per tensor, or one
+   per token (row) */
+enum { NVFP4_GS_DYNAMIC = 0, NVFP4_GS_STATIC = 1, NVFP4_GS_TOKEN_DYNAMIC = 2, NVFP4_GS_TOKEN_STATIC = 3 };
 
 /* ops for nvfp4_workspace_size */
 enum { NVFP4_OP_PACK = 0, NVFP4_OP_QUANT = 1, NVFP4_OP_GEMV = 2, NVFP4_OP_GEMV_LMHEAD = 3, NVFP4_OP_SAMPLE = 4 };
@@ -107,6 +108,12 @@ int nvfp4_pack_weights(const float* w, int64_t N, int64_t K,
  *           row's codes depend on the other rows);
  *   flags = NVFP4_GS_STATIC:  *gscale (device) is READ (a calibrated
  *           scale); rows are then independent.
+ *   flags = NVFP4_GS_TOKEN_DYNAMIC: gscale[M] (device) is WRITTEN, row m's
+ *           scale being the amax over that row alone / 2688 (the recipe
+ *           applied to each row as its own tensor; K <= 131072).  Rows are
+ *           independent and the quantization is one launch at every M.
+ *   flags = NVFP4_GS_TOKEN_STATIC: gscale[M] (device) is READ.
+ *   Per-token scales go with nvfp4_gemv_smallm_token_scales.
  * Codes, scales and gscale are bit-identical to the reference recipe.
  * Workspace: nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K) bytes (may be 0;
  * ws may then be NULL).
@@ -173,6 +180,21 @@ int nvfp4_gemv_smallm(int M, int64_t N, int64_t K,
                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
                       float* y, const nvfp4_lmhead_epilogue_t* epi,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_gemv_smallm for an activation quantized with one global scale per
+ * token (NVFP4_GS_TOKEN_*): a_gscale points to M floats (device) and output
+ * row m is scaled by a_gscale[m] * (*w_gscale).  This is one of the ways to
+ * shorten the separate "Q" step (reading notes, section 5.3): no tensor-wide
+ * amax has to finish before any row is quantized.  Everything else,
+ * including the epilogue, workspace and error behaviour, is as for
+ * nvfp4_gemv_smallm, with the same kernels.
+ */
+int nvfp4_gemv_smallm_token_scales(int M, int64_t N, int64_t K,
+                                   const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                                   const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                                   float* y, const nvfp4_lmhead_epilogue_t* epi,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Name of the kernel variant nvfp4_gemv_smallm launches for this shape

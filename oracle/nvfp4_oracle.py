@@ -191,13 +191,17 @@ def unpack_codes(codes: np.ndarray) -> np.ndarray:
     return q
 
 
-def dequantize(codes: np.ndarray, scales: np.ndarray, gscale: float) -> np.ndarray:
+def dequantize(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
     """Exact real values E2M1(q) * E4M3(s_b) * s_g as float64 [rows][K]
-    (each product has at most 6 + 24 significant bits, exact in float64)."""
+    (each product has at most 6 + 24 significant bits, exact in float64).
+    ``gscale`` is one scale for the tensor, or one per row ([rows])."""
     q = unpack_codes(codes)
     vals = E2M1_TABLE[q]
     sc = np.repeat(E4M3_TABLE[scales], BLOCK, axis=1)
-    return vals * sc * np.float64(np.float32(gscale))
+    g = np.asarray(gscale, dtype=np.float32).astype(np.float64)
+    if g.ndim == 1:
+        g = g[:, None]
+    return vals * sc * g
 
 
 # ---------------------------------------------------------------------------
@@ -230,3 +234,15 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 def quantize_act_bf16(x_bits: np.ndarray, gscale: float | None = None):
     """Quantize a bf16 activation [M][K] given as bit patterns."""
     return quantize_nvfp4(bf16_to_f32(x_bits), gscale)
+
+
+def quantize_act_bf16_per_token(x_bits: np.ndarray, gscales=None):
+    """Per-token global scales: each row [1][K] of the bf16 activation is
+    quantized as a tensor of its own (its own amax / 2688, or its entry of
+    ``gscales``), the recipe of the reading notes, section 5.3, applied row by
+    row.  Returns (codes [M][K/2], scales [M][K/16], gscales float32 [M])."""
+    rows = []
+    for m in range(x_bits.shape[0]):
+        rows.append(quantize_act_bf16(x_bits[m:m + 1], None if gscales is None else gscales[m]))
+    return (np.concatenate([r[0] for r in rows]), np.concatenate([r[1] for r in rows]),
+            np.array([r[2] for r in rows], dtype=np.float32))

@@ -103,6 +103,27 @@ def test_quantize_act_errors(L):
     assert L.nvfp4_workspace_size(F.NVFP4_OP_QUANT, 1, 0, 4096) == 0
 
 
+def test_per_token_scale_errors(L):
+    q = L.nvfp4_quantize_act
+    x, c, s, g = A, A + BIG, A + 2 * BIG, A + 3 * BIG
+    assert q(x, 1, 64, c, s, g, 4, None, 0, None) == F.NVFP4_ERR_ARG                 # unknown flag
+    assert q(x, 2, 131072 + 32, c, s, g, F.NVFP4_GS_TOKEN_DYNAMIC, None, 0, None) == F.NVFP4_ERR_SHAPE
+    # gscale [M]: 8 floats from 4 bytes below the codes reach into them
+    assert q(x, 8, 64, c, s, c - 4, F.NVFP4_GS_TOKEN_DYNAMIC, None, 0, None) == F.NVFP4_ERR_ARG
+    assert q(x, 8, 64, c, s, c - 4, F.NVFP4_GS_DYNAMIC, None, 0, None) not in (F.NVFP4_ERR_ARG,)
+    # per-token flags need no workspace at any size: validation passes
+    for fl in (F.NVFP4_GS_TOKEN_DYNAMIC, F.NVFP4_GS_TOKEN_STATIC):
+        assert q(x, 8, 25600, c, s, g, fl, None, 0, None) in (F.NVFP4_ERR_DEVICE, F.NVFP4_ERR_HIP)
+    gt = L.nvfp4_gemv_smallm_token_scales
+    a, asc, ag, w, wsc, wg, y = A, A + BIG, A + 2 * BIG, A + 3 * BIG, A + 4 * BIG, A + 5 * BIG, A + 6 * BIG
+    assert gt(0, 64, 64, a, asc, ag, w, wsc, wg, y, None, None, 0, None) == F.NVFP4_ERR_SHAPE
+    assert gt(4, 64, 64, a, asc, None, w, wsc, wg, y, None, None, 0, None) == F.NVFP4_ERR_NULL
+    # a_gscale [4] reaching into y (its last float is y's first)
+    assert gt(4, 64, 64, a, asc, y - 12, w, wsc, wg, y, None, None, 0, None) == F.NVFP4_ERR_ARG
+    assert _gemv(L, M=4, ag=y - 12) != F.NVFP4_ERR_ARG    # one scale (4 bytes) ends before y
+    assert gt(4, 64, 64, a, asc, ag, w, wsc, wg, y, None, None, 0, None) in (F.NVFP4_ERR_DEVICE, F.NVFP4_ERR_HIP)
+
+
 def test_pack_errors(L):
     p = L.nvfp4_pack_weights
     w, c, s, g, ws = A, A + BIG, A + 2 * BIG, A + 3 * BIG, A + 4 * BIG

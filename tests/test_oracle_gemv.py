@@ -90,3 +90,23 @@ def test_row_permutation_commutes_and_ref_abs_bounds():
     assert np.all(np.abs(y2 - y[:, p]) <= 1e-13 * ra[:, p])
     assert np.all(np.abs(ra2 - ra[:, p]) <= 1e-13 * ra[:, p])
     assert np.all(ra >= np.abs(y))
+
+
+def test_per_token_global_scales_match_exact_rationals():
+    """One activation global scale per row: y[m] uses row m's own scale
+    (exact rationals, each row decoded with its own scale)."""
+    e2m1, e4m3 = _tables()
+    rng = np.random.default_rng(23)
+    M, N, K = 3, 2, 32
+    codes, scales, _ = _rand_q(rng, M, K)
+    gs = np.array([0.25, 3.0, 1e-3], np.float32)
+    w = _rand_q(rng, N, K)
+    y, ref_abs = O.gemv_ref((codes, scales, gs), w)
+    W = _exact(w, e2m1, e4m3)
+    for m in range(M):
+        A = _exact((codes[m:m + 1], scales[m:m + 1], gs[m]), e2m1, e4m3)[0]
+        for n in range(N):
+            ex = sum(A[k] * W[n][k] for k in range(K))
+            ab = sum(abs(A[k] * W[n][k]) for k in range(K))
+            assert abs(Fraction(y[m, n]) - ex) <= Fraction(1, 10 ** 14) * ab
+            assert abs(Fraction(ref_abs[m, n]) - ab) <= Fraction(1, 10 ** 14) * ab

@@ -151,3 +151,38 @@ def test_quantized_values_are_monotone_in_x():
     for b in range(64):
         o = np.argsort(xb[b], kind="stable")
         assert np.all(np.diff(xh[b][o]) >= 0)
+
+
+def _bf16_rows(seed, M, K):
+    x = np.random.default_rng(seed).standard_normal((M, K)).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)  # truncation keeps the values exactly bf16
+
+
+def test_per_token_scales_equal_the_tensor_scale_when_row_maxima_agree():
+    """Rows whose amax is the same value: per-token quantization gives the
+    per-tensor codes, scales and (in every row) the tensor's global scale."""
+    xb = _bf16_rows(31, 4, 96)
+    xb[:, 7] = 0x4120                      # 10.0 in every row, above any N(0,1) draw here
+    codes, scales, gs = O.quantize_act_bf16(xb)
+    tc, ts, tg = O.quantize_act_bf16_per_token(xb)
+    assert tg.shape == (4,) and np.all(tg.view(np.uint32) == np.float32(gs).view(np.uint32))
+    assert np.array_equal(tc, codes) and np.array_equal(ts, scales)
+    assert gs == np.float32(10.0) / np.float32(2688.0)
+
+
+def test_per_token_scale_follows_only_its_own_row():
+    """Scaling row 1 by 2^3 (exact in bf16) multiplies only its global scale
+    by 8 and leaves every code and block scale as it was; an all-zero row has
+    global scale 0 and zero codes without touching the other rows."""
+    xb = _bf16_rows(32, 3, 160)
+    c0, s0, g0 = O.quantize_act_bf16_per_token(xb)
+    x2 = xb.copy()
+    x2[1] = x2[1] + np.where((x2[1] & 0x7FFF) != 0, 3 << 7, 0).astype(np.uint16)  # exponent + 3
+    c1, s1, g1 = O.quantize_act_bf16_per_token(x2)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    assert g1[1] == np.float32(8.0) * g0[1] and g1[0] == g0[0] and g1[2] == g0[2]
+    x3 = xb.copy()
+    x3[2] = 0
+    c2, s2, g2 = O.quantize_act_bf16_per_token(x3)
+    assert g2[2] == 0 and not c2[2].any() and not s2[2].any()
+    assert np.array_equal(c2[:2], c0[:2]) and np.array_equal(g2[:2], g0[:2])
