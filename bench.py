@@ -57,8 +57,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "b0d492f2440a8b276681f499d8e114bae00de462a062fade2c202d0bca2fa62e",
-    "bytes_per_step": 1108170582,
+    "sha256": "cdddf94f97f5141e5560e047ad92dd13dbff0859e4eeca2a1e92c284b3a27774",
+    "bytes_per_step": 1108566105,
 }
 
 
@@ -230,6 +230,36 @@ def main():
     log(args, f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s effective (quantization included)")
     del g_step
 
+    # the same step with one activation global scale per token (the
+    # quantization's per-token option, which needs no tensor-wide amax; not
+    # the metric's per-tensor recipe, so it is reported apart from `value`)
+    tok_out = {k: F.nvfp4_quantize_act(v[0], per_token=True) for k, v in acts.items() if k[1] in M_LIST}
+
+    def step_token():
+        for mi, M in enumerate(M_LIST):
+            for c in cases:
+                x, _, _, gws, y = acts[(c.name, M)]
+                at = tok_out[(c.name, M)]
+                F.nvfp4_quantize_act(x, out=at, stream=stream, per_token=True)
+                copies = wq[c.name]
+                F.nvfp4_gemv_smallm(at, copies[mi % len(copies)], y=y, ws=gws, stream=stream)
+
+    g_tok = capture(step_token)
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            g_tok.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            g_tok.replay()
+    torch.cuda.synchronize()
+    tok_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    token_scales = {"ms_per_step": round(tok_ms, 4),
+                    "gbs": round(bytes_per_step / (tok_ms * 1e-3) / 1e9, 1)}
+    log(args, f"[bench] per-token scales: {tok_ms * 1e3:.1f} us/step, {token_scales['gbs']:.0f} GB/s effective")
+    del g_tok
+
     # the same step launched eagerly from Python, for reference (host-bound)
     with torch.cuda.stream(stream):
         step()
@@ -275,7 +305,7 @@ def main():
                       f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us")
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
 
-    extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4)}
+    extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4), "token_scales": token_scales}
     if not args.no_wide:
         # 16, 32, 64 and 128 tokens (1, 2, 4 or 8 16-token MFMA column tiles): the
         # same per-kernel timing, outside the step and the roofline figures
