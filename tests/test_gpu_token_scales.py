@@ -117,3 +117,43 @@ def test_lm_head_epilogue_with_token_scales(M):
     assert np.all(np.abs(ent.cpu().numpy() - Href) <= 1e-4), (ent.cpu().numpy(), Href)
     y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16_per_token(xb), O.quantize_nvfp4(w))
     assert_gemv_close(logits, y_ref, ref_abs, what=f"lm M={M}")
+
+
+def test_graph_replays_match_eager():
+    """Per-token quantization + GEMV captured in a HIP graph and replayed
+    with a new activation before each replay (eager work in between) gives
+    the eager bits every time."""
+    M, N, K = 8, 6000, 5120
+    w = W.small_random_weights(71, N, K)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    xs = [bf16_dev(_spread_rows(W.small_random_bf16(72 + i, M, K), 73 + i)) for i in range(3)]
+    ref = []
+    for xi in xs:
+        aq = F.nvfp4_quantize_act(xi, per_token=True)
+        ref.append((F.nvfp4_gemv_smallm(aq, wq).clone(), aq.gscale.clone()))
+    x = torch.empty_like(xs[0])
+    aq = F.nvfp4_quantize_act(xs[0], per_token=True)
+    y = torch.empty((M, N), device=x.device)
+    s = torch.cuda.Stream()
+
+    def call():
+        F.nvfp4_quantize_act(x, out=aq, stream=s, per_token=True)
+        F.nvfp4_gemv_smallm(aq, wq, y=y, stream=s)
+
+    with torch.cuda.stream(s):
+        x.copy_(xs[0])
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for r in range(6):
+        x.copy_(xs[r % 3])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[r % 3][0]), r
+        assert torch.equal(aq.gscale, ref[r % 3][1]), r
+        y.zero_()
+        torch.cuda.synchronize()
