@@ -58,7 +58,7 @@ CPU_ROWS = 2048
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
     "sha256": "cdddf94f97f5141e5560e047ad92dd13dbff0859e4eeca2a1e92c284b3a27774",
-    "bytes_per_step": 1108566105,
+    "bytes_per_step": 1108508048,
 }
 
 
@@ -523,26 +523,31 @@ def bench_chain(args, stream):
                 c = W.chain_case(l, p)
                 x = torch.from_numpy(W.chain_activations_bf16(l, p, M).view(np.int16)).to(dev).view(torch.bfloat16)
                 aq = F.nvfp4_quantize_act(x)
+                at = F.nvfp4_quantize_act(x, per_token=True)
                 qn = F.nvfp4_workspace_size(F.NVFP4_OP_QUANT, M, 0, c.K)
                 gn = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, c.N, c.K)
-                io[(l, p)] = (x, aq, F.new_workspace(qn, dev) if qn else None,
+                io[(l, p)] = (x, aq, at, F.new_workspace(qn, dev) if qn else None,
                               F.new_workspace(gn, dev) if gn else None, torch.empty((M, c.N), device=dev))
         res = {"M": M, "weight_bytes": total}
-        for quantize in (True, False):
+        # per-tensor quantization + GEMV, per-token quantization + GEMV, GEMV alone
+        for key in ("quant_gemv", "token_quant_gemv", "gemv_only"):
             def step(_i):
                 for l in range(W.CHAIN_LAYERS):
                     for p in range(4):
-                        x, aq, qws, gws, y = io[(l, p)]
-                        if quantize:
+                        x, aq, at, qws, gws, y = io[(l, p)]
+                        if key == "quant_gemv":
                             F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
-                        F.nvfp4_gemv_smallm(aq, ws[(l, p)], y=y, ws=gws, stream=stream)
+                        elif key == "token_quant_gemv":
+                            F.nvfp4_quantize_act(x, out=at, stream=stream, per_token=True)
+                        F.nvfp4_gemv_smallm(at if key == "token_quant_gemv" else aq, ws[(l, p)], y=y, ws=gws,
+                                            stream=stream)
             us = _graph_us(step, 1, stream)
-            key = "quant_gemv" if quantize else "gemv_only"
             res[key + "_us_per_step"] = round(us, 1)
             res[key + "_gbs"] = round(total / us / 1e3, 1)
         out.append(res)
         log(args, f"[chain] M={M} {res['quant_gemv_us_per_step']:.1f} us/step with quantization "
-                  f"({res['quant_gemv_gbs']:.0f} GB/s), {res['gemv_only_us_per_step']:.1f} us GEMV only "
+                  f"({res['quant_gemv_gbs']:.0f} GB/s), {res['token_quant_gemv_us_per_step']:.1f} us with "
+                  f"per-token scales, {res['gemv_only_us_per_step']:.1f} us GEMV only "
                   f"({res['gemv_only_gbs']:.0f} GB/s)")
         del io
     del ws
