@@ -65,8 +65,8 @@ const char* nvfp4_status_str(int status) {
     case NVFP4_OK: return "NVFP4_OK";
     case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
     case NVFP4_ERR_SHAPE:
-      return "NVFP4_ERR_SHAPE: a size is out of range (GEMV and quantization: 1<=M<=8, N>=1, 32<=K<=2^24, "
-             "K%32==0; sampler: 1<=M<=65535, 1<=N<2^24)";
+      return "NVFP4_ERR_SHAPE: a size is out of range (GEMV and quantization: 1<=M<=128, N>=1, 32<=K<=2^24, "
+             "K%32==0, K<=131072 for dynamic per-token scales; sampler: 1<=M<=65535, 1<=N<2^24)";
     case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a pointer is not aligned (16 bytes; 4 for the sampler)";
     case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
     case NVFP4_ERR_DEVICE: return "NVFP4_ERR_DEVICE: the current device is not a gfx950";

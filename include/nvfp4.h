@@ -56,8 +56,9 @@ extern "C" {
 typedef enum {
   NVFP4_OK = 0,
   NVFP4_ERR_NULL = -1,      /* a required pointer is NULL                     */
-  NVFP4_ERR_SHAPE = -2,     /* M not in [1,8], N < 1, K outside [32, 2^24] or
-                               K % 32 != 0; with the LM-head epilogue also an
+  NVFP4_ERR_SHAPE = -2,     /* M not in [1,128], N < 1, K outside [32, 2^24]
+                               or K % 32 != 0 (K > 131072 for dynamic
+                               per-token scales); with the LM-head epilogue also an
                                N whose workspace would pass 2 GB (N beyond
                                about 10^8); sampler sizes out of range        */
   NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned (the
