@@ -80,6 +80,31 @@ def n_copies(args, c) -> int:
     return max(2, math.ceil(args.rotate_mb * 1e6 / weight_bytes(c.N, c.K)))
 
 
+# VALU issue peak of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+
+
+def valu_ops_per_element(variant: str, M: int) -> float:
+    """Estimated VALU operations per weight element of a GEMV variant, from
+    its decode and dot-product instruction counts: the E2M1 -> f16 decode
+    with the block-scale multiply (1 per element), the activation decode of
+    the MFMA kernels (shared by the R row tiles, once per 16-token column
+    tile), or the f16 dot2 work of the VALU kernels."""
+    kind = variant.split("_")[0]
+    f = {t[0]: int(t[1:]) for t in variant.split("_")[1:] if t[:1] in "mr" and t[1:].isdigit()}
+    mt, r = f.get("m", 8), f.get("r", 1)
+    ct = max(1, mt // 16)
+    if kind == "direct":
+        return 1.1 + 0.6 * M / r
+    if kind in ("staged", "valu"):
+        return 0.5 + 0.56 * M + (0.5 / r if kind == "staged" else 0.0)
+    if kind == "fmma":
+        return mt / 8 + 0.2
+    if kind == "lmfma":
+        return 1 + ct / r
+    return 1 + 1 / r  # dma, mfma
+
+
 def weight_bytes(N: int, K: int) -> int:
     """Algorithmic bytes of one GEMV: codes + E4M3 scales + global scale."""
     return N * K // 2 + N * K // 16 + 4
@@ -297,12 +322,16 @@ def main():
                 "gemv_us": round(gus, 3),
                 "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1),
                 "gemv_hbm_frac": round(wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                # estimated VALU issue utilisation (the secondary ceiling at larger M)
+                "valu_util_est": round(valu_ops_per_element(F.nvfp4_gemv_variant(M, c.N, c.K), M) * c.N * c.K
+                                       / (gus * 1e-6) / VALU_LANE_OPS_PER_S, 3),
                 "quant_us": round(qus, 3),
             })
             gemv_bytes += wb
             gemv_us += gus
             log(args, f"[kern] {c.name:18s} M={M} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s "
-                      f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us")
+                      f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s, VALU est "
+                      f"{detail[-1]['valu_util_est'] * 100:4.1f}%)  quant {qus:6.2f} us")
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
 
     extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4), "token_scales": token_scales}
