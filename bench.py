@@ -57,8 +57,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "cdddf94f97f5141e5560e047ad92dd13dbff0859e4eeca2a1e92c284b3a27774",
-    "bytes_per_step": 1108530446,
+    "sha256": "c08a3dbac0500ba65b89f26d10ac67042e04c6d2966e05183a6d216e595920fe",
+    "bytes_per_step": 1108297068,
 }
 
 

@@ -777,6 +777,14 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
   // wave w finalizes the (r, ct, v) register slots w, w + NW, ...; D layout:
   // lane (li, kg) holds rows 4*kg + v of each 16-row tile, token 16 ct + li
   constexpr int NV = (R * CT * 4 + NW - 1) / NW;
+  // each output's global scale, every load issued before the first store (a
+  // load between stores would wait for the stores before it)
+  float tsc[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int t = 16 * (((wave + u * NW) >> 2) % CT) + li;
+    tsc[u] = token_scale(p, t < M ? t : 0);
+  }
   float out[NV];
   int tok[NV], rowt[NV];
   bool ok[NV], own[NV];
@@ -793,7 +801,7 @@ __device__ __forceinline__ void mfma_finish(const GemvParams& p, const float4_t 
       float sum = 0.0f;
       for (int w = 0; w < NW; ++w) sum += red[((w * R * CT + rc) * 4 + v) * 64 + lane];
       const int64_t row = tile0 + 16 * r + 4 * kg + v;
-      out[u] = sum * token_scale(p, t < M ? t : 0);
+      out[u] = sum * tsc[u];
       tok[u] = t < MT ? t : 0;
       rowt[u] = 16 * r + 4 * kg + v;
       own[u] = t < M;
@@ -1754,6 +1762,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
   __syncthreads();
   constexpr int OUTS = 16 * R * MT;                     // (row, token) results of the tile
   constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);  // per thread
+  float tsc[NV];  // global scales, loaded before the first store
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int j = ((int)threadIdx.x + u * NW * 64) % MT;
+    tsc[u] = token_scale(p, j < M ? j : 0);
+  }
   float out[NV];
   int tok[NV], rowt[NV];
   bool ok[NV], own[NV];
@@ -1775,7 +1789,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
           for (int v = 0; v < 4; ++v)
             if ((4 * g + v) % MT == j) sum += red[((w * R + r) * 4 + v) * 64 + g * 16 + nn];
       const int64_t row = tile0 + rt;
-      out[u] = sum * token_scale(p, j < M ? j : 0);
+      out[u] = sum * tsc[u];
       tok[u] = j;
       rowt[u] = rt;
       own[u] = j < M;
