@@ -60,6 +60,7 @@ EXPORTED = (
     "nvfp4_gemv_smallm_token_scales",
     "nvfp4_gemv_variant",
     "nvfp4_gemv_variant_name",
+    "nvfp4_gemv_tune",
     "nvfp4_sample_top_p",
 )
 
@@ -120,6 +121,8 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_gemv_variant.argtypes = [c_int, i64, i64, c_int]
     L.nvfp4_gemv_variant_name.restype = ctypes.c_char_p
     L.nvfp4_gemv_variant_name.argtypes = [c_int]
+    L.nvfp4_gemv_tune.restype = c_int
+    L.nvfp4_gemv_tune.argtypes = [ctypes.c_char_p, c_int]
     L.nvfp4_gemv_smallm.restype = c_int
     L.nvfp4_gemv_smallm.argtypes = [c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(LmheadEpilogue), vp, sz, vp]
@@ -155,6 +158,34 @@ def _stream(stream) -> int | None:
     return int(stream.cuda_stream) or None
 
 
+def _require(t, name: str, dtype, device, shape=None, min_numel: int | None = None) -> None:
+    """Raise ValueError unless t is a contiguous tensor of dtype on device
+    (with the given shape / at least min_numel elements).  The C ABI sees
+    only pointers, so every size it relies on is checked here."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements, got {t.numel()}")
+
+
+def _require_ws(ws, need: int, device) -> None:
+    import torch
+
+    if ws is None:
+        return
+    _require(ws, "ws", torch.uint8, device)
+    if ws.numel() < need:
+        raise ValueError(f"ws holds {ws.numel()} bytes, {need} needed")
+
+
 @dataclass
 class NvFp4Tensor:
     """An NVFP4 matrix on the device: codes [rows][K/2], E4M3 scales
@@ -174,16 +205,42 @@ class NvFp4Tensor:
 
 
 _WS_SIZES: dict = {}
+_TUNING = (None, 1)  # (forced variant, balance) last set through nvfp4_gemv_tune
 
 
 def nvfp4_workspace_size(op: int, M: int, N: int, K: int) -> int:
-    # remembered per shape (and per forced kernel variant and row mapping,
-    # which can change it)
-    key = (op, M, N, K, os.environ.get("NVFP4_GEMV_VARIANT"), os.environ.get("NVFP4_GEMV_BALANCE"))
+    # remembered per shape and per tuning override (which can change it)
+    key = (op, M, N, K, _TUNING)
     n = _WS_SIZES.get(key)
     if n is None:
         n = _WS_SIZES[key] = int(lib().nvfp4_workspace_size(op, M, N, K))
     return n
+
+
+def nvfp4_gemv_tune(variant: str | None = None, balance: bool = True) -> None:
+    """Force a compiled GEMV variant for every shape it covers (None: the
+    launch table's choice) and choose the MFMA kernels' row mapping
+    (balance=False: whole tiles).  Process-wide; for tuning and tests."""
+    global _TUNING
+    name = None if variant is None else variant.encode()
+    _check(lib().nvfp4_gemv_tune(name, int(bool(balance))), "nvfp4_gemv_tune")
+    _TUNING = (variant, int(bool(balance)))
+
+
+class forced_variant:
+    """Context manager around nvfp4_gemv_tune that restores the launch table
+    on exit."""
+
+    def __init__(self, variant: str | None, balance: bool = True):
+        self.variant, self.balance = variant, balance
+
+    def __enter__(self):
+        nvfp4_gemv_tune(self.variant, self.balance)
+        return self
+
+    def __exit__(self, *exc):
+        nvfp4_gemv_tune(None, True)
+        return False
 
 
 def nvfp4_workspace_init(ws, stream=None) -> None:
@@ -205,14 +262,21 @@ def nvfp4_pack_weights(w, ws=None, out: NvFp4Tensor | None = None, stream=None) 
     """Pack W fp32 [N][K] (device, contiguous) into NVFP4."""
     import torch
 
+    if w.dim() != 2:
+        raise ValueError("w must be [N][K]")
     N, K = int(w.shape[0]), int(w.shape[1])
+    _require(w, "w", torch.float32, w.device)
     if out is None:
         out = NvFp4Tensor(torch.empty((N, K // 2), dtype=torch.uint8, device=w.device),
                           torch.empty((N, K // 16), dtype=torch.uint8, device=w.device),
                           torch.empty(1, dtype=torch.float32, device=w.device))
+    _require(out.codes, "out.codes", torch.uint8, w.device, (N, K // 2))
+    _require(out.scales, "out.scales", torch.uint8, w.device, (N, K // 16))
+    _require(out.gscale, "out.gscale", torch.float32, w.device, min_numel=1)
     need = nvfp4_workspace_size(NVFP4_OP_PACK, 0, N, K)
     if ws is None:
         ws = new_workspace(need, w.device, stream)
+    _require_ws(ws, need, w.device)
     _check(lib().nvfp4_pack_weights(_ptr(w), N, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
                                     _ptr(ws), ws.numel(), _stream(stream)), "nvfp4_pack_weights")
     return out
@@ -226,19 +290,31 @@ def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, 
     row (out.gscale [M]) instead of one for the tensor ([1])."""
     import torch
 
+    if x.dim() != 2:
+        raise ValueError("x must be [M][K]")
     M, K = int(x.shape[0]), int(x.shape[1])
+    dev = x.device
+    _require(x, "x", torch.bfloat16, dev)
+    ng = M if per_token else 1
+    if gscale is not None:
+        _require(gscale, "gscale", torch.float32, dev, min_numel=ng)
     if per_token:
         flags = NVFP4_GS_TOKEN_DYNAMIC if gscale is None else NVFP4_GS_TOKEN_STATIC
     else:
         flags = NVFP4_GS_DYNAMIC if gscale is None else NVFP4_GS_STATIC
     if out is None:
-        out = NvFp4Tensor(torch.empty((M, K // 2), dtype=torch.uint8, device=x.device),
-                          torch.empty((M, K // 16), dtype=torch.uint8, device=x.device),
-                          gscale if gscale is not None else
-                          torch.empty(M if per_token else 1, dtype=torch.float32, device=x.device))
+        out = NvFp4Tensor(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+                          gscale if gscale is not None else torch.empty(ng, dtype=torch.float32, device=dev))
+    _require(out.codes, "out.codes", torch.uint8, dev, (M, K // 2))
+    _require(out.scales, "out.scales", torch.uint8, dev, (M, K // 16))
+    _require(out.gscale, "out.gscale", torch.float32, dev, min_numel=ng)
+    if gscale is not None and out.gscale.data_ptr() != gscale.data_ptr():
+        raise ValueError("a static gscale must be out.gscale")
     need = 0 if per_token else nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K)
     if need and ws is None:
-        ws = new_workspace(need, x.device, stream)
+        ws = new_workspace(need, dev, stream)
+    _require_ws(ws, need, dev)
     _check(lib().nvfp4_quantize_act(_ptr(x), M, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
                                     flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "nvfp4_quantize_act")
@@ -251,7 +327,7 @@ def nvfp4_gemv_variant(M: int, N: int, K: int, lmhead: bool = False) -> str:
 
 
 def nvfp4_gemv_variant_names() -> list[str]:
-    """Every compiled GEMV kernel variant (names usable in NVFP4_GEMV_VARIANT)."""
+    """Every compiled GEMV kernel variant (names usable in nvfp4_gemv_tune)."""
     out, i = [], 0
     while True:
         n = lib().nvfp4_gemv_variant_name(i)
@@ -267,9 +343,12 @@ def variant_tokens(name: str) -> int:
 
 
 def variant_k_multiple(name: str) -> int:
-    """K granularity a variant needs: the direct-to-LDS kernels (``dma_*``,
-    ``staged_*``, ``fmma_*``) copy whole 256-element steps, every other kernel
-    32-element chunks."""
+    """K granularity a variant needs: the streaming kernels (``stream_*``,
+    ``fstream_*``) stream whole 512-element chunks, the direct-to-LDS kernels
+    (``dma_*``, ``staged_*``, ``fmma_*``) copy whole 256-element steps, every
+    other kernel 32-element chunks."""
+    if name.startswith(("stream_", "fstream_")):
+        return 512
     return 256 if name.startswith(("dma_", "staged_", "fmma_")) else 32
 
 
@@ -314,20 +393,45 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
                       M: int | None = None, stream=None):
     """y [M][N] fp32 = dequant(a) . dequant(w)^T.  ``ws``: a zero-filled
     workspace of at least nvfp4_workspace_size(...) bytes (allocated here
-    when needed and not given)."""
+    when needed and not given).  ``M`` (default: a's rows) may use only the
+    first rows of ``a``.  An activation with one global scale per row goes
+    to the per-token entry point."""
     import torch
 
-    M = a.rows if M is None else M
+    dev = w.codes.device
+    for name, t in (("a.codes", a.codes), ("a.scales", a.scales), ("w.codes", w.codes), ("w.scales", w.scales)):
+        _require(t, name, torch.uint8, dev)
+        if t.dim() != 2:
+            raise ValueError(f"{name} must be 2-D")
     N, K = w.rows, w.K
+    if a.K != K:
+        raise ValueError(f"activation K {a.K} != weight K {K}")
+    M = a.rows if M is None else int(M)
+    if not 1 <= M <= a.rows:
+        raise ValueError(f"M must be in [1, {a.rows}], got {M}")
+    _require(a.scales, "a.scales", torch.uint8, dev, (a.rows, K // 16))
+    _require(w.scales, "w.scales", torch.uint8, dev, (N, K // 16))
+    _require(w.gscale, "w.gscale", torch.float32, dev, min_numel=1)
+    _require(a.gscale, "a.gscale", torch.float32, dev, min_numel=1)
+    per_token = a.gscale.numel() > 1
+    if per_token and a.gscale.numel() < M:
+        raise ValueError(f"per-token a.gscale holds {a.gscale.numel()} scales, {M} needed")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=w.codes.device)
-    ce = None if epi is None else epi.as_c()
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    _require(y, "y", torch.float32, dev, (M, N))
+    ce = None
+    if epi is not None:
+        _require(epi.step_start, "epi.step_start", torch.uint8, dev, min_numel=M)
+        _require(epi.state, "epi.state", torch.uint8, dev, min_numel=M * nvfp4_reset_state_size(epi.window))
+        _require(epi.entropy, "epi.entropy", torch.float32, dev, min_numel=M)
+        _require(epi.temperature, "epi.temperature", torch.float32, dev, min_numel=M)
+        ce = epi.as_c()
     need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD if epi is not None else NVFP4_OP_GEMV, M, N, K)
     if need and ws is None:
-        ws = new_workspace(need, w.codes.device, stream)
+        ws = new_workspace(need, dev, stream)
+    _require_ws(ws, need, dev)
     ws_bytes = 0 if ws is None else ws.numel()
-    # an activation with one global scale per row goes to the per-token entry point
-    fn = lib().nvfp4_gemv_smallm_token_scales if a.gscale.numel() > 1 else lib().nvfp4_gemv_smallm
+    fn = lib().nvfp4_gemv_smallm_token_scales if per_token else lib().nvfp4_gemv_smallm
     _check(fn(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale), _ptr(w.codes), _ptr(w.scales),
               _ptr(w.gscale), _ptr(y), None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,
               _stream(stream)), "nvfp4_gemv_smallm")

@@ -1,7 +1,12 @@
-"""Compile the HIP library ``lib/libnvfp4.so`` for gfx950 with hipcc.
+"""Compile the HIP libraries for gfx950 with hipcc.
 
-Every source in ``csrc/`` is compiled to an object under ``_build/`` and
-linked into one shared library.  Flags:
+* ``lib/libnvfp4.so``: the decode-projection library (every source in
+  ``csrc/``), the C ABI of ``include/nvfp4.h``;
+* ``lib/libnvfp4_probe.so``: the measurement and test probes of
+  ``csrc/probe/`` (``include/nvfp4_probe.h``), which the projection library
+  never calls.
+
+Each source is compiled to an object under ``_build/``.  Flags:
 
 * ``--offload-arch=gfx950`` only (no other targets, no CUDA);
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops`` keeps the compiler
@@ -26,10 +31,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libnvfp4.so")
+PROBE_LIB = os.path.join(LIBDIR, "libnvfp4_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 
 SOURCES = ["nvfp4_abi.cpp", "nvfp4_quant.hip", "nvfp4_gemv.hip", "nvfp4_sample.hip"]
+PROBE_SOURCES = ["probe/nvfp4_probe.hip"]
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950",
@@ -52,7 +59,7 @@ def hipcc() -> str:
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    obj = os.path.join(BUILD_DIR, src.replace("/", "_") + ".o")
     cmd = [hipcc(), *COMMON_FLAGS, "-I", INCLUDE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -66,20 +73,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``lib/libnvfp4.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``lib/libnvfp4.so`` and
+    ``lib/libnvfp4_probe.so``; returns the projection library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 4)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB, verbose)
     return LIB
 
 

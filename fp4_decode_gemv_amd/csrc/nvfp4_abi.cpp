@@ -66,7 +66,8 @@ const char* nvfp4_status_str(int status) {
     case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
     case NVFP4_ERR_SHAPE:
       return "NVFP4_ERR_SHAPE: a size is out of range (GEMV and quantization: 1<=M<=128, N>=1, 32<=K<=2^24, "
-             "K%32==0, K<=131072 for dynamic per-token scales; sampler: 1<=M<=65535, 1<=N<2^24)";
+             "K%32==0, K<=131072 for dynamic per-token scales, M*K<2^30 for a per-tensor scale; sampler: "
+             "1<=M<=65535, 1<=N<2^24)";
     case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: a pointer is not aligned (16 bytes; 4 for the sampler)";
     case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
     case NVFP4_ERR_DEVICE: return "NVFP4_ERR_DEVICE: the current device is not a gfx950";
@@ -137,6 +138,9 @@ int nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K, uint8_t* codes,
   if (flags == NVFP4_GS_TOKEN_DYNAMIC && K > kTokenScaleMaxK) return NVFP4_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
   const int64_t elems = (int64_t)M * K;
+  // the quantizer addresses a tensor (per-tensor scale) or a row (per-token)
+  // through a buffer of 2-byte elements with 32-bit byte offsets
+  if (!per_token && elems >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
   const bool two = flags == NVFP4_GS_DYNAMIC && elems > kActSelfAmaxMaxElems;
   const size_t need = quant_ws_bytes(elems, two);
   if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
@@ -259,6 +263,11 @@ const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead) {
 }
 
 const char* nvfp4_gemv_variant_name(int index) { return gemv_variant_by_index(index); }
+
+int nvfp4_gemv_tune(const char* variant, int balance) {
+  if (balance != 0 && balance != 1) return NVFP4_ERR_ARG;
+  return set_gemv_tuning(variant, balance) == 0 ? NVFP4_OK : NVFP4_ERR_ARG;
+}
 
 int nvfp4_sample_top_p(int M, int64_t N, const float* logits, const float* temperature, float top_p,
                        const float* uniforms, int32_t* tokens, int32_t* nucleus, void* ws, size_t ws_bytes,

@@ -70,6 +70,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
@@ -1800,6 +1802,360 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
   if constexpr (EPI) lmhead_partials<MT, 16 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
 }
 
+// ----------------------------------------------------------------------------
+// Streaming MFMA kernels: weights straight from HBM into MFMA operands
+// ----------------------------------------------------------------------------
+// Both kernels below load the weight codes straight into the register
+// operand of an MFMA, with no LDS staging, barrier or transpose in the loop.
+// The 16 weight-side rows of the MFMA tile are 4 weight rows x 4 windows of
+// K: weight lane (j, kg), j = lane % 16, kg = lane / 16, holds row j / 4 of
+// the row group, window w = j % 4: the 16 bytes (32 codes) at byte
+// 64 kg + 16 w of the row's 256-byte chunk (512 elements).  So the four
+// lanes of a quad read 64 contiguous bytes of one row and a wave instruction
+// reads 4 rows x 256 bytes: the address unit sees whole 64-byte quads.  (A
+// row per column of the tile puts every lane of a quad on another cache line;
+// that stalls the address unit four times as often and costs more than the
+// arithmetic does.)  A window is the 4 pieces of 16 bytes with the same w;
+// the activation side takes the same pieces, the MFMA sums over k, and only
+// the results whose two sides share a window are used: lane l holds them as
+// its accumulator entry l % 4.
+// Before the loop every workgroup copies the activation codes and scales and
+// its rows' block scales into LDS with direct-to-LDS loads of whole
+// contiguous kilobytes, so the loop's only memory instructions are the
+// weight-code loads (small scattered scale loads next to the code stream
+// cost more HBM time than they carry).  Each wave keeps U chunks of loads in
+// flight in a register ring (non-temporal loads) over R row groups of 4
+// rows; waves split the chunks of K and the finish adds the waves' results
+// in a fixed order.  Rows past the workgroup's rows get a per-lane offset
+// outside the buffer and read as zeros; the chunk offset is a scalar operand
+// (not range-checked), which only ever addresses bytes inside the rows.
+constexpr int kStreamChunk = 512;          // K elements per chunk and row
+constexpr uint32_t kOffOut = 0x80000000u;  // beyond any buffer resource used here
+
+// 32 codes (one 16-byte word) times two block scales (16 elements each) ->
+// four f16 operands of 8 elements
+__device__ __forceinline__ void decode32_scaled(const u32x4_t& v, uint32_t s2, half8_t (&out)[4]) {
+  const float2_t s = __builtin_amdgcn_cvt_pk_f32_fp8(s2, false);
+  const half2_t h0 = as_half2(pack_f16x2(s[0], s[0])), h1 = as_half2(pack_f16x2(s[1], s[1]));
+  out[0] = wdecode8_scaled(v[0], h0);
+  out[1] = wdecode8_scaled(v[1], h0);
+  out[2] = wdecode8_scaled(v[2], h1);
+  out[3] = wdecode8_scaled(v[3], h1);
+}
+
+// LDS the streaming kernels stage: activation codes [T][K/2] and scales
+// [T][K/16] for T tokens, the tile's block scales [tile_rows][K/16]
+__host__ __device__ constexpr int64_t stream_lds_bytes(int T, int64_t K, int64_t tile_rows) {
+  return pad1k(T * (K / 2)) + pad1k(T * (K / 16)) + pad1k(tile_rows * (K / 16));
+}
+
+// Copies the activation (rows >= M are never read for a stored result) and
+// the tile's block scales into LDS; returns the LDS offsets of the three
+// regions through acb / asb (activation scales at acb, block scales at
+// acb + asb).
+template <int NW>
+__device__ __forceinline__ void stream_stage(const GemvParams& p, int T, int64_t rows, int64_t tile0, int wave,
+                                             int lane, int64_t& acb, int64_t& asb) {
+  const int64_t K = p.K;
+  const int M = p.M;
+  acb = pad1k(T * (K / 2));
+  asb = pad1k(T * (K / 16));
+  extern __shared__ uint4 lds4[];
+  const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+  stage_to_lds<NW>(raw_rsrc(p.a_codes, (int64_t)M * (K / 2)), l0, (int64_t)M * (K / 2), wave, lane);
+  stage_to_lds<NW>(raw_rsrc(p.a_scales, (int64_t)M * (K / 16)), l0 + (uint32_t)acb, (int64_t)M * (K / 16), wave, lane);
+  stage_to_lds<NW>(raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16)), l0 + (uint32_t)(acb + asb),
+                   rows * (K / 16), wave, lane);
+}
+
+// (a) f16 form, M <= MT (MT = 4 or 8), K % 512 == 0.  The token side of an
+// MFMA is 4 tokens x the 4 windows (token lane (i, kg): token i / 4 of the
+// set, window i % 4, the same 32 elements of the token's codes); MT = 8 runs
+// two sets of tokens against each decoded weight operand.  Both sides are
+// decoded to exact f16 values E2M1 * E4M3 (at most 6 significant bits) and
+// v_mfma_f32_16x16x32_f16 adds the products: D[4 wr + w][4 t + w] is row wr
+// with token t over window w.  Tokens >= M read as zeros.
+template <int MT, int R, int NW, int U, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
+  static_assert(MT == 4 || MT == 8, "token sets of 4");
+  constexpr int S = MT / 4;  // token sets
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, kg = lane >> 4;
+  const int jr = j >> 2, jw = j & 3;  // row (weight side) / token (token side), window
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
+  const int nchunks = (int)(K / kStreamChunk);
+  const int n = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;  // chunks wave, wave + NW, ...
+
+  int64_t acb, asb;
+  stream_stage<NW>(p, MT, rows, tile0, wave, lane, acb, asb);
+  const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const int b0 = 64 * kg + 16 * jw;  // byte of this lane within a row's chunk
+  uint32_t vw[R];
+  const char* lds = reinterpret_cast<const char*>(lds4);
+  const char* lsw[R];  // block scales of each row group's row (+ 32 c); rows past the tile read the last row's
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = 4 * r + jr;
+    vw[r] = row < rows ? (uint32_t)(row * (int)(K / 2) + b0) : kOffOut;
+    lsw[r] = lds + acb + asb + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;
+  }
+  bool tin[S];
+  const char* la[S];
+  const char* lsa[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int t = 4 * s + jr;
+    tin[s] = t < M;
+    la[s] = lds + (t < M ? t : 0) * (K / 2) + b0;                   // + 256 c
+    lsa[s] = lds + acb + (t < M ? t : 0) * (K / 16) + b0 / 8;       // + 32 c
+  }
+
+  float4_t acc[R][S];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc[r][s] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4_t ring[U][R];
+  auto load = [&](int u, int i) {  // the wave's i-th chunk into slot u; past the last, the last again (never used)
+    const int c = wave + (i < n ? i : n - 1) * NW;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+  };
+  if (n > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<(U * R < 63 ? U * R : 63)>();  // this wave's staging copies (issued first) have landed ...
+  asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
+  if (n > 0) {
+    for (int i0 = 0; i0 < n; i0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u;
+        const int c = wave + (i < n ? i : n - 1) * NW;
+        u32x4_t w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[r] = ring[u][r];
+        load(u, i + U);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < n) {
+          half8_t b[S][4];
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            const uint4 a4 = *reinterpret_cast<const uint4*>(la[s] + 256 * c);
+            const u32x4_t av = tin[s] ? u32x4_t{a4.x, a4.y, a4.z, a4.w} : u32x4_t{0u, 0u, 0u, 0u};
+            const uint32_t as = tin[s] ? *reinterpret_cast<const uint16_t*>(lsa[s] + 32 * c) : 0u;
+            decode32_scaled(av, as, b[s]);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            half8_t a[4];
+            decode32_scaled(w[r], *reinterpret_cast<const uint16_t*>(lsw[r] + 32 * c), a);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int s = 0; s < S; ++s)
+                acc[r][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[s][q], acc[r][s], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // finish: lane l's entry l % 4 holds row 4 r + l / 16 with token (l % 16) / 4
+  // of set s over window l % 4; output (t, row) = the sum over waves and the
+  // four windows (lanes 16 (row % 4) + 4 (t % 4) + w, entry w)
+  __syncthreads();  // every wave is done with the staged data before the reduction reuses the LDS
+  float* red = reinterpret_cast<float*>(lds4);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < S; ++s) red[((wave * R + r) * S + s) * 64 + lane] = acc[r][s][lane & 3];
+  __syncthreads();
+  constexpr int OUTS = 4 * R * MT;
+  constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);
+  float tsc[NV];  // global scales, all loaded before the first store
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int t = ((int)threadIdx.x + u * NW * 64) / (4 * R);
+    tsc[u] = token_scale(p, t < M ? t : 0);
+  }
+  float out[NV];
+  int tok[NV], rowt[NV];
+  bool ok[NV], own[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int o = (int)threadIdx.x + u * NW * 64;
+    out[u] = 0.0f;
+    tok[u] = 0;
+    rowt[u] = 0;
+    ok[u] = own[u] = false;
+    if (o < OUTS) {
+      const int rt = o % (4 * R), t = o / (4 * R);  // consecutive threads: consecutive rows
+      const int r = rt >> 2, wr = rt & 3, s = t >> 2, tt = t & 3;
+      float sum = 0.0f;
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) sum += red[((w * R + r) * S + s) * 64 + 16 * wr + 4 * tt + ww];
+      out[u] = sum * tsc[u];
+      tok[u] = t;
+      rowt[u] = rt;
+      own[u] = t < M;
+      ok[u] = t < M && rt < rows;
+      if (ok[u]) p.y[(int64_t)t * N + tile0 + rt] = out[u];
+    }
+  }
+  if constexpr (EPI) lmhead_partials<MT, 4 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
+}
+
+// (b) FP4 form, M = 1, K % 512 == 0.  The weight codes go into
+// v_mfma_scale_f32_16x16x128_f8f6f4 as they are (E2M1 x E2M1 products are
+// exact, its E8M0 scales stay 1), so no weight element is decoded.  NVFP4's
+// E4M3 scales cover 16 elements, so every used result must hold a single
+// 16-element block: the activation side is block-diagonal.  A lane's 32
+// elements are two blocks (its low and high 8 bytes); activation row
+// i = 4 b + w holds window w and, in the chunk's MFMA s (s = 0, 1), only
+// half s of k-group b, so D[4 b + w][4 wr + w] is the exact block sum of row
+// wr over the block 8 b + 2 w + s of the chunk (bytes 64 b + 16 w + 8 s).
+// Lane l's used entry l % 4 is scaled by its two E4M3 block scales and added
+// up in f32: about 12 vector operations per 16 bytes of codes per lane,
+// against about 36 for decoding them to f16.
+template <int R, int NW, int U, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_fstream_kernel(GemvParams p) {
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, kg = lane >> 4;
+  const int jr = j >> 2, jw = j & 3;
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
+  const int nchunks = (int)(K / kStreamChunk);
+  const int n = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;
+
+  int64_t acb, asb;
+  stream_stage<NW>(p, 1, rows, tile0, wave, lane, acb, asb);
+  const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const int b0 = 64 * kg + 16 * jw;
+  // this lane's used result: row jr, window jw, blocks 8 kg + 2 jw + s (the
+  // same byte offset as its own weight codes, b0 / 8 + s)
+  const char* lds = reinterpret_cast<const char*>(lds4);
+  uint32_t vw[R];
+  const char* lsw[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = 4 * r + jr;
+    vw[r] = row < rows ? (uint32_t)(row * (int)(K / 2) + b0) : kOffOut;
+    lsw[r] = lds + acb + asb + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;  // + 32 c
+  }
+  // activation side of this lane (A row j = 4 b + w, b = jr, w = jw): the
+  // token's codes at b0 (+ 256 c), kept in MFMA s only if kg == b
+  const char* la = lds + b0;
+  const char* lsa = lds + acb + b0 / 8;  // + 32 c: the two block scales of the used result
+  const uint32_t keep = kg == jr ? ~0u : 0u;
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4_t ring[U][R];
+  auto load = [&](int u, int i) {
+    const int c = wave + (i < n ? i : n - 1) * NW;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+  };
+  if (n > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmcnt<(U * R < 63 ? U * R : 63)>();  // this wave's staging copies (issued first) have landed ...
+  asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
+  if (n > 0) {
+    for (int i0 = 0; i0 < n; i0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u;
+        const int c = wave + (i < n ? i : n - 1) * NW;
+        u32x4_t w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[r] = ring[u][r];
+        load(u, i + U);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < n) {
+          const uint4 av = *reinterpret_cast<const uint4*>(la + 256 * c);
+          const float2_t sa = __builtin_amdgcn_cvt_pk_f32_fp8(*reinterpret_cast<const uint16_t*>(lsa + 32 * c), false);
+          const uint4 A0 = make_uint4(av.x & keep, av.y & keep, 0u, 0u);
+          const uint4 A1 = make_uint4(0u, 0u, av.z & keep, av.w & keep);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const float2_t sw =
+                __builtin_amdgcn_cvt_pk_f32_fp8(*reinterpret_cast<const uint16_t*>(lsw[r] + 32 * c), false);
+            const uint4 B = make_uint4(w[r][0], w[r][1], w[r][2], w[r][3]);
+            const float4_t d0 = mfma_fp4(A0, B), d1 = mfma_fp4(A1, B);
+            const float f0 = sw[0] * sa[0], f1 = sw[1] * sa[1];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[r][v] = __builtin_fmaf(d1[v], f1, __builtin_fmaf(d0[v], f0, acc[r][v]));
+          }
+        }
+      }
+    }
+  }
+
+  // finish: output row 4 r + wr = the sum over waves and the 16 lanes
+  // 16 b + 4 wr + w (entry w) holding its windows and block groups
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds4);
+#pragma unroll
+  for (int r = 0; r < R; ++r) red[(wave * R + r) * 64 + lane] = acc[r][lane & 3];
+  __syncthreads();
+  constexpr int OUTS = 4 * R;
+  constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);
+  const float tsc = token_scale(p, 0);
+  float out[NV];
+  int tok[NV], rowt[NV];
+  bool ok[NV], own[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int o = (int)threadIdx.x + u * NW * 64;
+    out[u] = 0.0f;
+    tok[u] = 0;
+    rowt[u] = 0;
+    ok[u] = own[u] = false;
+    if (o < OUTS) {
+      const int r = o >> 2, wr = o & 3;
+      float sum = 0.0f;
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int ww = 0; ww < 4; ++ww) sum += red[(w * R + r) * 64 + 16 * b + 4 * wr + ww];
+      out[u] = sum * tsc;
+      rowt[u] = o;
+      own[u] = true;
+      ok[u] = o < rows;
+      if (ok[u]) p.y[tile0 + o] = out[u];
+    }
+  }
+  if constexpr (EPI) lmhead_partials<1, 4 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
+}
+
 __global__ void reset_state_init_kernel(char* state, int M, int window, size_t sbytes) {
   const int m = blockIdx.x;
   if (m >= M) return;
@@ -1819,7 +2175,7 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8 };
+enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8, STREAM = 9, FSTREAM = 10 };
 
 struct Variant {
   const char* name;
@@ -1827,7 +2183,7 @@ struct Variant {
   int mt, g, r, nw, p;
   void (*plain)(GemvParams);
   void (*epi)(GemvParams);
-  void (*plain_k64)(GemvParams);  // LDS-staged kernel only: K % 64 == 0 instantiations
+  void (*plain_k64)(GemvParams);  // register-staged MFMA kernel: K % 64 == 0 instantiations
   void (*epi_k64)(GemvParams);
 };
 
@@ -1884,44 +2240,38 @@ struct Variant {
         gemv_dma_kernel<MT, R, NW, D, true, false>, gemv_dma_kernel<MT, R, NW, D, true, true> \
   }
 
+#define STREAM_V(MT, R, NW, U)                                                              \
+  Variant {                                                                               \
+    "stream_m" #MT "_r" #R "_w" #NW "_u" #U, STREAM, MT, 16, R, NW, U,                       \
+        gemv_stream_kernel<MT, R, NW, U, false>, gemv_stream_kernel<MT, R, NW, U, true>     \
+  }
+#define FSTREAM_V(R, NW, U)                                                                 \
+  Variant {                                                                               \
+    "fstream_m1_r" #R "_w" #NW "_u" #U, FSTREAM, 1, 16, R, NW, U,                            \
+        gemv_fstream_kernel<R, NW, U, false>, gemv_fstream_kernel<R, NW, U, true>           \
+  }
+
+// The launch table's variants and the fallbacks it uses where a choice does
+// not fit a shape (LDS size, K granularity, 32-bit buffer offsets).  Further
+// instantiations for sweeps can be compiled in by defining
+// NVFP4_GEMV_EXTRA_VARIANTS as a list of the *_V initialisers above.
 const Variant kVariants[] = {
-    // direct VALU (no LDS), one and two tokens; _nt: non-temporal weight loads
-    DIRECT_V(1, 16, 1, 4, 1), DIRECT_V(1, 32, 1, 4, 1), DIRECT_V(1, 32, 2, 4, 1), DIRECT_V(1, 64, 1, 4, 1),
-    DIRECT_V(2, 32, 1, 4, 1), DIRECT_V(2, 64, 1, 4, 1), DIRECT_V(1, 32, 1, 4, 2),
-    DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), DIRECT_NT_V(1, 64, 1, 4, 1),
-    DIRECT_NT_V(2, 32, 1, 4, 1), DIRECT_NT_V(2, 64, 1, 4, 1),
-    // LDS VALU, any M (the pages' CUDA-core design)
-    VALU_V(1, 16, 2, 4, 1), VALU_V(8, 16, 2, 4, 1),
-    // MFMA straight from registers (also the fallback past 32-bit buffer offsets)
-    MFMA_V(4, 2, 8, 1), MFMA_V(8, 1, 4, 1), MFMA_V(8, 2, 8, 1),
-    // LDS-staged MFMA
-    LMFMA_V(2, 2, 4, 1), LMFMA_V(4, 2, 4, 1), LMFMA_V(4, 2, 8, 1), LMFMA_V(8, 1, 4, 1), LMFMA_V(8, 1, 8, 1),
-    LMFMA_V(8, 2, 4, 1), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 2),
-    // ... for 9..16 tokens (every column of the 16-token MFMA tile in use)
-    LMFMA_V(16, 1, 4, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(16, 1, 8, 1), LMFMA_V(16, 2, 8, 1),
-    // ... for 17..32, 33..64 and 65..128 tokens (2, 4 or 8 16-token column
-    // tiles per decoded weight operand)
-    LMFMA_V(32, 1, 4, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(32, 1, 8, 1), LMFMA_V(32, 2, 8, 1),
-    LMFMA_V(64, 1, 4, 1), LMFMA_V(64, 2, 4, 1), LMFMA_V(64, 1, 8, 1), LMFMA_V(64, 2, 8, 1),
-    LMFMA_V(128, 1, 4, 1), LMFMA_V(128, 2, 4, 1), LMFMA_V(128, 1, 2, 1),
-    // direct-to-LDS MFMA (K % 256 == 0)
-    DMA_V(2, 2, 4, 3), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3), DMA_V(8, 2, 8, 2), DMA_V(8, 1, 8, 2),
-    DMA_V(8, 1, 4, 3), DMA_V(8, 1, 4, 4), DMA_V(8, 2, 4, 4),
-    // direct-to-LDS MFMA, activation and the tile's weight scales staged once (K % 256 == 0)
-    DMA_SA_V(4, 2, 4, 3), DMA_SA_V(4, 2, 4, 2), DMA_SA_V(4, 1, 4, 3), DMA_SA_V(8, 2, 4, 3), DMA_SA_V(8, 2, 4, 2),
-    DMA_SA_V(8, 1, 4, 3), DMA_SA_V(8, 1, 4, 4), DMA_SA_V(8, 1, 8, 2), DMA_SA_V(8, 2, 8, 2), DMA_SA_V(8, 1, 4, 2),
-    // LDS-staged VALU (K % 256 == 0)
-    STAGED_V(1, 32, 1, 4, 1), STAGED_V(1, 32, 2, 4, 1), STAGED_V(1, 64, 1, 4, 1), STAGED_V(1, 32, 1, 4, 2),
-    STAGED_V(1, 32, 2, 4, 2), STAGED_V(1, 64, 1, 4, 2), STAGED_V(1, 64, 2, 4, 1), STAGED_V(1, 32, 4, 4, 1),
-    STAGED_V(1, 32, 2, 8, 1), STAGED_V(1, 64, 1, 8, 2), STAGED_V(2, 32, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
-    STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 64, 1, 4, 2),
-    // FP4 MFMA on raw weight codes (K % 256 == 0)
-    FMMA_V(2, 2, 4, 3), FMMA_V(2, 1, 4, 3), FMMA_V(2, 2, 8, 2), FMMA_V(2, 1, 8, 2), FMMA_V(2, 2, 4, 2),
-    FMMA_V(4, 2, 4, 3), FMMA_V(4, 1, 4, 3), FMMA_V(4, 2, 8, 2), FMMA_V(4, 1, 8, 2), FMMA_V(4, 2, 4, 2),
-    FMMA_V(8, 2, 4, 3), FMMA_V(8, 1, 8, 2),
-    FMMA_SA_V(2, 2, 4, 3), FMMA_SA_V(2, 1, 4, 3), FMMA_SA_V(2, 1, 4, 4), FMMA_SA_V(2, 2, 4, 2),
-    FMMA_SA_V(4, 2, 4, 3), FMMA_SA_V(4, 1, 4, 3), FMMA_SA_V(4, 1, 4, 4), FMMA_SA_V(4, 2, 4, 2),
-    FMMA_SA_V(8, 2, 4, 2), FMMA_SA_V(8, 1, 4, 3), FMMA_SA_V(8, 1, 8, 2), FMMA_SA_V(8, 2, 4, 3),
+    // one token
+    DIRECT_NT_V(1, 64, 1, 4, 1), DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), STAGED_V(1, 32, 1, 4, 2),
+    // two tokens
+    FMMA_SA_V(2, 1, 4, 3), STAGED_V(2, 64, 1, 4, 2), STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
+    // 3..8 tokens
+    STREAM_V(4, 5, 4, 2), STREAM_V(8, 5, 4, 2), DMA_V(4, 2, 4, 3), DMA_SA_V(8, 2, 4, 2), DMA_V(8, 2, 4, 3),
+    FMMA_V(4, 2, 4, 3), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 1),
+    // 9..128 tokens
+    LMFMA_V(16, 2, 8, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(32, 2, 8, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(64, 2, 8, 1),
+    LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1),
+    // fallbacks
+    DIRECT_V(2, 64, 1, 4, 1), MFMA_V(4, 2, 8, 1), MFMA_V(8, 2, 8, 1), LMFMA_V(16, 1, 4, 1), LMFMA_V(32, 1, 4, 1),
+    LMFMA_V(64, 1, 4, 1), LMFMA_V(128, 1, 4, 1),
+#ifdef NVFP4_GEMV_EXTRA_VARIANTS
+    NVFP4_GEMV_EXTRA_VARIANTS
+#endif
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1933,6 +2283,51 @@ int find_variant(const char* name) {
   for (int i = 0; i < kNumVariants; ++i)
     if (strcmp(kVariants[i].name, name) == 0) return i;
   return -1;
+}
+
+// Tuning override (nvfp4_gemv_tune): a forced variant index (-1 = none) and
+// the row mapping of the MFMA tile kernels (1 = rows dealt out evenly where
+// whole tiles would leave CUs idle, 0 = whole tiles).  Process-wide.
+std::atomic<int> g_forced_variant{-1};
+std::atomic<int> g_balance{1};
+
+// Rows per workgroup of the MFMA tile kernels.  A workgroup streams its rows
+// at a rate set by the loads it keeps in flight, so a grid of N / (16 R)
+// workgroups that leaves CUs idle (N = 5120: 160 or 320 tiles on 256 CUs)
+// runs at the speed of the busiest CU.  When the tiles fill the CUs at most
+// twice over, the rows are instead dealt out evenly: ceil(N / (256 k))
+// rows per workgroup for the smallest k that fits a 16 R-row tile, so that
+// every CU streams the same number of rows.  The tuning override
+// (nvfp4_gemv_tune) can keep whole tiles instead, for timing comparisons.
+constexpr int64_t kComputeUnits = 256;  // MI355X
+
+int64_t tile_rows_for(int64_t N, int64_t tile) {
+  if (g_balance.load(std::memory_order_relaxed) == 0) return tile;
+  const int64_t k = (N + tile * kComputeUnits - 1) / (tile * kComputeUnits);
+  if (k > 2) return tile;
+  const int64_t rows = (N + kComputeUnits * k - 1) / (kComputeUnits * k);
+  return rows < tile ? rows : tile;
+}
+
+constexpr int64_t kLdsBytes = 163840;  // LDS per workgroup (gfx950)
+
+// Rows of the tile a kernel's LM-head partials cover (the ROWS of its
+// lmhead_partials instantiation)
+int64_t epi_tile_rows(const Variant& v) {
+  switch (v.kind) {
+    case STREAM:
+    case FSTREAM: return 4 * v.r;
+    case VALU:
+    case DIRECT:
+    case STAGED: return (int64_t)v.r * v.nw * (64 / v.g);
+    default: return 16 * v.r;
+  }
+}
+
+// LDS a streaming kernel stages: activation and block scales (the FP4 form
+// for its 1 or 2 tokens, the f16 form for 8)
+int64_t stream_kernel_lds(const Variant& v, int64_t K, int64_t tile_rows) {
+  return stream_lds_bytes(v.kind == FSTREAM ? 1 : v.mt, K, tile_rows);
 }
 
 // LDS of the direct-to-LDS kernels with staged activation (f16 and FP4
@@ -1960,13 +2355,25 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   (void)epi;
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
-  auto fmma_sa = [&](int i, int otherwise) { return sa_lds_bytes(kVariants[i], K) <= 163840 ? i : otherwise; };
+  auto fmma_sa = [&](int i, int otherwise) {
+    return sa_lds_bytes(kVariants[i], K) + (epi ? 4 * kVariants[i].mt * epi_tile_rows(kVariants[i]) : 0) <= kLdsBytes
+               ? i
+               : otherwise;
+  };
   // 65..128 tokens: eight 16-token column tiles; 33..64: four; 17..32: two;
   // 9..16: all 16 token columns of one tile (the register-staged MFMA kernel)
   if (M > 64) return VARIANT("lmfma_m128_r2_w4_p1");
   if (M > 32) return K >= 16384 ? VARIANT("lmfma_m64_r2_w8_p1") : VARIANT("lmfma_m64_r2_w4_p1");
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
+  // 2..8 tokens on long rows of few output rows (o_proj, down_proj): the
+  // streaming MFMA kernel, when its staged activation and scales fit
+  if (M >= 2 && N < 16384 && K >= 8192 && K % kStreamChunk == 0) {
+    const int i = M <= 4 ? VARIANT("stream_m4_r5_w4_u2") : VARIANT("stream_m8_r5_w4_u2");
+    const Variant& v = kVariants[i];
+    if (stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
+      return i;
+  }
   if (M <= 1) {
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
@@ -1988,36 +2395,7 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   return VARIANT("lmfma_m8_r1_w4_p1");
 }
 
-// NVFP4_GEMV_VARIANT lookup, remembering the last string seen by this thread
-int env_variant(const char* env) {
-  thread_local char last[64] = {0};
-  thread_local int last_index = -1;
-  if (strncmp(env, last, sizeof(last)) == 0) return last_index;
-  last_index = find_variant(env);
-  strncpy(last, env, sizeof(last) - 1);
-  return last_index;
-}
-
 int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
-
-// Rows per workgroup of the MFMA tile kernels.  A workgroup streams its rows
-// at a rate set by the loads it keeps in flight, so a grid of N / (16 R)
-// workgroups that leaves CUs idle (N = 5120: 160 or 320 tiles on 256 CUs)
-// runs at the speed of the busiest CU.  When the tiles fill the CUs at most
-// twice over, the rows are instead dealt out evenly: ceil(N / (256 k))
-// rows per workgroup for the smallest k that fits a 16 R-row tile, so that
-// every CU streams the same number of rows.  NVFP4_GEMV_BALANCE=0 keeps
-// whole tiles (for timing comparisons).
-constexpr int64_t kComputeUnits = 256;  // MI355X
-
-int64_t tile_rows_for(int64_t N, int64_t tile) {
-  const char* env = getenv("NVFP4_GEMV_BALANCE");
-  if (env && env[0] == '0') return tile;
-  const int64_t k = (N + tile * kComputeUnits - 1) / (tile * kComputeUnits);
-  if (k > 2) return tile;
-  const int64_t rows = (N + kComputeUnits * k - 1) / (kComputeUnits * k);
-  return rows < tile ? rows : tile;
-}
 
 // LDS of the staged kernel: activation codes and scales for MT tokens and
 // the block scales of the workgroup's rows, each padded to whole KB
@@ -2038,19 +2416,24 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // the LDS-staged kernel addresses a row tile and the activation with
   // 32-bit buffer offsets
   auto fits = [&](int i) {
-    const Kind kd = kVariants[i].kind;
+    const Variant& v = kVariants[i];
+    const Kind kd = v.kind;
     if ((kd == DMA || kd == DMASA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
-    if ((kd == FMMASA || kd == DMASA) && sa_lds_bytes(kVariants[i], K) > 163840) return false;
-    if (kVariants[i].kind == STAGED && staged_lds_bytes(kVariants[i], K) > 65536) return false;
-    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA) ||
-           (int64_t)16 * kVariants[i].r * (K / 2) < (1ll << 31);
+    if ((kd == STREAM || kd == FSTREAM) && K % kStreamChunk != 0) return false;
+    // the LM-head instantiations also hold the static softmax slots
+    // [MT][tile rows] of their partials
+    const int64_t slot = epi ? (int64_t)4 * v.mt * epi_tile_rows(v) : 0;
+    if ((kd == FMMASA || kd == DMASA) && sa_lds_bytes(v, K) + slot > kLdsBytes) return false;
+    if ((kd == STREAM || kd == FSTREAM) && stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + slot > kLdsBytes)
+      return false;
+    if (kd == STAGED && staged_lds_bytes(v, K) > 65536) return false;
+    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != FSTREAM) ||
+           (int64_t)16 * v.r * (K / 2) < (1ll << 31);
   };
-  // tuning override: NVFP4_GEMV_VARIANT=<variant name>, used when its
-  // compiled token count covers M
-  if (const char* env = getenv("NVFP4_GEMV_VARIANT")) {
-    const int i = env_variant(env);
-    if (i >= 0 && kVariants[i].mt >= M && fits(i)) vi = i;
-  }
+  // tuning override, used when the forced variant's compiled token count
+  // covers M and it fits the shape
+  const int forced = g_forced_variant.load(std::memory_order_relaxed);
+  if (forced >= 0 && forced < kNumVariants && kVariants[forced].mt >= M && fits(forced)) vi = forced;
   if (vi < 0) vi = default_variant(M, N, K, epi);
   if (!fits(vi))
     vi = mt_of(M) <= 2   ? VARIANT("direct_m2_g64_r1_w4_p1")
@@ -2070,9 +2453,11 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
-  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA) {
+  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA ||
+      v.kind == STREAM || v.kind == FSTREAM) {
     c.kp = (int)K;
-    c.rows_per_wg = v.kind == MFMA ? (int64_t)16 * v.r : tile_rows_for(N, (int64_t)16 * v.r);
+    const int64_t tile = (int64_t)(v.kind == STREAM || v.kind == FSTREAM ? 4 : 16) * v.r;  // rows of the kernel's tile
+    c.rows_per_wg = v.kind == MFMA ? tile : tile_rows_for(N, tile);
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     const int ct = v.mt > 16 ? v.mt / 16 : 1;              // 16-token column tiles
     c.lds_bytes = (int64_t)v.nw * v.r * ct * 4 * 64 * 4;  // partial tiles of the final reduction
@@ -2082,6 +2467,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     }
     if (v.kind == FMMASA || v.kind == DMASA) {
       const int64_t b = sa_lds_bytes(v, K);
+      if (b > c.lds_bytes) c.lds_bytes = b;
+    }
+    if (v.kind == FSTREAM || v.kind == STREAM) {
+      const int64_t b = stream_kernel_lds(v, K, c.rows_per_wg);
       if (b > c.lds_bytes) c.lds_bytes = b;
     }
     if (v.kind == DMA || v.kind == FMMA) {
@@ -2106,6 +2495,17 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // merge's slice partials
   c.ws_bytes = epi ? align256(merge_slices_offset(c.grid, c.mt) + (int64_t)c.mt * kMergeGroups * 16) : 0;
   return c;
+}
+
+int set_gemv_tuning(const char* variant, int balance) {
+  int vi = -1;
+  if (variant && variant[0]) {
+    vi = find_variant(variant);
+    if (vi < 0) return -1;
+  }
+  g_forced_variant.store(vi, std::memory_order_relaxed);
+  g_balance.store(balance, std::memory_order_relaxed);
+  return 0;
 }
 
 const char* gemv_variant_name(int vi) { return vi >= 0 && vi < kNumVariants ? kVariants[vi].name : "?"; }

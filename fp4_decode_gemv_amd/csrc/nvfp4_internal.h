@@ -71,6 +71,10 @@ struct GemvConfig {
 
 GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi);
 const char* gemv_variant_name(int variant);
+// Tuning override: force a variant by name (NULL or "" = none) and choose
+// the MFMA kernels' row mapping (balance 1 = even deal, 0 = whole tiles).
+// Returns -1 for an unknown name (nothing changes), else 0.
+int set_gemv_tuning(const char* variant, int balance);
 const char* gemv_variant_by_index(int index);  // NULL past the end
 
 // Workspace bytes the GEMV needs for this shape (with or without the

@@ -58,7 +58,8 @@ typedef enum {
   NVFP4_ERR_NULL = -1,      /* a required pointer is NULL                     */
   NVFP4_ERR_SHAPE = -2,     /* M not in [1,128], N < 1, K outside [32, 2^24]
                                or K % 32 != 0 (K > 131072 for dynamic
-                               per-token scales); with the LM-head epilogue also an
+                               per-token scales; M x K >= 2^30 for the
+                               per-tensor quantization); with the LM-head epilogue also an
                                N whose workspace would pass 2 GB (N beyond
                                about 10^8); sampler sizes out of range        */
   NVFP4_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned (the
@@ -106,9 +107,9 @@ int nvfp4_pack_weights(const float* w, int64_t N, int64_t K,
  * [M][K/2], scales u8 [M][K/16] and the global scale.
  *   flags = NVFP4_GS_DYNAMIC: *gscale (device) is WRITTEN with
  *           amax over all M x K elements / 2688 (one scale per tensor, so a
- *           row's codes depend on the other rows);
+ *           row's codes depend on the other rows); M x K < 2^30;
  *   flags = NVFP4_GS_STATIC:  *gscale (device) is READ (a calibrated
- *           scale); rows are then independent.
+ *           scale); rows are then independent; M x K < 2^30;
  *   flags = NVFP4_GS_TOKEN_DYNAMIC: gscale[M] (device) is WRITTEN, row m's
  *           scale being the amax over that row alone / 2688 (the recipe
  *           applied to each row as its own tensor; K <= 131072).  Rows are
@@ -227,7 +228,7 @@ const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead);
  * aligned) of nvfp4_workspace_size(NVFP4_OP_SAMPLE, M, N, 0) bytes; it
  * needs no zero-fill (every call clears what it accumulates into) and holds
  * nothing between calls.  Outputs and ws must not overlap inputs or each
- * other.  Three launches on `stream`.
+ * other.  Four launches on `stream`.
  * Errors: NVFP4_ERR_SHAPE (M outside [1, 65535], N outside [1, 2^24 - 1]),
  * NVFP4_ERR_NULL, NVFP4_ERR_ALIGN, NVFP4_ERR_WORKSPACE, NVFP4_ERR_ARG
  * (top_p outside (0, 1], overlap), NVFP4_ERR_DEVICE, NVFP4_ERR_HIP.
@@ -236,15 +237,21 @@ int nvfp4_sample_top_p(int M, int64_t N, const float* logits, const float* tempe
                        const float* uniforms, int32_t* tokens, int32_t* nucleus, void* ws, size_t ws_bytes,
                        void* stream);
 
-/* Name of compiled kernel variant `index` (0-based), NULL past the end.
- * Setting the environment variable NVFP4_GEMV_VARIANT to one of these
- * names makes nvfp4_gemv_smallm launch that variant for every M it covers
- * (for tuning and testing; read on each call).  NVFP4_GEMV_BALANCE=0 makes
- * the MFMA kernels keep whole 16-row tiles per workgroup instead of dealing
- * the rows of small-N shapes out evenly over the CUs (also read on each
- * call; it changes the LM-head workspace size, which must then be queried
- * again). */
+/* Name of compiled kernel variant `index` (0-based), NULL past the end. */
 const char* nvfp4_gemv_variant_name(int index);
+
+/*
+ * Tuning and test hook, process-wide: nvfp4_gemv_smallm (and
+ * nvfp4_workspace_size, nvfp4_gemv_variant) use the compiled variant named
+ * `variant` for every M its token count covers and every shape it fits
+ * (NULL or "" = the launch table's choice).  balance = 1 (the default)
+ * deals the rows of small-N shapes out evenly over the CUs in the MFMA tile
+ * kernels; balance = 0 keeps whole 16- or 4-row-group tiles.  Both change
+ * workspace sizes, which must be queried again.  Not for use while another
+ * thread launches GEMVs.  Errors: NVFP4_ERR_ARG (unknown name, balance not
+ * 0 or 1; nothing changes).
+ */
+int nvfp4_gemv_tune(const char* variant, int balance);
 
 #ifdef __cplusplus
 }

@@ -160,13 +160,13 @@ def test_reset_state_and_workspace_helpers(L):
     assert a > b > 0
 
 
-def test_launch_table_names_real_variants(L, monkeypatch):
+def test_launch_table_names_real_variants(L):
     """Every shape of the workloads resolves to a compiled variant whose
     token count covers M and whose K granularity K satisfies (host logic
     only: no kernel runs)."""
     import workloads as W
 
-    monkeypatch.delenv("NVFP4_GEMV_VARIANT", raising=False)
+    F.nvfp4_gemv_tune(None, True)
     names = set(F.nvfp4_gemv_variant_names())
     shapes = [(c.N, c.K) for c in W.qwen3_8b_cases() + W.qwen3_32b_cases()]
     shapes += [(W.lm_head_case().N, W.lm_head_case().K), (4096, 4096), (4097, 4128), (300, 96), (1, 32)]
@@ -179,13 +179,32 @@ def test_launch_table_names_real_variants(L, monkeypatch):
                 assert K % F.variant_k_multiple(v) == 0, (M, N, K, v)
 
 
-def test_forced_variant_falls_back_when_k_does_not_fit(L, monkeypatch):
+def test_forced_variant_falls_back_when_k_does_not_fit(L):
     """A direct-to-LDS variant forced on a K that is not a multiple of 256
     is not launched; the default for that shape is used instead."""
-    monkeypatch.setenv("NVFP4_GEMV_VARIANT", "dma_m8_r2_w4_d3")
-    assert F.nvfp4_gemv_variant(8, 1024, 4096) == "dma_m8_r2_w4_d3"
-    v = F.nvfp4_gemv_variant(8, 1024, 4128)
-    assert v != "dma_m8_r2_w4_d3" and 4128 % F.variant_k_multiple(v) == 0
+    with F.forced_variant("dma_m8_r2_w4_d3"):
+        assert F.nvfp4_gemv_variant(8, 1024, 4096) == "dma_m8_r2_w4_d3"
+        v = F.nvfp4_gemv_variant(8, 1024, 4128)
+        assert v != "dma_m8_r2_w4_d3" and 4128 % F.variant_k_multiple(v) == 0
+    assert F.nvfp4_gemv_variant(8, 1024, 4096) != "dma_m8_r2_w4_d3"
+
+
+def test_gemv_tune_rejects_unknown_names(L):
+    assert L.nvfp4_gemv_tune(b"no_such_variant", 1) == F.NVFP4_ERR_ARG
+    assert L.nvfp4_gemv_tune(None, 2) == F.NVFP4_ERR_ARG
+    assert L.nvfp4_gemv_tune(None, 1) == F.NVFP4_OK
+    with pytest.raises(F.Nvfp4Error):
+        F.nvfp4_gemv_tune("no_such_variant")
+
+
+def test_quantize_rejects_tensors_past_32_bit_offsets(L):
+    """A per-tensor quantization of M x K >= 2^30 elements is a shape error
+    (its 2-byte elements are addressed with 32-bit byte offsets); per-token
+    rows are short enough."""
+    far = 1 << 44
+    x, c, sc, g, ws = A, A + far, A + 2 * far, A + 3 * far, A + 4 * far
+    assert L.nvfp4_quantize_act(x, 128, 1 << 23, c, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_SHAPE
+    assert L.nvfp4_quantize_act(x, 128, 1 << 24, c, sc, g, F.NVFP4_GS_DYNAMIC, ws, 1 << 40, None) == F.NVFP4_ERR_SHAPE
 
 
 def test_gemv_epilogue_partials_beyond_2gb_are_a_shape_error(L):

@@ -126,18 +126,28 @@ def test_gemv_is_repeatable_and_rows_do_not_depend_on_m():
 VARIANT_SHAPES = [(1, 37, 160), (16, 515, 4128), (16, 300, 5120), (16, 129, 25600)]
 # kernels that need K % 256 == 0: one step, 17 steps over the waves, two full sizes
 VARIANT_SHAPES_K256 = [(1, 37, 256), (16, 515, 4352), (16, 300, 5120), (16, 129, 25600)]
+# ... K % 512 == 0: one chunk, 9 chunks over the waves, two full sizes
+VARIANT_SHAPES_K512 = [(1, 37, 512), (16, 515, 4608), (16, 300, 5120), (16, 129, 25600)]
+
+
+@pytest.fixture
+def force():
+    """forced_variant(...) for the test's duration; the launch table is
+    restored afterwards."""
+    yield F.forced_variant
+    F.nvfp4_gemv_tune(None, True)
 
 
 @pytest.mark.parametrize("variant", F.nvfp4_gemv_variant_names() if __import__("os").path.exists(F.LIB_PATH) else [])
-def test_every_kernel_variant(variant, monkeypatch):
-    """Each compiled variant (forced through NVFP4_GEMV_VARIANT) against the
+def test_every_kernel_variant(variant, force):
+    """Each compiled variant (forced through nvfp4_gemv_tune) against the
     oracle: ragged row tails, K not a multiple of 128, several K phases, and
     M below and at the variant's token count.  A variant whose LDS would not
     fit a shape is not launched there (the default runs instead); every
     variant runs at least two of the shapes."""
     mt = F.variant_tokens(variant)
-    monkeypatch.setenv("NVFP4_GEMV_VARIANT", variant)
-    shapes = VARIANT_SHAPES if F.variant_k_multiple(variant) == 32 else VARIANT_SHAPES_K256
+    force(variant).__enter__()
+    shapes = {32: VARIANT_SHAPES, 256: VARIANT_SHAPES_K256, 512: VARIANT_SHAPES_K512}[F.variant_k_multiple(variant)]
     ran = 0
     for M in sorted({1, max(1, mt - 1), mt}):
         for (nmul, N, K) in shapes:
@@ -153,25 +163,25 @@ def test_every_kernel_variant(variant, monkeypatch):
     assert ran >= 2, variant
 
 
-# Row mapping of the MFMA tile kernels: whole 16R-row tiles (forced with
-# NVFP4_GEMV_BALANCE=0) against rows dealt out evenly over the CUs (the
+# Row mapping of the MFMA tile kernels: whole tiles (forced with
+# nvfp4_gemv_tune(..., balance=False)) against rows dealt out evenly over the CUs (the
 # default where whole tiles would leave CUs idle; N = 5120 gives 20 or 10
 # rows per workgroup).  N = 4099 leaves a ragged last tile in both mappings;
 # N = 5120 - 3 a ragged last workgroup of the even deal.
 ROW_MAP_CASES = [("lmfma_m8_r2_w8_p1", 8, 4099, 2048), ("lmfma_m8_r1_w4_p1", 5, 5117, 1280),
                  ("lmfma_m16_r2_w8_p1", 16, 5117, 2048), ("lmfma_m16_r1_w4_p1", 10, 4099, 1312),
                  ("lmfma_m32_r2_w8_p1", 32, 5117, 2048), ("lmfma_m32_r1_w4_p1", 20, 4099, 1312),
-                 ("lmfma_m64_r1_w8_p1", 64, 5117, 2048), ("lmfma_m64_r2_w4_p1", 40, 4099, 1312),
+                 ("lmfma_m64_r2_w8_p1", 64, 5117, 2048), ("lmfma_m64_r2_w4_p1", 40, 4099, 1312),
                  ("lmfma_m128_r1_w4_p1", 128, 5117, 1024), ("lmfma_m128_r2_w4_p1", 90, 4099, 1312),
                  ("dma_m8_r2_w4_d3", 8, 5117, 1024), ("dma_m8_r2_w4_d2_sa", 7, 4099, 2048),
-                 ("fmma_m4_r2_w4_d3", 4, 5117, 1024), ("fmma_m2_r1_w4_d3_sa", 2, 4099, 1024)]
+                 ("fmma_m4_r2_w4_d3", 4, 5117, 1024), ("fmma_m2_r1_w4_d3_sa", 2, 4099, 1024),
+                 ("stream_m8_r5_w4_u2", 8, 5117, 1024), ("stream_m4_r5_w4_u2", 3, 4099, 2048)]
 
 
 @pytest.mark.parametrize("balance", ["0", "1"])
 @pytest.mark.parametrize("variant,M,N,K", ROW_MAP_CASES)
-def test_row_mapping(variant, M, N, K, balance, monkeypatch):
-    monkeypatch.setenv("NVFP4_GEMV_VARIANT", variant)
-    monkeypatch.setenv("NVFP4_GEMV_BALANCE", balance)
+def test_row_mapping(variant, M, N, K, balance, force):
+    force(variant, balance == "1").__enter__()
     assert F.nvfp4_gemv_variant(M, N, K) == variant
     w = W.small_random_weights(N + 5 * K, N, K)
     xb = W.small_random_bf16(N + M, M, K)

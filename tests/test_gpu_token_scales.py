@@ -60,9 +60,13 @@ def test_static_token_scales_bit_exact():
 
 # one shape every variant runs (K % 256 == 0, small enough for every LDS layout)
 @pytest.mark.parametrize("variant", F.nvfp4_gemv_variant_names() if __import__("os").path.exists(F.LIB_PATH) else [])
-def test_every_kernel_variant_with_token_scales(variant, monkeypatch):
+def test_every_kernel_variant_with_token_scales(variant):
     mt = F.variant_tokens(variant)
-    monkeypatch.setenv("NVFP4_GEMV_VARIANT", variant)
+    with F.forced_variant(variant):
+        _token_variant_case(variant, mt)
+
+
+def _token_variant_case(variant, mt):
     N, K = 300, 5120
     w = W.small_random_weights(N + 5, N, K)
     wq = F.nvfp4_pack_weights(f32_dev(w))
