@@ -155,11 +155,14 @@ template <int B>
 __device__ __forceinline__ uint32_t f16x2_of_fp4(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B));
 }
+// Vector elements are converted to bits with __float_as_uint: hipcc (clang
+// 22, ROCm 7.2) compiles __builtin_bit_cast of an element of an
+// ext_vector_type float pair as a bit cast of element 0.
 template <int B>
 __device__ __forceinline__ void f32x2_of_fp4(uint32_t w, uint32_t* o) {
   const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
-  o[0] = __builtin_bit_cast(uint32_t, f[0]);
-  o[1] = __builtin_bit_cast(uint32_t, f[1]);
+  o[0] = __float_as_uint(f[0]);
+  o[1] = __float_as_uint(f[1]);
 }
 
 __global__ void convert_kernel(int op, const uint32_t* __restrict__ in, uint32_t* __restrict__ out, int n) {
@@ -182,10 +185,10 @@ __global__ void convert_kernel(int op, const uint32_t* __restrict__ in, uint32_t
     case NVFP4_PROBE_FP8_TO_F32: {  // low and high 16 bits, two floats each
       const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
       const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-      out[4 * i + 0] = __builtin_bit_cast(uint32_t, lo[0]);
-      out[4 * i + 1] = __builtin_bit_cast(uint32_t, lo[1]);
-      out[4 * i + 2] = __builtin_bit_cast(uint32_t, hi[0]);
-      out[4 * i + 3] = __builtin_bit_cast(uint32_t, hi[1]);
+      out[4 * i + 0] = __float_as_uint(lo[0]);
+      out[4 * i + 1] = __float_as_uint(lo[1]);
+      out[4 * i + 2] = __float_as_uint(hi[0]);
+      out[4 * i + 3] = __float_as_uint(hi[1]);
       break;
     }
     case NVFP4_PROBE_F32_TO_FP4: {  // in[2i], in[2i+1] are two floats -> one byte (n counts pairs)

@@ -47,3 +47,26 @@ def assert_gemv_close(y_gpu: np.ndarray, y_ref: np.ndarray, ref_abs: np.ndarray,
         raise AssertionError(f"{what}: {int((~ok).sum())} outputs out of tolerance; first at {tuple(i)}: "
                              f"gpu={y_gpu[tuple(i)]!r} ref={y_ref[tuple(i)]!r} ref_abs={ref_abs[tuple(i)]!r}")
     return float(np.max(err / np.maximum(ref_abs, 1e-300)))
+
+
+def oracle_rows_ref(w: np.ndarray, s_g, a_qs, chunk: int = 2048, workers: int = 8):
+    """The oracle's (y, ref_abs) for every row of a large weight matrix w
+    (fp32 [N][K], global scale s_g of the whole matrix) against each of the
+    oracle's quantized activations in a_qs: the oracle's own quantization
+    (once per row chunk) and fp64 GEMV, run on row chunks in threads (numpy
+    releases the GIL), joined in row order."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import nvfp4_oracle as O
+
+    N = w.shape[0]
+    starts = list(range(0, N, chunk))
+
+    def one(r0):
+        wq = O.quantize_nvfp4(w[r0:r0 + chunk], s_g)
+        return [O.gemv_ref(a_q, wq) for a_q in a_qs]
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(one, starts))
+    return [(np.concatenate([p[i][0] for p in parts], axis=1), np.concatenate([p[i][1] for p in parts], axis=1))
+            for i in range(len(a_qs))]

@@ -8,7 +8,7 @@ import torch
 import fp4_decode_gemv_amd as F
 import workloads as W
 from oracle import nvfp4_oracle as O
-from gpu_util import assert_gemv_close, assert_same_q, bf16_dev, f32_dev, host
+from gpu_util import assert_gemv_close, assert_same_q, bf16_dev, f32_dev, host, oracle_rows_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -89,6 +89,26 @@ def test_qwen3_32b_projections(case):
 
 def test_lm_head_projection():
     _full_size(W.lm_head_case(), (1, 8))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", W.qwen3_32b_cases(), ids=lambda c: c.name)
+def test_qwen3_32b_every_row(case):
+    """Every output row of the full-size Qwen3-32B projections at M = 1 and
+    8, against the oracle's own quantization and fp64 GEMV of the whole
+    weight matrix (row chunks)."""
+    w = W.weights(case.w_seed, case.N, case.K, case.w_outlier_rows)
+    wq = F.nvfp4_pack_weights(f32_dev(w))
+    s_g = O.global_scale(np.max(np.abs(w)))
+    xb = W.case_activations_bf16(case, 8)
+    ys = {}
+    for M in (1, 8):
+        print(f"[gemv rows] {case.name} M={M} N={case.N} K={case.K}", flush=True)
+        aq = F.nvfp4_quantize_act(bf16_dev(xb[:M]))
+        ys[M] = F.nvfp4_gemv_smallm(aq, wq).cpu().numpy()
+    refs = oracle_rows_ref(w, s_g, [O.quantize_act_bf16(xb[:1]), O.quantize_act_bf16(xb)])
+    for (M, (y_ref, ref_abs)) in zip((1, 8), refs):
+        assert_gemv_close(ys[M], y_ref, ref_abs, what=f"{case.name} M={M} all rows")
 
 
 def test_zero_activation_and_zero_rows():

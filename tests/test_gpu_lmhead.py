@@ -10,7 +10,7 @@ import fp4_decode_gemv_amd as F
 import workloads as W
 from oracle import nvfp4_oracle as O
 from oracle import reset_oracle as R
-from gpu_util import assert_gemv_close, bf16_dev, f32_dev
+from gpu_util import assert_gemv_close, bf16_dev, f32_dev, oracle_rows_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -24,15 +24,18 @@ def _decisions_agree(tr: R.ResetTrace, T_gpu: np.ndarray, p: R.ResetParams, band
     return ok, int(tie.sum())
 
 
-def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None):
-    """Decode `positions` steps; returns logits of the last step, H [P][M], T [P][M]."""
+def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None, keep=None):
+    """Decode `positions` steps; returns the logits of the kept positions
+    (all by default, else {t: logits} for t in `keep`), H [P][M], T [P][M]
+    and, for every position, the fp64 entropy of the GPU's own logits."""
     dev = torch.device("cuda:0")
     P = xbits_pos.shape[0]
     st = F.new_reset_state(M, p.window, dev)
     ent = torch.empty(M, device=dev)
     tmp = torch.empty(M, device=dev)
     ws = F.new_workspace(F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, wq.rows, wq.K), dev)
-    Hs, Ts, logits = [], [], []
+    Hs, Ts, Hrefs = [], [], []
+    logits = [] if keep is None else {}
     for t in range(P):
         xb = xbits_pos[t]
         aq = F.nvfp4_quantize_act(bf16_dev(xb))
@@ -44,8 +47,13 @@ def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None):
         y = F.nvfp4_gemv_smallm(aq, wq, epi=epi, ws=ws)
         Hs.append(ent.cpu().numpy().copy())
         Ts.append(tmp.cpu().numpy().copy())
-        logits.append(y.cpu().numpy())
-    return logits, np.array(Hs), np.array(Ts)
+        yh = y.cpu().numpy()
+        Hrefs.append(R.entropy_rows(yh.astype(np.float64)))
+        if keep is None:
+            logits.append(yh)
+        elif t in keep:
+            logits[t] = yh
+    return logits, np.array(Hs), np.array(Ts), np.array(Hrefs)
 
 
 @pytest.mark.parametrize("mode,M,N,K", [(0, 4, 3000, 512), (1, 4, 3000, 512), (2, 4, 3000, 512), (0, 1, 2500, 1024),
@@ -61,10 +69,9 @@ def test_small_vocab_sequence(mode, M, N, K):
     flags = W.step_flags(43, P, M, p=0.15)
     p = R.ResetParams(tau0=0.6, t_low=0.4, t_high=1.0, t_base=0.6, window=4, mode=mode)
     wq = F.nvfp4_pack_weights(f32_dev(w))
-    logits, H, T = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
+    logits, H, T, Href = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
     for t in range(P):
-        Href = R.entropy_rows(logits[t].astype(np.float64))
-        assert np.all(np.abs(H[t] - Href) <= 1e-4), (t, H[t], Href)
+        assert np.all(np.abs(H[t] - Href[t]) <= 1e-4), (t, H[t], Href[t])
     assert H.min() < 0.6 < H.max(), "sequence must exercise both sides of tau0"
     ties = 0
     for m in range(M):
@@ -94,7 +101,7 @@ def test_chunked_runs_carry_state():
     flags = W.step_flags(52, 40, M, p=0.2)
     p = R.ResetParams(window=3)
     wq = F.nvfp4_pack_weights(f32_dev(w))
-    _, H1, T1 = _run_sequence(wq, xs, flags, p, M)
+    _, H1, T1, _ = _run_sequence(wq, xs, flags, p, M)
     # same thing, state re-initialised only once, in two halves
     dev = torch.device("cuda:0")
     st = F.new_reset_state(M, p.window, dev)
@@ -110,10 +117,19 @@ def test_chunked_runs_carry_state():
     assert np.array_equal(np.array(T2), T1)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("M", [1, 8])
 def test_full_lm_head_sequence(M):
+    """The LM-head workload end to end: 512 positions of M sequences with
+    fresh activations (exponents 2^u spreading the entropies over every
+    branch of the rule), seeded step flags, the full 151936-row head.
+    Entropies within 1e-4 nats of the fp64 entropy of the GPU's logits at
+    every position and, at two positions, of the oracle's own logits over
+    the whole vocabulary; temperatures equal to the oracle's ReSET rule
+    wherever it is not within rounding of a tie; sampled logits of those two
+    positions against the oracle."""
     case = W.lm_head_case()
-    P = 48
+    P = 512
     print(f"[lmhead] N={case.N} K={case.K} M={M} positions={P}", flush=True)
     w = W.weights(case.w_seed, case.N, case.K, case.w_outlier_rows)
     wq = F.nvfp4_pack_weights(f32_dev(w))
@@ -122,24 +138,23 @@ def test_full_lm_head_sequence(M):
     flags = W.step_flags(3300, P, M)
     u = W.pow2_exponents(3400, P)
     p = R.ResetParams(tau0=0.6, t_low=0.4, t_high=1.0, t_base=0.6, window=8)
-    logits, H, T = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
+    checked = (0, P - 1)
+    logits, H, T, Href = _run_sequence(wq, xs, flags, p, M, scale_exp=u, keep=checked)
     for t in range(P):
-        Href = R.entropy_rows(logits[t].astype(np.float64))
-        assert np.all(np.abs(H[t] - Href) <= 1e-4), (t, H[t], Href)
+        assert np.all(np.abs(H[t] - Href[t]) <= 1e-4), (t, H[t], Href[t])
     for m in range(M):
         tr = R.reset_sequence(H[:, m].astype(np.float32).astype(np.float64), flags[:, m], p)
         ok, _ = _decisions_agree(tr, T[:, m], p, BAND)
         assert ok.all(), (m, np.nonzero(~ok))
-    # sampled logits of two positions against the oracle
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, case.N - 1], rng.choice(case.N, 64, replace=False)]))
+    print(f"[lmhead] M={M}: {P} positions checked; oracle logits of positions {checked}", flush=True)
     s_g = O.global_scale(np.max(np.abs(w)))
-    wr = O.quantize_nvfp4(w[rows], s_g)
-    for t in (0, P - 1):
+    ars = []
+    for t in checked:
         ar = O.quantize_act_bf16(xs[t])
-        ar = (ar[0], ar[1], np.float32(ar[2] * np.float32(2.0 ** u[t])))
-        y_ref, ref_abs = O.gemv_ref(ar, wr)
-        assert_gemv_close(logits[t][:, rows], y_ref, ref_abs, what=f"lm head t={t}")
+        ars.append((ar[0], ar[1], np.float32(ar[2] * np.float32(2.0 ** u[t]))))
+    for t, (y_ref, ref_abs) in zip(checked, oracle_rows_ref(w, s_g, ars)):
+        assert_gemv_close(logits[t], y_ref, ref_abs, what=f"lm head t={t}")
+        assert np.all(np.abs(H[t] - R.entropy_rows(y_ref)) <= 1e-4), (t, H[t], R.entropy_rows(y_ref))
 
 
 @pytest.mark.parametrize("M", [1, 8])
