@@ -58,6 +58,8 @@ EXPORTED = (
     "nvfp4_reset_state_init",
     "nvfp4_gemv_smallm",
     "nvfp4_gemv_smallm_token_scales",
+    "nvfp4_gemv_smallm_noalloc",
+    "nvfp4_gemv_noalloc_scratch_bytes",
     "nvfp4_gemv_variant",
     "nvfp4_gemv_variant_name",
     "nvfp4_gemv_tune",
@@ -128,6 +130,11 @@ def lib() -> ctypes.CDLL:
                                     ctypes.POINTER(LmheadEpilogue), vp, sz, vp]
     L.nvfp4_gemv_smallm_token_scales.restype = c_int
     L.nvfp4_gemv_smallm_token_scales.argtypes = L.nvfp4_gemv_smallm.argtypes
+    L.nvfp4_gemv_smallm_noalloc.restype = c_int
+    L.nvfp4_gemv_smallm_noalloc.argtypes = [c_int, i64, i64, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.POINTER(LmheadEpilogue), vp]
+    L.nvfp4_gemv_noalloc_scratch_bytes.restype = sz
+    L.nvfp4_gemv_noalloc_scratch_bytes.argtypes = []
     L.nvfp4_sample_top_p.restype = c_int
     L.nvfp4_sample_top_p.argtypes = [c_int, i64, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
     _lib = L
@@ -389,13 +396,8 @@ class Epilogue:
                               _ptr(self.temperature))
 
 
-def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | None = None, ws=None,
-                      M: int | None = None, stream=None):
-    """y [M][N] fp32 = dequant(a) . dequant(w)^T.  ``ws``: a zero-filled
-    workspace of at least nvfp4_workspace_size(...) bytes (allocated here
-    when needed and not given).  ``M`` (default: a's rows) may use only the
-    first rows of ``a``.  An activation with one global scale per row goes
-    to the per-token entry point."""
+def _gemv_args(a: NvFp4Tensor, w: NvFp4Tensor, y, epi: Epilogue | None, M: int | None):
+    """Check a GEMV's tensors; returns (M, N, K, y, per_token, C epilogue)."""
     import torch
 
     dev = w.codes.device
@@ -426,6 +428,18 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
         _require(epi.entropy, "epi.entropy", torch.float32, dev, min_numel=M)
         _require(epi.temperature, "epi.temperature", torch.float32, dev, min_numel=M)
         ce = epi.as_c()
+    return M, N, K, y, per_token, ce
+
+
+def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | None = None, ws=None,
+                      M: int | None = None, stream=None):
+    """y [M][N] fp32 = dequant(a) . dequant(w)^T.  ``ws``: a zero-filled
+    workspace of at least nvfp4_workspace_size(...) bytes (allocated here
+    when needed and not given).  ``M`` (default: a's rows) may use only the
+    first rows of ``a``.  An activation with one global scale per row goes
+    to the per-token entry point."""
+    M, N, K, y, per_token, ce = _gemv_args(a, w, y, epi, M)
+    dev = w.codes.device
     need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD if epi is not None else NVFP4_OP_GEMV, M, N, K)
     if need and ws is None:
         ws = new_workspace(need, dev, stream)
@@ -435,6 +449,21 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
     _check(fn(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale), _ptr(w.codes), _ptr(w.scales),
               _ptr(w.gscale), _ptr(y), None if ce is None else ctypes.byref(ce), _ptr(ws), ws_bytes,
               _stream(stream)), "nvfp4_gemv_smallm")
+    return y
+
+
+def nvfp4_gemv_smallm_noalloc(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | None = None,
+                              M: int | None = None, stream=None):
+    """nvfp4_gemv_smallm with its workspace in the library's static device
+    scratch (the entry point for callers that cannot allocate; one global
+    activation scale).  ``y`` must be given to allocate nothing here either."""
+    M, N, K, y, per_token, ce = _gemv_args(a, w, y, epi, M)
+    if per_token:
+        raise ValueError("nvfp4_gemv_smallm_noalloc takes one activation global scale")
+    _check(lib().nvfp4_gemv_smallm_noalloc(M, N, K, _ptr(a.codes), _ptr(a.scales), _ptr(a.gscale), _ptr(w.codes),
+                                           _ptr(w.scales), _ptr(w.gscale), _ptr(y),
+                                           None if ce is None else ctypes.byref(ce), _stream(stream)),
+           "nvfp4_gemv_smallm_noalloc")
     return y
 
 

@@ -32,6 +32,25 @@ bool shape_ok(int M, int64_t N, int64_t K) {
   return M >= 1 && M <= kMaxTokens && N >= 1 && N <= ((int64_t)1 << 40) && shape_ok_k(K);
 }
 
+// Scratch of the entry point that allocates nothing
+// (nvfp4_gemv_smallm_noalloc): a file-scope device array, one copy per GPU,
+// held until the process ends.  In host code `scratch` is only a handle:
+// its device address (per device) comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_ptr[64];
+
+// Device address of this device's scratch array (the current device);
+// NULL after a HIP error.
+void* scratch_for(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 // Device check, cached per device ordinal (1 = gfx950, 2 = other).
 std::atomic<int> g_arch_cache[64];
 
@@ -256,6 +275,24 @@ int nvfp4_gemv_smallm_token_scales(int M, int64_t N, int64_t K, const uint8_t* a
   return gemv_entry(M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y, epi, ws, ws_bytes, stream,
                     true);
 }
+
+int nvfp4_gemv_smallm_noalloc(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_gscale, float* y, const nvfp4_lmhead_epilogue_t* epi, void* stream) {
+  // host checks first: shape, then the scratch this shape needs
+  if (!shape_ok(M, N, K)) return NVFP4_ERR_SHAPE;
+  if (gemv_workspace_bytes(M, N, K, epi != nullptr) > kNoAllocScratchBytes) return NVFP4_ERR_WORKSPACE;
+  const int d = check_device();
+  if (d != NVFP4_OK) return d;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NVFP4_ERR_HIP;
+  void* ws = scratch_for(dev);
+  if (!ws) return NVFP4_ERR_HIP;
+  return gemv_entry(M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y, epi, ws,
+                    kNoAllocScratchBytes, stream, false);
+}
+
+size_t nvfp4_gemv_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead) {
   if (!shape_ok(M, N, K)) return "invalid shape";

@@ -199,6 +199,30 @@ int nvfp4_gemv_smallm_token_scales(int M, int64_t N, int64_t K,
                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_gemv_smallm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation, kernels, arguments and errors, without a
+ * workspace argument.  The workspace (the LM-head epilogue's partials; a
+ * plain projection needs none) lives in a static device array of
+ * nvfp4_gemv_noalloc_scratch_bytes() = 16 MiB that each GPU the library runs
+ * on holds until the process ends; nothing is allocated or freed by the
+ * call.  Shapes whose workspace would exceed it (the LM-head epilogue at
+ * about N * M > 10^7, e.g. M = 128 with N > 130000) return
+ * NVFP4_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * that GPU's array: calls that can overlap on one GPU (different streams
+ * without ordering, or threads) race and give undefined results; calls on
+ * one stream are ordered.  The array keeps the last call's contents; no
+ * call depends on them (every partial is written before it is read).
+ */
+int nvfp4_gemv_smallm_noalloc(int M, int64_t N, int64_t K,
+                              const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                              const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
+                              float* y, const nvfp4_lmhead_epilogue_t* epi, void* stream);
+
+/* Bytes of the static scratch array of nvfp4_gemv_smallm_noalloc. */
+size_t nvfp4_gemv_noalloc_scratch_bytes(void);
+
+/*
  * Name of the kernel variant nvfp4_gemv_smallm launches for this shape
  * (lmhead != 0: with the epilogue).  Static string; pure host function.
  * The launch table is chosen per (M, N, K) on the host, like the pages'

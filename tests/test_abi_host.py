@@ -13,12 +13,13 @@ from conftest import ROOT
 F = pytest.importorskip("fp4_decode_gemv_amd")
 
 HDR = os.path.join(ROOT, "include", "nvfp4.h")
+PROBE_HDR = os.path.join(ROOT, "include", "nvfp4_probe.h")
 A = 0x7F0000000000          # a 16-byte-aligned fake device address
 BIG = 1 << 30               # spacing so fake buffers never overlap
 
 
-def _declared():
-    txt = open(HDR).read()
+def _declared(path=HDR):
+    txt = open(path).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(nvfp4_[a-z_0-9]+)\s*\(", txt, re.M)))
 
 
@@ -36,6 +37,40 @@ def test_every_declared_symbol_is_exported(L):
     assert set(names) == set(F.EXPORTED), names
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_probe_library_exports_every_declared_symbol(L):
+    from fp4_decode_gemv_amd import probe as P
+
+    names = _declared(PROBE_HDR)
+    assert set(names) == set(P.EXPORTED), names
+    PL = P.lib()
+    for n in names:
+        assert hasattr(PL, n), n
+    assert P.read_variants()[0].startswith("vgpr_u")
+
+
+def test_probe_rejects_bad_arguments(L):
+    from fp4_decode_gemv_amd import probe as P
+
+    PL = P.lib()
+    assert PL.nvfp4_probe_read(-1, A, 1024, 1, A + BIG, None) == -1
+    assert PL.nvfp4_probe_read(0, A + 4, 1024, 1, A + BIG, None) == -1   # misaligned
+    assert PL.nvfp4_probe_read(0, A, 1000, 1, A + BIG, None) == -1       # not a multiple of 16
+    assert PL.nvfp4_probe_read(0, A, 1 << 33, 1, A + BIG, None) == -1    # one slice past 2 GB
+    assert PL.nvfp4_probe_convert(9, A, A + BIG, 4, None) == -1
+    assert PL.nvfp4_probe_empty(0, 64, None) == -1
+
+
+def test_noalloc_rejects_shapes_before_any_hip_call(L):
+    """The scratch entry point refuses out-of-range shapes and shapes whose
+    LM-head workspace exceeds its static array on the host (no GPU here)."""
+    assert L.nvfp4_gemv_noalloc_scratch_bytes() == 16 << 20
+    e = ctypes.byref(F.LmheadEpilogue(0.6, 0.4, 1.0, 0.6, 8, 0, A, A, A, A))
+    args = (A, A + BIG, A + 2 * BIG, A + 3 * BIG, A + 4 * BIG, A + 5 * BIG, A + 6 * BIG)
+    assert L.nvfp4_gemv_smallm_noalloc(0, 64, 64, *args, None, None) == F.NVFP4_ERR_SHAPE
+    assert F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, 128, 400000, 32) > 16 << 20
+    assert L.nvfp4_gemv_smallm_noalloc(128, 400000, 32, *args, e, None) == F.NVFP4_ERR_WORKSPACE
 
 
 def test_status_strings(L):
