@@ -21,13 +21,19 @@ Prints one JSON line:
                step / their summed average durations (each case: `reps`
                back-to-back launches captured in a graph, HIP events around
                its replay on the launch stream), against the 8 TB/s HBM peak
+               and the measured read-stream ceiling: the fastest plain read of
+               the same bytes (probe library, best variant and grid per size),
+               timed the same way
   cpu_baseline the CPU oracle (quantize + dequantize + fp64 GEMV) on a
-               bounded row sample of the same projections, same byte formula
-  extra        the four projections at M = 16, 32, 64 and 128 (beyond the metric's M
-               range; per-kernel times only), the LM head (N=151936) with the
-               entropy / ReSET epilogue and the top-p = 0.95 draw at the
-               epilogue's temperatures, and the 64-layer decode chain
-               captured in one graph
+               bounded row sample of the same projections, same byte formula,
+               with the median time of every (projection, M) case
+  extra        the single 4096 x 4096 GEMV and the Qwen3-8B projections at
+               M = 1, 2, 4, 8 (per-kernel times, fractions of 8 TB/s and of the
+               measured read ceiling), the four projections at M = 16, 32, 64
+               and 128 (beyond the metric's M range; per-kernel times only),
+               the LM head (N=151936) with the entropy / ReSET epilogue and the
+               top-p = 0.95 draw at the epilogue's temperatures, and the
+               64-layer decode chain captured in one graph
 """
 
 from __future__ import annotations
@@ -124,6 +130,8 @@ def parse():
     ap.add_argument("--no-lmhead", action="store_true", help="skip the LM-head + ReSET epilogue figures")
     ap.add_argument("--no-chain", action="store_true", help="skip the 64-layer hipGraph chain figures")
     ap.add_argument("--no-wide", action="store_true", help="skip the M = 16, 32, 64 and 128 projection figures (extra.wide)")
+    ap.add_argument("--no-small", action="store_true", help="skip the 4096 x 4096 and Qwen3-8B projection figures")
+    ap.add_argument("--no-probe", action="store_true", help="skip the measured read-stream ceiling")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="at the end, fill and copy a buffer of this many MiB three times: a plain copy of "
                          "known size to calibrate hardware byte counters against")
@@ -136,14 +144,19 @@ def log(args, *a):
         print(*a, file=sys.stderr, flush=True)
 
 
-def setup(args):
+def setup(args, cases=None, Ms=None):
+    """Pack every case's weights on the GPU (enough copies to rotate through
+    args.rotate_mb) and make its activations for each M."""
     import torch
 
     import fp4_decode_gemv_amd as F
     import workloads as W
 
     dev = torch.device("cuda:0")
-    cases = W.qwen3_32b_cases()
+    if cases is None:
+        cases = W.qwen3_32b_cases()
+    if Ms is None:
+        Ms = M_LIST + (M_WIDE if not args.no_wide else ())
     wq = {}      # name -> list of NvFp4Tensor copies
     samples = {}  # name -> (first CPU_ROWS rows of W, global scale of the whole W)
     for c in cases:
@@ -163,7 +176,7 @@ def setup(args):
         log(args, f"[setup] packed {c.name} {c.N}x{c.K} x{len(copies)} in {time.perf_counter() - t0:.1f}s")
     acts = {}
     for c in cases:
-        for M in M_LIST + (M_WIDE if not args.no_wide else ()):
+        for M in Ms:
             acts[(c.name, M)] = make_activation(c, M, dev)
     torch.cuda.synchronize()
     return cases, wq, acts, samples
@@ -303,54 +316,44 @@ def main():
     # average is the kernel's duration as a decode step runs it (it agrees
     # with rocprofv3's per-dispatch durations); host launch overhead is not
     # in it.
-    detail = []
-    gemv_bytes = 0
-    gemv_us = 0.0
-
-    def b2b(fn):
-        g = capture(lambda: [fn(i) for i in range(args.reps)])
-        # 7 timed replays of `reps` launches: >= 200 timed dispatches per case
-        return _replay_us(g, args.reps, stream, replays=7)
-
-    for c in cases:
-        for M in M_LIST:
-            gus = b2b(lambda i: gemv(c, M, i))
-            qus = b2b(lambda i: quant(c, M))
-            wb = weight_bytes(c.N, c.K)
-            detail.append({
-                "proj": c.name, "M": M, "N": c.N, "K": c.K, "weight_bytes": wb,
-                "variant": F.nvfp4_gemv_variant(M, c.N, c.K),
-                "gemv_us": round(gus, 3),
-                "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1),
-                "gemv_hbm_frac": round(wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                # estimated VALU issue utilisation (the secondary ceiling at larger M)
-                "valu_util_est": round(valu_ops_per_element(F.nvfp4_gemv_variant(M, c.N, c.K), M) * c.N * c.K
-                                       / (gus * 1e-6) / VALU_LANE_OPS_PER_S, 3),
-                "quant_us": round(qus, 3),
-            })
-            gemv_bytes += wb
-            gemv_us += gus
-            log(args, f"[kern] {c.name:18s} M={M} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s "
-                      f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s, VALU est "
-                      f"{detail[-1]['valu_util_est'] * 100:4.1f}%)  quant {qus:6.2f} us")
+    detail = time_cases(args, stream, cases, wq, acts, M_LIST, with_valu=True)
+    gemv_bytes = sum(d["weight_bytes"] for d in detail)
+    gemv_us = sum(d["gemv_us"] for d in detail)
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
 
     extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4), "token_scales": token_scales}
     if not args.no_wide:
         # 16, 32, 64 and 128 tokens (1, 2, 4 or 8 16-token MFMA column tiles): the
         # same per-kernel timing, outside the step and the roofline figures
-        wide = []
-        for Mw in M_WIDE:
-            for c in cases:
-                gus = b2b(lambda i: gemv(c, Mw, i))
-                qus = b2b(lambda i: quant(c, Mw))
-                wb = weight_bytes(c.N, c.K)
-                wide.append({"proj": c.name, "M": Mw, "N": c.N, "K": c.K,
-                             "variant": F.nvfp4_gemv_variant(Mw, c.N, c.K), "gemv_us": round(gus, 3),
-                             "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1), "quant_us": round(qus, 3)})
-                log(args, f"[kern] {c.name:18s} M={Mw} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s  "
-                          f"quant {qus:6.2f} us")
-        extra["wide"] = wide
+        extra["wide"] = time_cases(args, stream, cases, wq, acts, M_WIDE)
+    copies_rotated = {c.name: len(wq[c.name]) for c in cases}
+    del wq, acts
+    torch.cuda.empty_cache()
+
+    # ---------------- measured read-stream ceiling ----------------
+    import workloads as W
+
+    small_cases = [W.single_case()] + W.qwen3_8b_cases()
+    sizes = {weight_bytes(c.N, c.K) for c in cases + small_cases}
+    if not args.no_lmhead:
+        sizes.add(weight_bytes(W.lm_head_case().N, W.lm_head_case().K))
+    ceiling = read_ceiling(args, stream, sizes) if not args.no_probe else {}
+    for d in detail:
+        _attach_ceiling(d, ceiling)
+    probe_us = sum(ceiling[d["weight_bytes"]]["us"] for d in detail) if ceiling else None
+    extra["read_ceiling"] = {str(k): v for k, v in sorted(ceiling.items())}
+
+    # ---------------- the 4096 x 4096 GEMV and the Qwen3-8B projections ----------------
+    if not args.no_small:
+        sc, swq, sacts, _ = setup(args, small_cases, M_LIST)
+        small = time_cases(args, stream, sc, swq, sacts, M_LIST)
+        for d in small:
+            _attach_ceiling(d, ceiling)
+        extra["single_4096"] = [d for d in small if d["proj"] == "square_4096"]
+        extra["qwen3_8b"] = [d for d in small if d["proj"] != "square_4096"]
+        del swq, sacts
+        torch.cuda.empty_cache()
+
     if not args.no_lmhead:
         extra["lm_head"] = bench_lm_head(args, stream)
     if not args.no_chain:
@@ -391,7 +394,7 @@ def main():
                         "quantization + GEMV for each (projection, M)",
             "global_batch": list(M_LIST),
             "weight_bytes_per_step": bytes_per_step,
-            "weight_copies_rotated": {c.name: len(wq[c.name]) for c in cases},
+            "weight_copies_rotated": copies_rotated,
             "parallelism": "single-gpu",
         },
         "roofline": {
@@ -400,6 +403,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "measured_ceiling": None if probe_us is None else round(gemv_bytes / (probe_us * 1e-6) / 1e9, 1),
+            "frac_of_measured_ceiling": None if probe_us is None else round(probe_us / gemv_us, 4),
+            "measured_ceiling_note": "the fastest plain read of each case's weight bytes on this GPU (probe library: "
+                                     "best of its register-ring and LDS-ring variants over 256..2048 workgroups, timed "
+                                     "like the GEMVs, rotated past the caches), summed over the 16 cases",
             "traffic": measured_traffic(),
             "traffic_unit": "HBM bytes read + written by the 16 GEMV launches of one step (rocprofv3 "
                             "FETCH_SIZE / WRITE_SIZE, copy-calibrated)",
@@ -413,6 +421,85 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_cases(args, stream, cases, wq, acts, Ms, with_valu=False):
+    """Per-kernel duration of the GEMV and of the activation quantization of
+    every (case, M): `reps` back-to-back launches captured in one graph (each
+    GEMV on the next packed copy of its weights), 7 timed replays."""
+    import fp4_decode_gemv_amd as F
+
+    def gemv(c, M, copy):
+        x, aq, ws, gws, y = acts[(c.name, M)]
+        copies = wq[c.name]
+        F.nvfp4_gemv_smallm(aq, copies[copy % len(copies)], y=y, ws=gws, stream=stream)
+
+    def quant(c, M):
+        x, aq, ws, gws, y = acts[(c.name, M)]
+        F.nvfp4_quantize_act(x, ws=ws, out=aq, stream=stream)
+
+    def b2b(fn):
+        return _graph_us(fn, args.reps, stream, replays=7)  # >= 200 timed dispatches per case
+
+    rows = []
+    for c in cases:
+        for M in Ms:
+            gus = b2b(lambda i: gemv(c, M, i))
+            qus = b2b(lambda i: quant(c, M))
+            wb = weight_bytes(c.N, c.K)
+            v = F.nvfp4_gemv_variant(M, c.N, c.K)
+            d = {"proj": c.name, "M": M, "N": c.N, "K": c.K, "weight_bytes": wb, "variant": v,
+                 "gemv_us": round(gus, 3), "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1),
+                 "gemv_hbm_frac": round(wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "quant_us": round(qus, 3)}
+            if with_valu:
+                # estimated VALU issue utilisation (the secondary ceiling at larger M)
+                d["valu_util_est"] = round(valu_ops_per_element(v, M) * c.N * c.K / (gus * 1e-6) / VALU_LANE_OPS_PER_S, 3)
+            rows.append(d)
+            log(args, f"[kern] {c.name:18s} M={M:<3d} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s "
+                      f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us  {v}")
+    return rows
+
+
+def read_ceiling(args, stream, sizes):
+    """For each byte count: the fastest plain read of that many bytes (the
+    probe library's register-ring and LDS-ring variants over 256..2048
+    workgroups), each launch on the next copy of a rotation past the caches,
+    timed like the GEMVs."""
+    import torch
+
+    from fp4_decode_gemv_amd import probe as P
+
+    names = P.read_variants()
+    cand = [names.index(n) for n in ("vgpr_u2_1", "vgpr_u4_1", "vgpr_u8_1", "vgpr_u16_1", "lds_d4") if n in names]
+    pool_bytes = 1400 << 20
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda:0")
+    pool.fill_(1)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for nb in sorted(sizes):
+        b16 = nb // 16 * 16  # the probe reads whole 16-byte units (the 4-byte global scale left out)
+        stride = (b16 + 4095) // 4096 * 4096
+        ncop = max(1, pool_bytes // stride)
+        reps = min(ncop, max(20, math.ceil(600e6 / b16)))
+        best = None
+        for vi in cand:
+            for grid in (256, 512, 1024, 2048):
+                us = _graph_us(lambda i: P.read(vi, pool[(i % ncop) * stride:], b16, grid, sink, stream), reps, stream)
+                if best is None or us < best[0]:
+                    best = (us, names[vi], grid)
+        out[nb] = {"us": round(best[0], 3), "gbs": round(nb / (best[0] * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(nb / (best[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "variant": best[1], "grid": best[2]}
+        log(args, f"[ceiling] {nb / 1e6:8.2f} MB: {best[0]:7.2f} us {out[nb]['gbs']:7.0f} GB/s ({best[1]}, grid {best[2]})")
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
+def _attach_ceiling(d, ceiling):
+    c = ceiling.get(d["weight_bytes"])
+    if c:
+        d["read_ceiling_us"] = c["us"]
+        d["frac_of_read_ceiling"] = round(c["us"] / d["gemv_us"], 4)
 
 
 def _replay_us(g, reps, stream, replays=5):
@@ -432,7 +519,7 @@ def _replay_us(g, reps, stream, replays=5):
     return e0.elapsed_time(e1) * 1e3 / (reps * replays)
 
 
-def _graph_us(fn, reps, stream):
+def _graph_us(fn, reps, stream, replays=5):
     """Capture `reps` calls of fn(i) in a graph on `stream` and time it."""
     import torch
 
@@ -444,7 +531,7 @@ def _graph_us(fn, reps, stream):
         for i in range(reps):
             fn(i)
     torch.cuda.synchronize()
-    us = _replay_us(g, reps, stream)
+    us = _replay_us(g, reps, stream, replays)
     del g
     return us
 
@@ -587,7 +674,8 @@ def bench_chain(args, stream):
 
 def cpu_baseline(args, cases, samples):
     """Time the oracle on the host: activation quantization plus dequantize +
-    fp64 GEMV over a row sample of each projection (M = 1..8 as in a step)."""
+    fp64 GEMV over a row sample of each projection (M = 1..8 as in a step),
+    with the median time of every (projection, M) case."""
     from oracle import nvfp4_oracle as O
     import workloads as W
 
@@ -599,13 +687,15 @@ def cpu_baseline(args, cases, samples):
         w, amax = samples[c.name]
         packed[c.name] = O.quantize_nvfp4(w, O.global_scale(amax))
     xs = {(c.name, M): W.case_activations_bf16(c, M) for c in cases for M in M_LIST}
-    runs = []
+    runs, per_case = [], {(c.name, M): [] for c in cases for M in M_LIST}
     for _ in range(7):
         t0 = time.perf_counter()
         for M in M_LIST:
             for c in cases:
+                tc = time.perf_counter()
                 aq = O.quantize_act_bf16(xs[(c.name, M)])
                 O.gemv_ref(aq, packed[c.name])
+                per_case[(c.name, M)].append(time.perf_counter() - tc)
         runs.append(time.perf_counter() - t0)
         if len(runs) >= 3 and time.perf_counter() - t_start > args.cpu_seconds:
             break
@@ -617,6 +707,12 @@ def cpu_baseline(args, cases, samples):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         threads = os.cpu_count()
+    cases_out = []
+    for c in cases:
+        for M in M_LIST:
+            tc = float(np.median(per_case[(c.name, M)]))
+            cases_out.append({"proj": c.name, "M": M, "rows": rows, "us": round(tc * 1e6, 1),
+                              "gbs": round(weight_bytes(rows, c.K) / tc / 1e9, 4)})
     return {
         "value": round(sample_bytes / t / 1e9, 4),
         "unit": "GB/s",
@@ -625,6 +721,7 @@ def cpu_baseline(args, cases, samples):
         "sample": f"first {rows} weight rows of each of the 4 projections x M in {{1,2,4,8}} "
                   f"(activation quantization + dequantize + fp64 GEMV), median of {len(runs)} runs, "
                   f"{t * 1e3:.0f} ms per sampled step; host {os.cpu_count()} logical CPUs",
+        "cases": cases_out,
     }
 
 
