@@ -63,8 +63,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "c08a3dbac0500ba65b89f26d10ac67042e04c6d2966e05183a6d216e595920fe",
-    "bytes_per_step": 1108297068,
+    "sha256": "e9606b85c1c17c2c595f4480c7dde37385b6fab27d9139c83402d4d0b02e12b1",
+    "bytes_per_step": 1115671461,
 }
 
 
@@ -135,8 +135,19 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="at the end, fill and copy a buffer of this many MiB three times: a plain copy of "
                          "known size to calibrate hardware byte counters against")
+    ap.add_argument("--proj", default=None,
+                    help="comma-separated subset of the projections (qkv,o,gate_up,down) for the step and the "
+                         "per-kernel timings, e.g. for a counter profile of a few cases; default: all four")
+    ap.add_argument("--m", default=None,
+                    help="comma-separated subset of the token counts 1,2,4,8; default: all four")
     ap.add_argument("--quiet", action="store_true")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.m_list = M_LIST if args.m is None else tuple(int(v) for v in args.m.split(","))
+    if not set(args.m_list) <= set(M_LIST):
+        ap.error(f"--m takes values out of {M_LIST}")
+    args.proj_list = None if args.proj is None else tuple(args.proj.split(","))
+    args.subset = args.m is not None or args.proj is not None
+    return args
 
 
 def log(args, *a):
@@ -154,9 +165,12 @@ def setup(args, cases=None, Ms=None):
 
     dev = torch.device("cuda:0")
     if cases is None:
-        cases = W.qwen3_32b_cases()
+        cases = [c for c in W.qwen3_32b_cases()
+                 if args.proj_list is None or any(c.name in (p, "qwen3_32b_" + p) for p in args.proj_list)]
+        if not cases:
+            raise SystemExit(f"--proj matches none of {[c.name for c in W.qwen3_32b_cases()]}")
     if Ms is None:
-        Ms = M_LIST + (M_WIDE if not args.no_wide else ())
+        Ms = args.m_list + (M_WIDE if not args.no_wide else ())
     wq = {}      # name -> list of NvFp4Tensor copies
     samples = {}  # name -> (first CPU_ROWS rows of W, global scale of the whole W)
     for c in cases:
@@ -235,7 +249,7 @@ def main():
         # the four launches of a projection in a step read four different
         # packed copies; between two reads of one copy a whole step (1.1 GB of
         # other weights) goes by, so a replayed step finds nothing in a cache
-        for mi, M in enumerate(M_LIST):
+        for mi, M in enumerate(args.m_list):
             for c in cases:
                 quant(c, M)
                 gemv(c, M, mi)
@@ -263,7 +277,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    bytes_per_step = sum(weight_bytes(c.N, c.K) for c in cases) * len(M_LIST)
+    bytes_per_step = sum(weight_bytes(c.N, c.K) for c in cases) * len(args.m_list)
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     log(args, f"[bench] {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s effective (quantization included)")
     del g_step
@@ -271,10 +285,10 @@ def main():
     # the same step with one activation global scale per token (the
     # quantization's per-token option, which needs no tensor-wide amax; not
     # the metric's per-tensor recipe, so it is reported apart from `value`)
-    tok_out = {k: F.nvfp4_quantize_act(v[0], per_token=True) for k, v in acts.items() if k[1] in M_LIST}
+    tok_out = {k: F.nvfp4_quantize_act(v[0], per_token=True) for k, v in acts.items() if k[1] in args.m_list}
 
     def step_token():
-        for mi, M in enumerate(M_LIST):
+        for mi, M in enumerate(args.m_list):
             for c in cases:
                 x, _, _, gws, y = acts[(c.name, M)]
                 at = tok_out[(c.name, M)]
@@ -316,7 +330,7 @@ def main():
     # average is the kernel's duration as a decode step runs it (it agrees
     # with rocprofv3's per-dispatch durations); host launch overhead is not
     # in it.
-    detail = time_cases(args, stream, cases, wq, acts, M_LIST, with_valu=True)
+    detail = time_cases(args, stream, cases, wq, acts, args.m_list, with_valu=True)
     gemv_bytes = sum(d["weight_bytes"] for d in detail)
     gemv_us = sum(d["gemv_us"] for d in detail)
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
@@ -392,10 +406,11 @@ def main():
             "workload": "Qwen3-32B decode projections, NVFP4 W4A4: qkv 10240x5120, o 5120x8192, "
                         "gate_up 51200x5120, down 5120x25600; M in {1,2,4,8}; one step = activation "
                         "quantization + GEMV for each (projection, M)",
-            "global_batch": list(M_LIST),
+            "global_batch": list(args.m_list),
             "weight_bytes_per_step": bytes_per_step,
             "weight_copies_rotated": copies_rotated,
             "parallelism": "single-gpu",
+            **({"subset": {"proj": list(args.proj_list or ()), "m": list(args.m_list)}} if args.subset else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -612,8 +627,9 @@ def bench_lm_head(args, stream):
 
 def bench_chain(args, stream):
     """64 Qwen3-32B layers x 4 projections (17.55 GB of packed weights)
-    captured in one hipGraph; microseconds per decode step at M = 1 and 8,
-    with the activation quantization and GEMV-only."""
+    captured in one hipGraph; microseconds per decode step at M = 1 and 8:
+    with the dynamic per-tensor, dynamic per-token or static activation
+    quantization before each GEMV, and GEMV-only."""
     import torch
 
     import fp4_decode_gemv_amd as F
@@ -641,30 +657,38 @@ def bench_chain(args, stream):
                 x = torch.from_numpy(W.chain_activations_bf16(l, p, M).view(np.int16)).to(dev).view(torch.bfloat16)
                 aq = F.nvfp4_quantize_act(x)
                 at = F.nvfp4_quantize_act(x, per_token=True)
+                # a calibrated (static) global scale: the dynamic one of this input, taken once
+                ast = F.nvfp4_quantize_act(x, gscale=aq.gscale.clone())
                 qn = F.nvfp4_workspace_size(F.NVFP4_OP_QUANT, M, 0, c.K)
                 gn = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, c.N, c.K)
-                io[(l, p)] = (x, aq, at, F.new_workspace(qn, dev) if qn else None,
+                io[(l, p)] = (x, aq, at, ast, F.new_workspace(qn, dev) if qn else None,
                               F.new_workspace(gn, dev) if gn else None, torch.empty((M, c.N), device=dev))
         res = {"M": M, "weight_bytes": total}
-        # per-tensor quantization + GEMV, per-token quantization + GEMV, GEMV alone
-        for key in ("quant_gemv", "token_quant_gemv", "gemv_only"):
+        # per-tensor dynamic quantization + GEMV, per-token dynamic quantization
+        # + GEMV, static (calibrated) per-tensor scale + GEMV, GEMV alone
+        for key in ("quant_gemv", "token_quant_gemv", "static_quant_gemv", "gemv_only"):
             def step(_i):
                 for l in range(W.CHAIN_LAYERS):
                     for p in range(4):
-                        x, aq, at, qws, gws, y = io[(l, p)]
+                        x, aq, at, ast, qws, gws, y = io[(l, p)]
+                        a = aq
                         if key == "quant_gemv":
                             F.nvfp4_quantize_act(x, ws=qws, out=aq, stream=stream)
                         elif key == "token_quant_gemv":
                             F.nvfp4_quantize_act(x, out=at, stream=stream, per_token=True)
-                        F.nvfp4_gemv_smallm(at if key == "token_quant_gemv" else aq, ws[(l, p)], y=y, ws=gws,
-                                            stream=stream)
+                            a = at
+                        elif key == "static_quant_gemv":
+                            F.nvfp4_quantize_act(x, gscale=ast.gscale, out=ast, stream=stream)
+                            a = ast
+                        F.nvfp4_gemv_smallm(a, ws[(l, p)], y=y, ws=gws, stream=stream)
             us = _graph_us(step, 1, stream)
             res[key + "_us_per_step"] = round(us, 1)
             res[key + "_gbs"] = round(total / us / 1e3, 1)
         out.append(res)
         log(args, f"[chain] M={M} {res['quant_gemv_us_per_step']:.1f} us/step with quantization "
                   f"({res['quant_gemv_gbs']:.0f} GB/s), {res['token_quant_gemv_us_per_step']:.1f} us with "
-                  f"per-token scales, {res['gemv_only_us_per_step']:.1f} us GEMV only "
+                  f"per-token scales, {res['static_quant_gemv_us_per_step']:.1f} us with a static scale, "
+                  f"{res['gemv_only_us_per_step']:.1f} us GEMV only "
                   f"({res['gemv_only_gbs']:.0f} GB/s)")
         del io
     del ws
@@ -686,11 +710,11 @@ def cpu_baseline(args, cases, samples):
     for c in cases:
         w, amax = samples[c.name]
         packed[c.name] = O.quantize_nvfp4(w, O.global_scale(amax))
-    xs = {(c.name, M): W.case_activations_bf16(c, M) for c in cases for M in M_LIST}
-    runs, per_case = [], {(c.name, M): [] for c in cases for M in M_LIST}
+    xs = {(c.name, M): W.case_activations_bf16(c, M) for c in cases for M in args.m_list}
+    runs, per_case = [], {(c.name, M): [] for c in cases for M in args.m_list}
     for _ in range(7):
         t0 = time.perf_counter()
-        for M in M_LIST:
+        for M in args.m_list:
             for c in cases:
                 tc = time.perf_counter()
                 aq = O.quantize_act_bf16(xs[(c.name, M)])
@@ -700,7 +724,7 @@ def cpu_baseline(args, cases, samples):
         if len(runs) >= 3 and time.perf_counter() - t_start > args.cpu_seconds:
             break
     t = float(np.median(runs))
-    sample_bytes = sum(weight_bytes(rows, c.K) for c in cases) * len(M_LIST)
+    sample_bytes = sum(weight_bytes(rows, c.K) for c in cases) * len(args.m_list)
     try:
         from threadpoolctl import threadpool_info
 
@@ -709,7 +733,7 @@ def cpu_baseline(args, cases, samples):
         threads = os.cpu_count()
     cases_out = []
     for c in cases:
-        for M in M_LIST:
+        for M in args.m_list:
             tc = float(np.median(per_case[(c.name, M)]))
             cases_out.append({"proj": c.name, "M": M, "rows": rows, "us": round(tc * 1e6, 1),
                               "gbs": round(weight_bytes(rows, c.K) / tc / 1e9, 4)})

@@ -352,11 +352,11 @@ def variant_tokens(name: str) -> int:
 def variant_k_multiple(name: str) -> int:
     """K granularity a variant needs: the streaming kernels (``stream_*``,
     ``fstream_*``) stream whole 512-element chunks, the direct-to-LDS kernels
-    (``dma_*``, ``staged_*``, ``fmma_*``) copy whole 256-element steps, every
-    other kernel 32-element chunks."""
+    (``dma_*``, ``staged_*``, ``fmma_*``) and the tiled GEMM (``gemm_*``)
+    copy whole 256-element steps, every other kernel 32-element chunks."""
     if name.startswith(("stream_", "fstream_")):
         return 512
-    return 256 if name.startswith(("dma_", "staged_", "fmma_")) else 32
+    return 256 if name.startswith(("dma_", "staged_", "fmma_", "gemm_")) else 32
 
 
 def nvfp4_reset_state_size(window: int) -> int:

@@ -100,6 +100,7 @@ struct GemvParams {
   // LM-head epilogue (used only by the EPI instantiations)
   EpilogueArgs epi;
   float* partials;         // epilogue: [row tiles][MT][4] = {max, S, T, -}
+  uint32_t* tickets;       // epilogue: [kMaxTokens] per-token counters, zero at rest
   size_t state_bytes;      // bytes per ReSET state
   // weight rows per workgroup of the MFMA kernels (<= 16 R): workgroup b
   // owns rows [b * tile_rows, (b + 1) * tile_rows); rows of its 16 R-row
@@ -265,20 +266,28 @@ __device__ __forceinline__ void lmhead_partials(const GemvParams& p, const float
   }
 }
 
-// LM-head epilogue, parts 2 and 3 (two launches after the GEMV; no atomics
-// or fences, which on gfx950 cost a write-back of the whole L2 per release):
-//   lmhead_slice_kernel: kMergeGroups workgroups per token each merge a
-//     contiguous slice of the token's row-tile partials in a fixed order and
-//     write one slice partial;
-//   lmhead_merge_kernel: one wave per token merges its kMergeGroups slice
-//     partials in a fixed order, computes H = log S - T/S (natural log) and
-//     runs the ReSET update of the token's sequence state.
-// Workspace: the row-tile partials [ntiles][MT], then [MT][kMergeGroups]
-// slice partials, all float4 {max, S, T, -}.
+// LM-head epilogue, part 2 (one launch after the GEMV): kMergeGroups
+// workgroups per token each merge a contiguous slice of the token's row-tile
+// partials in a fixed order and publish one slice partial; the token's last
+// slice workgroup to finish merges the kMergeGroups slice partials in index
+// order, computes H = log S - T/S (natural log) and runs the ReSET update of
+// the token's sequence state.  "Last" comes from a per-token ticket counter
+// that the last workgroup puts back to zero, so the counters need no clearing
+// between calls (and no memset node in a captured graph).  The slice
+// partials are written and read with device-scope atomic accesses (they go
+// past the per-XCD L2s), and the ticket is taken only after the write has
+// completed, so no release fence is needed (on gfx950 a release writes back
+// the whole L2).
+// Workspace: kEpiTicketBytes of tickets [kMaxTokens] (zero at rest), the
+// row-tile partials [ntiles][MT], then the slice partials [MT][kMergeGroups],
+// all float4 {max, S, T, -}.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = 64;
 constexpr int kMergeLoads = 4;  // partials per thread and round, all loads in flight at once
+constexpr int64_t kEpiTicketBytes = 512;
+static_assert(kEpiTicketBytes >= 4 * kMaxTokens, "one ticket per token");
 
+// offset of the slice partials from the row-tile partials
 __host__ __device__ constexpr int64_t merge_slices_offset(int64_t ntiles, int mt) {
   return (ntiles * mt * 16 + 255) / 256 * 256;
 }
@@ -291,10 +300,11 @@ __device__ __forceinline__ void merge_from_lane(float& m, float& S, float& T, in
 
 __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams p, int mt, int ntiles) {
   __shared__ float wm[kMergeThreads / 64], wS[kMergeThreads / 64], wt[kMergeThreads / 64];
+  __shared__ uint32_t is_last;
   const int m = blockIdx.x / kMergeGroups, grp = blockIdx.x % kMergeGroups;
   if (m >= p.M) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float4_t* slices = reinterpret_cast<float4_t*>(reinterpret_cast<char*>(p.partials) + merge_slices_offset(ntiles, mt));
+  float* slices = reinterpret_cast<float*>(reinterpret_cast<char*>(p.partials) + merge_slices_offset(ntiles, mt));
   // this workgroup's slice of tiles; thread t takes lo + t, lo + t + NT, ...
   const int per = (ntiles + kMergeGroups - 1) / kMergeGroups;
   const int lo = grp * per, hi = lo + per < ntiles ? lo + per : ntiles;
@@ -326,22 +336,30 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams 
     wt[wave] = Tm;
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
-  for (int w = 1; w < kMergeThreads / 64; ++w) merge_partial(gm, Sm, Tm, wm[w], wS[w], wt[w]);
-  slices[(int64_t)m * kMergeGroups + grp] = float4_t{gm, Sm, Tm, 0.0f};
-}
-
-__global__ __launch_bounds__(64) void lmhead_merge_kernel(GemvParams p, int mt, int ntiles) {
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kMergeThreads / 64; ++w) merge_partial(gm, Sm, Tm, wm[w], wS[w], wt[w]);
+    float* sp = slices + ((int64_t)m * kMergeGroups + grp) * 4;
+    __hip_atomic_store(sp, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sp + 1, Sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sp + 2, Tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the slice partial has landed
+    const uint32_t done = __hip_atomic_fetch_add(&p.tickets[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = done == kMergeGroups - 1 ? 1u : 0u;
+    if (done == kMergeGroups - 1) __hip_atomic_store(&p.tickets[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (is_last == 0 || wave != 0) return;
+  // the token's last slice workgroup, wave 0: lane g takes slice g, then the
+  // butterfly in a fixed order (the result does not depend on which
+  // workgroup came last)
+  const float* sp = slices + ((int64_t)m * kMergeGroups + lane) * 4;
+  gm = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  Sm = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  Tm = __hip_atomic_load(sp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   static_assert(kMergeGroups == 64, "one slice partial per lane of a wave");
-  const int m = blockIdx.x;
-  if (m >= p.M) return;
-  const float4_t* slices =
-      reinterpret_cast<const float4_t*>(reinterpret_cast<const char*>(p.partials) + merge_slices_offset(ntiles, mt));
-  const float4_t sp = slices[(int64_t)m * kMergeGroups + threadIdx.x];
-  float gm = sp[0], Sm = sp[1], Tm = sp[2];
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) merge_from_lane(gm, Sm, Tm, x);
-  if (threadIdx.x != 0) return;
+  if (lane != 0) return;
   const double Sd = Sm, Td = Tm;
   const float H = (float)(log(Sd) - Td / Sd);
   p.epi.entropy[m] = H;
@@ -2172,10 +2190,231 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 }
 
 // ----------------------------------------------------------------------------
+// Tiled MFMA GEMM for 17..128 tokens
+// ----------------------------------------------------------------------------
+// At 17..128 tokens the projection is a small GEMM (the pages route large M
+// to a dedicated GEMM, reading notes section 7.3): every decoded weight
+// element now feeds up to 128 products, so the bound is the MFMA and decode
+// work per byte as much as HBM.  A workgroup of 4 waves owns kGemmRows = 128
+// weight rows and all MT (32, 64 or 128) token columns.  The K loop runs in
+// stages of 256 elements: the stage's raw NVFP4 bytes (weight codes
+// [128][128 B], weight block scales [128][16 B], activation codes [MT][128 B]
+// and scales [MT][16 B]) are copied into one of two LDS buffers with
+// direct-to-LDS loads while the waves compute on the other buffer.  Waves
+// split the tile as a WR x WC grid (rows x token groups); each decodes its
+// weight rows and tokens from LDS to exact f16 values (E2M1 x E4M3 has at
+// most 6 significant bits) in registers and runs v_mfma_f32_16x16x32_f16 on
+// 16-row x 16-token tiles, so the products are exact and only the f32
+// accumulation rounds.
+// K order inside a stage: a 128-element half-stage of a row is 64 bytes;
+// lane (j, g) (j = lane % 16 the row or token of the 16-tile, g = lane / 16)
+// reads the 16 bytes at 16 g with one LDS load and feeds word q of them to
+// k-step q (q = 0..3).  Both operands use the same order, so each k-step
+// sums 32 distinct elements and the four k-steps cover the half-stage.  The
+// code rows are stored XOR-swizzled (16-byte window w of row r at slot
+// 8 r + (w ^ (r & 7))) so that the 16 lanes reading one window of 16 rows
+// spread over the LDS banks; the copy takes the permutation in its global
+// offsets.  Rows past N and tokens past M are copied from outside the
+// buffers (zeros) and never stored.
+constexpr int kGemmRows = 128;        // weight rows per workgroup
+constexpr int kGemmStageK = 256;      // K elements per stage
+constexpr int kGemmThreads = 256;     // 4 waves
+
+__host__ __device__ constexpr int gemm_stage_bytes(int mt) {
+  // weight codes, weight scales, activation codes, activation scales (each
+  // region a whole number of 1 KB copy instructions)
+  return kGemmRows * 128 + 2048 + (mt * 128 < 1024 ? 1024 : mt * 128) + (mt * 16 < 1024 ? 1024 : mt * 16);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vmcnt<N>();
+      return;
+    }
+    wait_vmcnt_le<N - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// The copies of one stage: kGemmCopies(MT) 1 KB direct-to-LDS loads (weight
+// codes, weight scales, activation codes, activation scales), dealt to the 4
+// waves round robin.  A copy's per-lane source offset and LDS offset do not
+// depend on the stage (the stage is the scalar offset), so each wave works
+// them out once, before the K loop.
+template <int MT>
+struct GemmCopies {
+  static constexpr int WC = kGemmRows * 128 / 1024;  // weight-code copies (16)
+  static constexpr int WS = 2;                       // weight scales: 128 rows x 16 B
+  static constexpr int AC = MT * 128 < 1024 ? 1 : MT * 128 / 1024;
+  static constexpr int AS = MT * 16 < 1024 ? 1 : MT * 16 / 1024;
+  static constexpr int TOTAL = WC + WS + AC + AS;
+  static constexpr int PER_WAVE = (TOTAL + kGemmThreads / 64 - 1) / (kGemmThreads / 64);
+};
+
+template <int MT>
+struct GemmCopyPlan {
+  int voff[GemmCopies<MT>::PER_WAVE];  // per-lane source offset (kOffOut: outside the buffer)
+  int n;                               // copies this wave issues per stage (wave-uniform)
+};
+
+template <int MT>
+__device__ __forceinline__ GemmCopyPlan<MT> gemm_copy_plan(int64_t K, int rows, int M, int wave, int lane) {
+  using C = GemmCopies<MT>;
+  const int kh = (int)(K / 2), ks = (int)(K / 16);
+  GemmCopyPlan<MT> pl;
+  pl.n = 0;
+#pragma unroll
+  for (int i = 0; i < C::PER_WAVE; ++i) {
+    const int ch = wave + 4 * i;
+    int v = (int)kOffOut;
+    if (ch < C::WC) {
+      const int s = 64 * ch + lane, r = s >> 3, w = (s & 7) ^ (r & 7);
+      if (r < rows) v = r * kh + 16 * w;
+    } else if (ch < C::WC + C::WS) {
+      const int r = 64 * (ch - C::WC) + lane;
+      if (r < rows) v = r * ks;
+    } else if (ch < C::WC + C::WS + C::AC) {
+      const int s = 64 * (ch - C::WC - C::WS) + lane, t = s >> 3, w = (s & 7) ^ (t & 7);
+      if (t < M && t < MT) v = t * kh + 16 * w;
+    } else if (ch < C::TOTAL) {
+      const int t = 64 * (ch - C::WC - C::WS - C::AC) + lane;
+      if (t < M && t < MT) v = t * ks;
+    }
+    pl.voff[i] = v;
+    if (ch < C::TOTAL) ++pl.n;
+  }
+  return pl;
+}
+
+// Issue this wave's copies of stage `st` into the stage buffer at LDS `dst`.
+// The copy regions are contiguous in the order weight codes, weight scales,
+// activation codes, activation scales, so copy ch lands at dst + 1 KB * ch.
+template <int MT>
+__device__ __forceinline__ void gemm_stage_copy(const GemmCopyPlan<MT>& pl, const i32x4_t& wcr, const i32x4_t& wsr,
+                                                const i32x4_t& acr, const i32x4_t& asr, uint32_t dst, int st,
+                                                int wave) {
+  using C = GemmCopies<MT>;
+#pragma unroll
+  for (int i = 0; i < C::PER_WAVE; ++i) {
+    const int ch = wave + 4 * i;  // wave-uniform
+    if (ch < C::WC)
+      dma_b128(wcr, dst + 1024 * ch, pl.voff[i], st * 128);
+    else if (ch < C::WC + C::WS)
+      dma_b128(wsr, dst + 1024 * ch, pl.voff[i], st * 16);
+    else if (ch < C::WC + C::WS + C::AC)
+      dma_b128(acr, dst + 1024 * ch, pl.voff[i], st * 128);
+    else if (ch < C::TOTAL)
+      dma_b128(asr, dst + 1024 * ch, pl.voff[i], st * 16);
+  }
+}
+
+// 32 codes of row (or token) r, window w, of a stage's swizzled code region,
+// with the two block scales of its 16-element halves, decoded to four f16
+// operands (one per k-step)
+__device__ __forceinline__ void gemm_load_decode(const char* codes, const char* scales, int r, int seg, int g,
+                                                 half8_t (&out)[4]) {
+  const int w = 4 * seg + g;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(codes + 16 * (8 * r + (w ^ (r & 7))));
+  const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales + 16 * r + 8 * seg + 2 * g);
+  decode32_scaled(v, s2, out);
+}
+
+template <int MT>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
+  constexpr int WR = MT >= 128 ? 2 : 4;  // wave grid: WR row groups x WC token groups
+  constexpr int WC = 4 / WR;
+  constexpr int RT = kGemmRows / WR / 16;  // 16-row tiles per wave
+  constexpr int CT = MT / WC / 16;         // 16-token tiles per wave
+  constexpr int STAGE = gemm_stage_bytes(MT);
+  extern __shared__ uint4 lds4[];
+  char* lds = reinterpret_cast<char*>(lds4);
+  const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(lds);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int wr = wave % WR, wc = wave / WR;
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * kGemmRows;
+  const int rows = N - tile0 < kGemmRows ? (int)(N - tile0) : kGemmRows;
+  const i32x4_t wcr = raw_rsrc(p.w_codes + tile0 * (K / 2), (int64_t)rows * (K / 2));
+  const i32x4_t wsr = raw_rsrc(p.w_scales + tile0 * (K / 16), (int64_t)rows * (K / 16));
+  const i32x4_t acr = raw_rsrc(p.a_codes, (int64_t)M * (K / 2));
+  const i32x4_t asr = raw_rsrc(p.a_scales, (int64_t)M * (K / 16));
+  const int nst = (int)(K / kGemmStageK);
+
+  float4_t acc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const GemmCopyPlan<MT> plan = gemm_copy_plan<MT>(K, rows, M, wave, lane);
+  gemm_stage_copy<MT>(plan, wcr, wsr, acr, asr, l0, 0, wave);
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    int ahead = 0;
+    if (st + 1 < nst) {
+      gemm_stage_copy<MT>(plan, wcr, wsr, acr, asr, l0 + (uint32_t)((buf ^ 1) * STAGE), st + 1, wave);
+      ahead = plan.n;
+    }
+    wait_vmcnt_le<GemmCopies<MT>::PER_WAVE>(ahead);  // this wave's copies of stage st have landed
+    __syncthreads();          // ... and every other wave's
+    const char* wcodes = lds + buf * STAGE;
+    const char* wscales = wcodes + kGemmRows * 128;
+    const char* acodes = wscales + 2048;
+    const char* ascales = acodes + (MT * 128 < 1024 ? 1024 : MT * 128);
+#pragma unroll
+    for (int seg = 0; seg < 2; ++seg) {
+      half8_t a[CT][4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) gemm_load_decode(acodes, ascales, wc * (MT / WC) + 16 * ct + j, seg, g, a[ct]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        half8_t w[4];
+        gemm_load_decode(wcodes, wscales, wr * (kGemmRows / WR) + 16 * rt + j, seg, g, w);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w[q], a[ct][q], acc[rt][ct], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the buffer is refilled two stages on
+  }
+  // lane (j, g) holds D[4 g + i][j]: weight rows 4 g .. 4 g + 3 of the tile
+  // for token j of the token tile
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int t = wc * (MT / WC) + 16 * ct + j;
+    if (t >= M) continue;
+    const float ts = token_scale(p, t);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = wr * (kGemmRows / WR) + 16 * rt + 4 * g;
+      float* y = p.y + (int64_t)t * N + tile0 + r;
+      if (r + 3 < rows && (N & 3) == 0) {
+        *reinterpret_cast<float4_t*>(y) = acc[rt][ct] * ts;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r + i < rows) y[i] = acc[rt][ct][i] * ts;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // Variant table
 // ----------------------------------------------------------------------------
 
-enum Kind { VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8, STREAM = 9, FSTREAM = 10 };
+enum Kind {
+  VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8, STREAM = 9,
+  FSTREAM = 10, GEMM = 11
+};
 
 struct Variant {
   const char* name;
@@ -2251,6 +2490,13 @@ struct Variant {
         gemv_fstream_kernel<R, NW, U, false>, gemv_fstream_kernel<R, NW, U, true>           \
   }
 
+// the tiled GEMM has no LM-head form: its epilogue slot repeats the plain
+// kernel and is never chosen (fits() refuses GEMM with the epilogue)
+#define GEMM_V(MT)                                                                    \
+  Variant {                                                                         \
+    "gemm_m" #MT, GEMM, MT, 16, kGemmRows / 16, kGemmThreads / 64, 0, gemm_kernel<MT>, gemm_kernel<MT> \
+  }
+
 // The launch table's variants and the fallbacks it uses where a choice does
 // not fit a shape (LDS size, K granularity, 32-bit buffer offsets).  Further
 // instantiations for sweeps can be compiled in by defining
@@ -2265,7 +2511,7 @@ const Variant kVariants[] = {
     FMMA_V(4, 2, 4, 3), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 1),
     // 9..128 tokens
     LMFMA_V(16, 2, 8, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(32, 2, 8, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(64, 2, 8, 1),
-    LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1),
+    LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1), GEMM_V(32), GEMM_V(64), GEMM_V(128),
     // fallbacks
     DIRECT_V(2, 64, 1, 4, 1), MFMA_V(4, 2, 8, 1), MFMA_V(8, 2, 8, 1), LMFMA_V(16, 1, 4, 1), LMFMA_V(32, 1, 4, 1),
     LMFMA_V(64, 1, 4, 1), LMFMA_V(128, 1, 4, 1),
@@ -2360,6 +2606,11 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
                ? i
                : otherwise;
   };
+  // 17..128 tokens on many rows (gate_up, N >= 16384): the tiled GEMM, whose
+  // 128-row workgroups then still fill the CUs (its LM-head form does not
+  // exist; the epilogue keeps the GEMV kernels)
+  if (M > 16 && !epi && N >= 16384 && K % kGemmStageK == 0)
+    return M > 64 ? VARIANT("gemm_m128") : M > 32 ? VARIANT("gemm_m64") : VARIANT("gemm_m32");
   // 65..128 tokens: eight 16-token column tiles; 33..64: four; 17..32: two;
   // 9..16: all 16 token columns of one tile (the register-staged MFMA kernel)
   if (M > 64) return VARIANT("lmfma_m128_r2_w4_p1");
@@ -2420,6 +2671,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     const Kind kd = v.kind;
     if ((kd == DMA || kd == DMASA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
     if ((kd == STREAM || kd == FSTREAM) && K % kStreamChunk != 0) return false;
+    if (kd == GEMM && (K % kGemmStageK != 0 || epi)) return false;
     // the LM-head instantiations also hold the static softmax slots
     // [MT][tile rows] of their partials
     const int64_t slot = epi ? (int64_t)4 * v.mt * epi_tile_rows(v) : 0;
@@ -2427,7 +2679,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     if ((kd == STREAM || kd == FSTREAM) && stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + slot > kLdsBytes)
       return false;
     if (kd == STAGED && staged_lds_bytes(v, K) > 65536) return false;
-    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != FSTREAM) ||
+    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != FSTREAM &&
+            kd != GEMM) ||
            (int64_t)16 * v.r * (K / 2) < (1ll << 31);
   };
   // tuning override, used when the forced variant's compiled token count
@@ -2453,7 +2706,12 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
-  if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA ||
+  if (v.kind == GEMM) {
+    c.kp = (int)K;
+    c.rows_per_wg = kGemmRows;
+    c.grid = (N + kGemmRows - 1) / kGemmRows;
+    c.lds_bytes = 2 * (int64_t)gemm_stage_bytes(v.mt);
+  } else if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA ||
       v.kind == STREAM || v.kind == FSTREAM) {
     c.kp = (int)K;
     const int64_t tile = (int64_t)(v.kind == STREAM || v.kind == FSTREAM ? 4 : 16) * v.r;  // rows of the kernel's tile
@@ -2491,9 +2749,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = v.kind == STAGED ? staged_lds_bytes(v, K) : 0;
   }
-  // workspace (epilogue only): per-workgroup softmax partials, then the
-  // merge's slice partials
-  c.ws_bytes = epi ? align256(merge_slices_offset(c.grid, c.mt) + (int64_t)c.mt * kMergeGroups * 16) : 0;
+  // workspace (epilogue only): the per-token tickets, per-workgroup softmax
+  // partials, then the slice partials
+  c.ws_bytes =
+      epi ? align256(kEpiTicketBytes + merge_slices_offset(c.grid, c.mt) + (int64_t)c.mt * kMergeGroups * 16) : 0;
   return c;
 }
 
@@ -2537,7 +2796,8 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   char* wsb = reinterpret_cast<char*>(ws);
   if (epi) {
     p.epi = *epi;
-    p.partials = reinterpret_cast<float*>(wsb);
+    p.tickets = reinterpret_cast<uint32_t*>(wsb);
+    p.partials = reinterpret_cast<float*>(wsb + kEpiTicketBytes);
     p.state_bytes = reset_state_bytes(epi->window);
   }
   const Variant& v = kVariants[cfg.variant];
@@ -2549,9 +2809,6 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_slice_kernel, dim3(M * kMergeGroups), dim3(kMergeThreads), 0, stream, p, cfg.mt,
                        (int)cfg.grid);
-    const hipError_t e2 = hipGetLastError();
-    if (e2 != hipSuccess) return e2;
-    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(M), dim3(64), 0, stream, p, cfg.mt, (int)cfg.grid);
   }
   return hipGetLastError();
 }

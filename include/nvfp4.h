@@ -39,9 +39,12 @@
  *   - Workspace `ws` is caller-owned device scratch of at least
  *     nvfp4_workspace_size(op, M, N, K) bytes; it must be zero-filled once
  *     after allocation (nvfp4_workspace_init does that with a kernel).
- *     It holds only per-call intermediates (no state carried between
- *     calls), so graph replays are safe.  Calls that share one workspace
- *     must be ordered on one stream.
+ *     It holds per-call intermediates, plus (the LM-head epilogue) one
+ *     ticket counter per token at its start that every call leaves at zero,
+ *     so graph replays are safe and no call needs the workspace cleared
+ *     again.  Calls that share one workspace must be ordered on one stream;
+ *     a call whose kernels did not run to completion can leave a ticket
+ *     non-zero, and the workspace must then be zero-filled again.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -212,7 +215,9 @@ int nvfp4_gemv_smallm_token_scales(int M, int64_t N, int64_t K,
  * that GPU's array: calls that can overlap on one GPU (different streams
  * without ordering, or threads) race and give undefined results; calls on
  * one stream are ordered.  The array keeps the last call's contents; no
- * call depends on them (every partial is written before it is read).
+ * call depends on them (every partial is written before it is read) except
+ * the epilogue's per-token ticket counters, which start at zero with the
+ * array and which every completed call leaves at zero.
  */
 int nvfp4_gemv_smallm_noalloc(int M, int64_t N, int64_t K,
                               const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,

@@ -44,6 +44,23 @@ def test_small_shapes_full_compare(M, N, K):
     assert_gemv_close(y, y_ref, ref_abs, what=f"M={M} N={N} K={K}")
 
 
+# the tiled GEMM as the launch table picks it (17..128 tokens, N >= 16384):
+# a ragged last 128-row tile, one stage and many stages of K, tokens below
+# and at each compiled token count
+GEMM_DEFAULT = [(17, 16500, 256), (32, 16500, 4352), (33, 16389, 1024), (64, 16389, 4352), (100, 16500, 512),
+                (128, 16389, 2304)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_DEFAULT)
+def test_gemm_default_full_compare(M, N, K):
+    assert F.nvfp4_gemv_variant(M, N, K).startswith("gemm_m")
+    w = W.small_random_weights(N * 3 + K + M, N, K)
+    xb = W.small_random_bf16(M * 17 + K, M, K)
+    wq, aq, y = _run(M, N, K, w, xb, F.nvfp4_gemv_variant(M, N, K))
+    y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+    assert_gemv_close(y, y_ref, ref_abs, what=f"gemm M={M} N={N} K={K}")
+
+
 def _full_size(case, Ms):
     w = W.weights(case.w_seed, case.N, case.K, case.w_outlier_rows)
     wt = f32_dev(w)
