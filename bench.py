@@ -32,8 +32,9 @@ Prints one JSON line:
                measured read ceiling), the four projections at M = 16, 32, 64
                and 128 (beyond the metric's M range; per-kernel times only),
                the LM head (N=151936) with the entropy / ReSET epilogue and the
-               top-p = 0.95 draw at the epilogue's temperatures, and the
-               64-layer decode chain captured in one graph
+               top-p = 0.95 draw at the epilogue's temperatures, the
+               64-layer decode chain captured in one graph, and the
+               rotation-fused quantization (Q+R) of the step's activations
 """
 
 from __future__ import annotations
@@ -336,6 +337,9 @@ def main():
     achieved = gemv_bytes / (gemv_us * 1e-6) / 1e9
 
     extra = {"eager_python_launch_ms_per_step": round(eager_ms, 4), "token_scales": token_scales}
+    # the rotation-fused quantization (Q+R) of the same activations, the
+    # pages' comparison point for the Q step
+    extra["q_plus_r"] = time_q_plus_r(args, stream, cases, acts, detail)
     if not args.no_wide:
         # 16, 32, 64 and 128 tokens (1, 2, 4 or 8 16-token MFMA column tiles): the
         # same per-kernel timing, outside the step and the roofline figures
@@ -472,6 +476,31 @@ def time_cases(args, stream, cases, wq, acts, Ms, with_valu=False):
             rows.append(d)
             log(args, f"[kern] {c.name:18s} M={M:<3d} gemv {gus:8.2f} us {wb / (gus * 1e-6) / 1e9:7.0f} GB/s "
                       f"({wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS * 100:4.1f}% of 8 TB/s)  quant {qus:6.2f} us  {v}")
+    return rows
+
+
+def time_q_plus_r(args, stream, cases, acts, detail):
+    """Per-launch time of the rotation-fused quantization (block Walsh-Hadamard
+    rotation of 16 and of 128 elements, then the NVFP4 recipe) next to the
+    plain quantization of the same (projection, M) cases."""
+    import fp4_decode_gemv_amd as F
+
+    q_us = {(d["proj"], d["M"]): d["quant_us"] for d in detail}
+    rows = []
+    for c in cases:
+        for M in args.m_list:
+            x, aq, ws, gws, y = acts[(c.name, M)]
+            row = {"proj": c.name, "M": M, "K": c.K, "quant_us": q_us[(c.name, M)]}
+            for R in (16, 128):
+                need = F.nvfp4_workspace_size(F.NVFP4_OP_QUANT_ROTATED, M, R, c.K)
+                rws = F.new_workspace(need, x.device) if need else None
+                us = _graph_us(lambda i: F.nvfp4_quantize_act_rotated(x, R, ws=rws, out=aq, stream=stream),
+                               args.reps, stream, replays=7)
+                row[f"quant_rot{R}_us"] = round(us, 3)
+            row["rot16_over_quant"] = round(row["quant_rot16_us"] / row["quant_us"], 3)
+            rows.append(row)
+            log(args, f"[q+r] {c.name:18s} M={M:<3d} Q {row['quant_us']:.2f} us, Q+R(16) {row['quant_rot16_us']:.2f} us, "
+                      f"Q+R(128) {row['quant_rot128_us']:.2f} us")
     return rows
 
 

@@ -10,6 +10,8 @@ Functions keep the C names:
 
 * ``nvfp4_pack_weights(w)`` -> ``(codes, scales, gscale)``
 * ``nvfp4_quantize_act(x_bf16, gscale=None)`` -> ``(codes, scales, gscale)``
+* ``nvfp4_quantize_act_rotated(x_bf16, rot=16, gscale=None)`` -> the same,
+  after a block Walsh-Hadamard rotation of each row ("Q+R")
 * ``nvfp4_gemv_smallm(a, w, ...)`` -> ``y`` (optionally with the LM-head
   epilogue)
 * ``nvfp4_sample_top_p(logits, temperature, top_p, uniforms)`` ->
@@ -47,6 +49,7 @@ NVFP4_OP_QUANT = 1
 NVFP4_OP_GEMV = 2
 NVFP4_OP_GEMV_LMHEAD = 3
 NVFP4_OP_SAMPLE = 4
+NVFP4_OP_QUANT_ROTATED = 5
 
 EXPORTED = (
     "nvfp4_status_str",
@@ -54,6 +57,7 @@ EXPORTED = (
     "nvfp4_workspace_init",
     "nvfp4_pack_weights",
     "nvfp4_quantize_act",
+    "nvfp4_quantize_act_rotated",
     "nvfp4_reset_state_size",
     "nvfp4_reset_state_init",
     "nvfp4_gemv_smallm",
@@ -115,6 +119,8 @@ def lib() -> ctypes.CDLL:
     L.nvfp4_pack_weights.argtypes = [vp, i64, i64, vp, vp, vp, vp, sz, vp]
     L.nvfp4_quantize_act.restype = c_int
     L.nvfp4_quantize_act.argtypes = [vp, c_int, i64, vp, vp, vp, c_int, vp, sz, vp]
+    L.nvfp4_quantize_act_rotated.restype = c_int
+    L.nvfp4_quantize_act_rotated.argtypes = [vp, c_int, i64, c_int, vp, vp, vp, c_int, vp, sz, vp]
     L.nvfp4_reset_state_size.restype = sz
     L.nvfp4_reset_state_size.argtypes = [c_int]
     L.nvfp4_reset_state_init.restype = c_int
@@ -325,6 +331,41 @@ def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, 
     _check(lib().nvfp4_quantize_act(_ptr(x), M, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
                                     flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
            "nvfp4_quantize_act")
+    return out
+
+
+def nvfp4_quantize_act_rotated(x, rot: int = 16, gscale=None, ws=None, out: NvFp4Tensor | None = None,
+                               stream=None) -> NvFp4Tensor:
+    """Q+R: rotate each run of ``rot`` elements of every row of x bf16 [M][K]
+    by the normalized Walsh-Hadamard matrix, then quantize (dynamic global
+    scale, or the static device fp32 ``gscale``, which is then out.gscale)."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError("x must be [M][K]")
+    M, K = int(x.shape[0]), int(x.shape[1])
+    dev = x.device
+    _require(x, "x", torch.bfloat16, dev)
+    if gscale is not None:
+        _require(gscale, "gscale", torch.float32, dev, min_numel=1)
+    flags = NVFP4_GS_DYNAMIC if gscale is None else NVFP4_GS_STATIC
+    if out is None:
+        out = NvFp4Tensor(torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+                          gscale if gscale is not None else torch.empty(1, dtype=torch.float32, device=dev))
+    _require(out.codes, "out.codes", torch.uint8, dev, (M, K // 2))
+    _require(out.scales, "out.scales", torch.uint8, dev, (M, K // 16))
+    _require(out.gscale, "out.gscale", torch.float32, dev, min_numel=1)
+    if gscale is not None and out.gscale.data_ptr() != gscale.data_ptr():
+        raise ValueError("a static gscale must be out.gscale")
+    need = nvfp4_workspace_size(NVFP4_OP_QUANT_ROTATED, M, rot, K) if gscale is None else 0
+    if need and ws is None:
+        ws = new_workspace(need, dev, stream)
+    _require_ws(ws, need, dev)
+    _check(lib().nvfp4_quantize_act_rotated(_ptr(x), M, K, int(rot), _ptr(out.codes), _ptr(out.scales),
+                                            _ptr(out.gscale), flags, _ptr(ws), 0 if ws is None else ws.numel(),
+                                            _stream(stream)),
+           "nvfp4_quantize_act_rotated")
     return out
 
 

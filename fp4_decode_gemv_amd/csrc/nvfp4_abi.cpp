@@ -70,6 +70,12 @@ int check_device() {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
+// Largest tensor the rotation-fused quantization reduces in one launch
+// (every workgroup rotating the whole tensor for the amax): 32768 elements
+// at rot = 16, halved for each doubling of the rotation (graph-replayed
+// timings of the decode shapes; above it the amax partials pass is faster).
+int64_t rot_self_max_elems(int rot) { return (int64_t)32768 * 16 / rot; }
+
 size_t quant_ws_bytes(int64_t elems, bool two_launch) {
   if (!two_launch) return 0;
   return ((size_t)amax_partial_count(elems) * sizeof(float) + 15) & ~(size_t)15;
@@ -96,6 +102,35 @@ const char* nvfp4_status_str(int status) {
   return "NVFP4: unknown status";
 }
 
+int nvfp4_quantize_act_rotated(const uint16_t* x_bf16, int M, int64_t K, int rot, uint8_t* codes, uint8_t* scales,
+                               float* gscale, int flags, void* ws, size_t ws_bytes, void* stream) {
+  if (rot != 16 && rot != 32 && rot != 64 && rot != 128) return NVFP4_ERR_ARG;
+  if (flags != NVFP4_GS_DYNAMIC && flags != NVFP4_GS_STATIC) return NVFP4_ERR_ARG;
+  if (M < 1 || M > kMaxTokens || !shape_ok_k(K) || K % rot != 0) return NVFP4_ERR_SHAPE;
+  if (!x_bf16 || !codes || !scales || !gscale) return NVFP4_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return NVFP4_ERR_ALIGN;
+  const int64_t elems = (int64_t)M * K;
+  // the quantizer addresses the tensor through a buffer of 2-byte elements
+  // with 32-bit byte offsets
+  if (elems >= ((int64_t)1 << 30)) return NVFP4_ERR_SHAPE;
+  const bool two = flags == NVFP4_GS_DYNAMIC && elems > rot_self_max_elems(rot);
+  const size_t need = flags == NVFP4_GS_DYNAMIC ? quant_ws_bytes(elems, two) : 0;
+  if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return NVFP4_ERR_ALIGN;
+  const size_t xb = (size_t)elems * 2, cb = (size_t)elems / 2, sb = (size_t)elems / 16;
+  if (overlaps(x_bf16, xb, codes, cb) || overlaps(x_bf16, xb, scales, sb) || overlaps(x_bf16, xb, gscale, 4) ||
+      overlaps(codes, cb, scales, sb) || overlaps(codes, cb, gscale, 4) || overlaps(scales, sb, gscale, 4) ||
+      (need > 0 && (overlaps(ws, need, x_bf16, xb) || overlaps(ws, need, codes, cb) ||
+                    overlaps(ws, need, scales, sb) || overlaps(ws, need, gscale, 4))))
+    return NVFP4_ERR_ARG;
+  const int d = check_device();
+  if (d != NVFP4_OK) return d;
+  const GsMode mode = flags == NVFP4_GS_STATIC ? GS_STATIC : two ? GS_FROM_PARTIALS : GS_SELF;
+  return hip_status(launch_quantize_rotated(x_bf16, elems, rot, codes, scales, gscale, mode,
+                                            two ? static_cast<float*>(ws) : nullptr,
+                                            two ? amax_partial_count(elems) : 0, static_cast<hipStream_t>(stream)));
+}
+
 size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K) {
   switch (op) {
     case NVFP4_OP_PACK:
@@ -110,6 +145,9 @@ size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K) {
     case NVFP4_OP_GEMV_LMHEAD:
       if (!shape_ok(M, N, K)) return 0;
       return gemv_workspace_bytes(M, N, K, true);
+    case NVFP4_OP_QUANT_ROTATED:  // N = the rotation size
+      if (M < 1 || M > kMaxTokens || !shape_ok_k(K) || (N != 16 && N != 32 && N != 64 && N != 128)) return 0;
+      return quant_ws_bytes((int64_t)M * K, (int64_t)M * K > rot_self_max_elems((int)N));
     case NVFP4_OP_SAMPLE:
       if (M < 1 || M > kSampleMaxM || N < 1 || N > kSampleMaxN) return 0;
       return sample_workspace_bytes(M, N);

@@ -32,6 +32,11 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint
 // largest K of a per-token dynamic quantization (one launch, every
 // workgroup of a row reads the whole row for its amax)
 constexpr int64_t kTokenScaleMaxK = 131072;
+// Rotation-fused quantization (one tensor of `elems` elements, rot = 16, 32,
+// 64 or 128; modes GS_SELF up to kActSelfAmaxMaxElems, GS_STATIC,
+// GS_FROM_PARTIALS with amax_partial_count(elems) partials)
+hipError_t launch_quantize_rotated(const uint16_t* x, int64_t elems, int rot, uint8_t* codes, uint8_t* scales,
+                                   float* gscale, GsMode mode, float* partials, int n_parts, hipStream_t stream);
 hipError_t launch_quantize_f32(const float* x, int64_t rows, int64_t K, uint8_t* codes,
                                uint8_t* scales, float* gscale, float* partials, int n_parts,
                                hipStream_t stream);

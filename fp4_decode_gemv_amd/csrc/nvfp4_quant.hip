@@ -348,6 +348,173 @@ __global__ void fill_zero_kernel(uint4* p, int64_t n16) {
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Rotation-fused activation quantization ("Q+R"): the comparison point of the
+// reading notes, section 5.3 and Table 3, where rotation-based NVFP4
+// pipelines rotate the activation before quantizing it.  Here the rotation
+// is the normalized Walsh-Hadamard transform H_R / sqrt(R) of every run of R
+// consecutive elements of a row (R = 16, 32, 64 or 128), then the unchanged
+// quantization.  A lane holds 8 consecutive elements, so an R-element block
+// spans R / 8 consecutive lanes of a wave.  The butterfly runs stages
+// h = 1, 2, 4 inside the lane, then h = 8, 16, 32, 64 across lanes (partner
+// lane = lane ^ (h / 8)); each pair (i, i + h) becomes (a + b, a - b) in
+// float32, then every element is multiplied by the float32 nearest to
+// 1 / sqrt(R).  The global amax is that of the rotated tensor.
+// ---------------------------------------------------------------------------
+
+// x of lane (lane ^ d), d = 1, 2, 4 or 8, by DPP moves inside a 16-lane row
+// (quad permutations for 1 and 2; row rotations, where lane i reads lane
+// (i - n) mod 16 of its row, for 4 and 8)
+__device__ __forceinline__ float lane_xor(float x, int d, int lane) {
+  const uint32_t u = __float_as_uint(x);
+  if (d == 1) return __uint_as_float(dpp_u32<0xB1>(u));  // quad_perm [1,0,3,2]
+  if (d == 2) return __uint_as_float(dpp_u32<0x4E>(u));  // quad_perm [2,3,0,1]
+  if (d == 8) return __uint_as_float(dpp_u32<0x128>(u));  // row_ror:8
+  // d == 4: lanes with bit 2 set read lane - 4 (row_ror:4), the others lane + 4 (row_ror:12)
+  const uint32_t down = dpp_u32<0x124>(u), up = dpp_u32<0x12C>(u);
+  return __uint_as_float((lane & 4) ? down : up);
+}
+
+template <int R>
+__device__ __forceinline__ float rotation_scale() {
+  static_assert(R == 16 || R == 32 || R == 64 || R == 128, "rotation sizes");
+  // 1 / sqrt(R): 1/4, 1/(4 sqrt 2), 1/8, 1/(8 sqrt 2)
+  return R == 16 ? 0.25f : R == 32 ? 0.17677669529663688f : R == 64 ? 0.125f : 0.088388347648318440f;
+}
+
+// bf16 bits of 8 consecutive elements -> their rotated float32 values
+// (every lane of the wave must call this together: the cross-lane stages
+// exchange values with __shfl_xor)
+template <int R>
+__device__ __forceinline__ void rotate8(const u32x4_t raw, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(raw[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(raw[i] >> 16);
+  }
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  const int lane = (int)threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < R / 8; d <<= 1) {
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = lane_xor(v[i], d, lane);
+      v[i] = upper ? q - v[i] : v[i] + q;
+    }
+  }
+  const float c = rotation_scale<R>();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = v[i] * c;
+}
+
+__device__ __forceinline__ uint32_t amax8_bits(const float (&v)[8]) {
+  uint32_t m = 0;  // |x| of non-negative floats orders like their bits
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  return m;
+}
+
+// Pass 1 of the two-launch Q+R path: partials[b] = max |rotated x| over
+// chunk b (chunks are whole multiples of 128 elements, so no rotation block
+// straddles two workgroups).
+template <int R>
+__global__ __launch_bounds__(kThreads) void amax_rot_partials_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                     float* __restrict__ partials) {
+  __shared__ __align__(16) uint32_t red[kThreads / 64];
+  const int64_t per = ((n / 128 + gridDim.x - 1) / gridDim.x) * 128;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, (int)(n * 2), kBufferWord3);
+  uint32_t m = 0;
+  for (int64_t i = lo; i < lo + per; i += (int64_t)kThreads * 8) {  // uniform trip count
+    const int64_t e = i + (int64_t)threadIdx.x * 8;
+    const int off = e < hi ? (int)(e * 2) : (int)0x7FFFFFF0;  // past the range: zeros
+    float v[8];
+    rotate8<R>(__builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0), v);
+    m = max(m, amax8_bits(v));
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t = max(t, red[w]);
+    partials[blockIdx.x] = __uint_as_float(t);
+  }
+}
+
+// Q+R, one launch per tensor (GS_SELF: every workgroup rotates the whole
+// tensor for the amax; GS_STATIC; GS_FROM_PARTIALS after the pass above).
+template <int T, int R>
+__global__ __launch_bounds__(T) void quantize_act_rot_kernel(
+    const uint16_t* __restrict__ x, int64_t nelem, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gscale, int mode,
+    const float* __restrict__ partials, int n_parts) {
+  __shared__ __align__(16) uint32_t red[T / 64];
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, (int)(nelem * 2), kBufferWord3);
+  const int mine = ((int)blockIdx.x * T + (int)threadIdx.x) * 8;  // first element of this thread
+  const u32x4_t raw = __builtin_amdgcn_raw_buffer_load_b128(xr, mine * 2, 0, 0);
+  float s_g;
+  if (mode == GS_SELF) {
+    uint32_t m = 0;
+    for (int base = 0; base < (int)nelem; base += T * 8 * kActBatch) {  // uniform trip count
+      u32x4_t v[kActBatch];
+#pragma unroll
+      for (int j = 0; j < kActBatch; ++j)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, (base + (j * T + (int)threadIdx.x) * 8) * 2, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kActBatch; ++j) {
+        float f[8];
+        rotate8<R>(v[j], f);
+        m = max(m, amax8_bits(f));
+      }
+    }
+    s_g = __uint_as_float(wg_max_u32<T>(m, red)) / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
+  } else if (mode == GS_STATIC) {
+    s_g = *gscale;
+  } else {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < n_parts; i += T) m = max(m, __float_as_uint(partials[i]));
+    s_g = __uint_as_float(wg_max_u32<T>(m, red)) / 2688.0f;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gscale = s_g;
+  }
+  float v[8];
+  rotate8<R>(raw, v);
+  // block amax over the two halves (neighbouring lanes 2k, 2k+1)
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(amax))));
+  if (mine < nelem) {
+    float tb = 0.0f;
+    if (s_g != 0.0f) {
+      const float denom = 6.0f * s_g;
+      tb = amax / denom;
+    }
+    const uint32_t sb = e4m3_code(tb);
+    const float e = e4m3_value(sb) * s_g;
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = e != 0.0f ? v[i] / e : copysignf(0.0f, v[i]);
+    const uint32_t c = e2m1_pair(r[0], r[1]) | (e2m1_pair(r[2], r[3]) << 8) | (e2m1_pair(r[4], r[5]) << 16) |
+                       (e2m1_pair(r[6], r[7]) << 24);
+    *reinterpret_cast<uint32_t*>(codes + mine / 2) = c;
+    if ((threadIdx.x & 1) == 0) scales[mine / 16] = (uint8_t)sb;
+  }
+}
+
 int64_t quant_grid(int64_t nblocks) {
   int64_t g = (nblocks + kThreads - 1) / kThreads;
   if (g > 4096) g = 4096;
@@ -391,6 +558,44 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t K, uint
   hipLaunchKernelGGL(fn, dim3((unsigned)grid, segs), dim3(threads), 0, stream, x, nelem, codes, scales, gscale,
                      (int)mode, partials, n_parts);
   return hipGetLastError();
+}
+
+namespace {
+
+template <int R>
+hipError_t launch_quantize_rot(const uint16_t* x, int64_t nelem, uint8_t* codes, uint8_t* scales, float* gscale,
+                               GsMode mode, float* partials, int n_parts, hipStream_t stream) {
+  if (mode == GS_FROM_PARTIALS)
+    hipLaunchKernelGGL(amax_rot_partials_kernel<R>, dim3(n_parts), dim3(kThreads), 0, stream, x, nelem, partials);
+  // the workgroup sizes of the plain quantization (the rotation adds a few
+  // VALU operations per element and does not change the balance)
+  const int threads = mode != GS_SELF  ? 64
+                      : nelem <= 8192  ? 64
+                      : nelem <= 16384 ? 128
+                      : nelem <= 32768 ? 256
+                                       : 512;
+  const int64_t grid = (nelem + (int64_t)threads * 8 - 1) / ((int64_t)threads * 8);
+  auto fn = threads == 64    ? quantize_act_rot_kernel<64, R>
+            : threads == 128 ? quantize_act_rot_kernel<128, R>
+            : threads == 256 ? quantize_act_rot_kernel<256, R>
+                             : quantize_act_rot_kernel<512, R>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(threads), 0, stream, x, nelem, codes, scales, gscale, (int)mode,
+                     partials, n_parts);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rotated(const uint16_t* x, int64_t elems, int rot, uint8_t* codes, uint8_t* scales,
+                                   float* gscale, GsMode mode, float* partials, int n_parts, hipStream_t stream) {
+  if (mode == GS_SELF && elems > kActSelfElems) return hipErrorInvalidValue;
+  switch (rot) {
+    case 16: return launch_quantize_rot<16>(x, elems, codes, scales, gscale, mode, partials, n_parts, stream);
+    case 32: return launch_quantize_rot<32>(x, elems, codes, scales, gscale, mode, partials, n_parts, stream);
+    case 64: return launch_quantize_rot<64>(x, elems, codes, scales, gscale, mode, partials, n_parts, stream);
+    case 128: return launch_quantize_rot<128>(x, elems, codes, scales, gscale, mode, partials, n_parts, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_quantize_f32(const float* x, int64_t rows, int64_t K, uint8_t* codes,

@@ -79,14 +79,18 @@ typedef enum {
 enum { NVFP4_GS_DYNAMIC = 0, NVFP4_GS_STATIC = 1, NVFP4_GS_TOKEN_DYNAMIC = 2, NVFP4_GS_TOKEN_STATIC = 3 };
 
 /* ops for nvfp4_workspace_size */
-enum { NVFP4_OP_PACK = 0, NVFP4_OP_QUANT = 1, NVFP4_OP_GEMV = 2, NVFP4_OP_GEMV_LMHEAD = 3, NVFP4_OP_SAMPLE = 4 };
+enum {
+  NVFP4_OP_PACK = 0, NVFP4_OP_QUANT = 1, NVFP4_OP_GEMV = 2, NVFP4_OP_GEMV_LMHEAD = 3, NVFP4_OP_SAMPLE = 4,
+  NVFP4_OP_QUANT_ROTATED = 5
+};
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* nvfp4_status_str(int status);
 
 /* Bytes of workspace the op needs for this shape (0 = none; M is ignored
  * for NVFP4_OP_PACK, where N x K is the weight; K is ignored for
- * NVFP4_OP_SAMPLE, where N is the vocabulary).  Pure host function. */
+ * NVFP4_OP_SAMPLE, where N is the vocabulary; for NVFP4_OP_QUANT_ROTATED, N
+ * is the rotation size).  Pure host function. */
 size_t nvfp4_workspace_size(int op, int M, int64_t N, int64_t K);
 
 /* Zero-fill a workspace with a kernel on `stream` (graph-capturable; no
@@ -126,6 +130,30 @@ int nvfp4_pack_weights(const float* w, int64_t N, int64_t K,
 int nvfp4_quantize_act(const uint16_t* x_bf16, int M, int64_t K,
                        uint8_t* codes, uint8_t* scales, float* gscale,
                        int flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Rotation-fused activation quantization "Q+R", a comparison point (reading
+ * notes, section 5.3 and Table 3: rotation-based NVFP4 pipelines rotate
+ * each layer's activation before quantizing it, at about 2.3x the cost of
+ * the plain Q step on the pages' GPU).  Each run of `rot` consecutive
+ * elements of a row (rot = 16, 32, 64 or 128; K % rot == 0) is multiplied
+ * by the normalized Walsh-Hadamard matrix H_rot / sqrt(rot) (Sylvester
+ * order), computed in float32 by butterfly stages h = 1, 2, ..., rot/2, each
+ * pair (i, i + h) becoming (a + b, a - b), then one multiply by the float32
+ * nearest to 1/sqrt(rot); the rotated tensor is then quantized exactly as
+ * nvfp4_quantize_act does (its amax sets the dynamic global scale).
+ * flags: NVFP4_GS_DYNAMIC or NVFP4_GS_STATIC (per-token flags:
+ * NVFP4_ERR_ARG).  A projection on such an activation needs weights rotated
+ * the same way before packing: (A Q)(W Q)^T = A W^T for the orthogonal Q.
+ * Same shapes (M x K < 2^30), outputs and errors as nvfp4_quantize_act;
+ * workspace: nvfp4_workspace_size(NVFP4_OP_QUANT_ROTATED, M, rot, K) bytes
+ * (may be 0; ws may then be NULL); rot not in {16, 32, 64, 128}: NVFP4_ERR_ARG;
+ * K % rot != 0: NVFP4_ERR_SHAPE.  Codes, scales and gscale are
+ * bit-identical to the oracle's rotation followed by the recipe.
+ */
+int nvfp4_quantize_act_rotated(const uint16_t* x_bf16, int M, int64_t K, int rot,
+                               uint8_t* codes, uint8_t* scales, float* gscale,
+                               int flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ReSET per-sequence state, device resident (ReSET reading notes, sections

@@ -285,3 +285,38 @@ def test_sample_top_p_errors(L):
     assert call(tok=T) == F.NVFP4_ERR_ARG             # output over an input
     assert call(ws=z + 256) == F.NVFP4_ERR_ARG        # workspace over the logits
     assert call(ws=tok - 256) == F.NVFP4_ERR_ARG      # workspace over an output
+
+
+def test_quantize_rotated_rejects_bad_arguments(L):
+    """Q+R: rotation sizes other than 16/32/64/128 and per-token flags are
+    argument errors, K not a multiple of the rotation a shape error, all
+    before any HIP call."""
+    far = 1 << 44
+    x, c, sc, g, ws = A, A + far, A + 2 * far, A + 3 * far, A + 4 * far
+    q = L.nvfp4_quantize_act_rotated
+    for rot in (0, 8, 48, 256):
+        assert q(x, 1, 512, rot, c, sc, g, F.NVFP4_GS_DYNAMIC, ws, 1 << 40, None) == F.NVFP4_ERR_ARG
+    for flags in (F.NVFP4_GS_TOKEN_DYNAMIC, F.NVFP4_GS_TOKEN_STATIC, 7):
+        assert q(x, 1, 512, 16, c, sc, g, flags, ws, 1 << 40, None) == F.NVFP4_ERR_ARG
+    assert q(x, 1, 96, 64, c, sc, g, F.NVFP4_GS_DYNAMIC, ws, 1 << 40, None) == F.NVFP4_ERR_SHAPE
+    assert q(x, 1, 160, 128, c, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_SHAPE
+    assert q(x, 0, 512, 16, c, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_SHAPE
+    assert q(x, 128, 1 << 23, 16, c, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_SHAPE
+    assert q(None, 1, 512, 16, c, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_NULL
+    assert q(x + 8, 1, 512, 16, c, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_ALIGN
+    # the two-launch dynamic path needs its partials workspace
+    assert q(x, 8, 25600, 16, c, sc, g, F.NVFP4_GS_DYNAMIC, None, 0, None) == F.NVFP4_ERR_WORKSPACE
+    # overlapping output and input
+    assert q(x, 1, 512, 16, x, sc, g, F.NVFP4_GS_STATIC, ws, 1 << 40, None) == F.NVFP4_ERR_ARG
+
+
+def test_rotated_quantization_workspace_sizes(L):
+    """Q+R keeps one launch up to 32768 elements at rot = 16 (halved per
+    doubling of rot) and needs amax partials above; unknown rotations ask
+    for nothing (the call itself rejects them)."""
+    ws = lambda M, rot, K: L.nvfp4_workspace_size(F.NVFP4_OP_QUANT_ROTATED, M, rot, K)
+    assert ws(1, 16, 32768) == 0 and ws(2, 16, 32768) > 0
+    assert ws(1, 32, 16384) == 0 and ws(1, 32, 16896) > 0
+    assert ws(1, 128, 4096) == 0 and ws(1, 128, 5120) > 0
+    assert ws(8, 16, 25600) == L.nvfp4_workspace_size(F.NVFP4_OP_QUANT, 8, 0, 25600)
+    assert ws(1, 48, 4096) == 0 and ws(0, 16, 4096) == 0
