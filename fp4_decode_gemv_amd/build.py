@@ -97,5 +97,51 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side checks: the library with its host code (the C ABI layer and the
+# launchers) built with AddressSanitizer and UndefinedBehaviorSanitizer; the
+# device code is the normal build.  Tests load it with the ASan runtime
+# preloaded and drive the argument validation on the CPU.
+SANITIZE_FLAGS = COMMON_FLAGS + [
+    "-g", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that matches hipcc."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no clang AddressSanitizer runtime under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Compile the host side of every source with ASan + UBSan and link
+    ``out_dir/libnvfp4_hostsan.so``; returns its path."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, src.replace("/", "_") + ".o")
+        cmd = [hipcc(), *SANITIZE_FLAGS, "-I", INCLUDE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized host build failed on {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "libnvfp4_hostsan.so")
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", *objs, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized host link failed:\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
