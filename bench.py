@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "e9606b85c1c17c2c595f4480c7dde37385b6fab27d9139c83402d4d0b02e12b1",
-    "bytes_per_step": 1115671461,
+    "sha256": "31c81731c74038de17b1a237560e118a8c4d9648b3ab6eb53563b25e4bf8955e",
+    "bytes_per_step": 1115895930,
 }
 
 
@@ -86,6 +86,9 @@ def n_copies(args, c) -> int:
     of distinct weights, and at least 2."""
     return max(2, math.ceil(args.rotate_mb * 1e6 / weight_bytes(c.N, c.K)))
 
+
+# dense f16 MFMA peak of MI355X (2.5 PFLOP/s, no sparsity)
+MFMA_F16_PEAK_FLOPS = 2.5e15
 
 # VALU issue peak of the chip: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 VALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
@@ -469,7 +472,10 @@ def time_cases(args, stream, cases, wq, acts, Ms, with_valu=False):
             v = F.nvfp4_gemv_variant(M, c.N, c.K)
             d = {"proj": c.name, "M": M, "N": c.N, "K": c.K, "weight_bytes": wb, "variant": v,
                  "gemv_us": round(gus, 3), "gemv_gbs": round(wb / (gus * 1e-6) / 1e9, 1),
-                 "gemv_hbm_frac": round(wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "quant_us": round(qus, 3)}
+                 "gemv_hbm_frac": round(wb / (gus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "quant_us": round(qus, 3),
+                 # the useful multiply-adds (M tokens, not the padded tiles) against the dense f16 MFMA peak
+                 "tflops": round(2.0 * M * c.N * c.K / (gus * 1e-6) / 1e12, 2),
+                 "mfma_f16_frac": round(2.0 * M * c.N * c.K / (gus * 1e-6) / MFMA_F16_PEAK_FLOPS, 4)}
             if with_valu:
                 # estimated VALU issue utilisation (the secondary ceiling at larger M)
                 d["valu_util_est"] = round(valu_ops_per_element(v, M) * c.N * c.K / (gus * 1e-6) / VALU_LANE_OPS_PER_S, 3)
