@@ -395,7 +395,7 @@ def variant_k_multiple(name: str) -> int:
     ``fstream_*``) stream whole 512-element chunks, the direct-to-LDS kernels
     (``dma_*``, ``staged_*``, ``fmma_*``) and the tiled GEMM (``gemm_*``)
     copy whole 256-element steps, every other kernel 32-element chunks."""
-    if name.startswith(("stream_", "fstream_")):
+    if name.startswith(("stream_", "fstream_", "wstream_")):
         return 512
     return 256 if name.startswith(("dma_", "staged_", "fmma_", "gemm_")) else 32
 

@@ -2037,6 +2037,125 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
   if constexpr (EPI) lmhead_partials<MT, 4 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
 }
 
+// (c) Wave-owned rows, for many-row projections at M = 2..8 (K % 512 == 0):
+// the operand layout and ring of form (a), but each wave owns 4 R rows of
+// the workgroup's NW x 4 R and streams every chunk of K for them, so a
+// workgroup stages the activation (and its rows' block scales) once for
+// NW x 4 R rows, and no partial sums cross waves: a row's four windows are
+// added inside the lane quad that holds them (DPP), then stored.
+template <int MT, int R, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
+  static_assert(MT == 4 || MT == 8, "token sets of 4");
+  constexpr int S = MT / 4;  // token sets
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, kg = lane >> 4;
+  const int jr = j >> 2, jw = j & 3;  // row (weight side) / token (token side), window
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
+  const int n = (int)(K / kStreamChunk);
+  const int wrow0 = wave * 4 * R;  // first row of this wave within the tile
+
+  int64_t acb, asb;
+  stream_stage<NW>(p, MT, rows, tile0, wave, lane, acb, asb);
+  const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const int b0 = 64 * kg + 16 * jw;  // byte of this lane within a row's chunk
+  uint32_t vw[R];
+  const char* lds = reinterpret_cast<const char*>(lds4);
+  const char* lsw[R];  // block scales of each row group's row (+ 32 c); rows past the tile read the last row's
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = wrow0 + 4 * r + jr;
+    vw[r] = row < rows ? (uint32_t)(row * (int)(K / 2) + b0) : kOffOut;
+    lsw[r] = lds + acb + asb + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;
+  }
+  bool tin[S];
+  const char* la[S];
+  const char* lsa[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int t = 4 * s + jr;
+    tin[s] = t < M;
+    la[s] = lds + (t < M ? t : 0) * (K / 2) + b0;               // + 256 c
+    lsa[s] = lds + acb + (t < M ? t : 0) * (K / 16) + b0 / 8;   // + 32 c
+  }
+
+  float4_t acc[R][S];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc[r][s] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4_t ring[U][R];
+  auto load = [&](int u, int i) {  // chunk i into slot u; past the last, the last again (never used)
+    const int c = i < n ? i : n - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    load(u, u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vmcnt<(U * R < 63 ? U * R : 63)>();  // this wave's staging copies (issued first) have landed ...
+  asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
+  for (int i0 = 0; i0 < n; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      const int c = i < n ? i : n - 1;
+      u32x4_t w[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[r] = ring[u][r];
+      load(u, i + U);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < n) {
+        half8_t b[S][4];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const uint4 a4 = *reinterpret_cast<const uint4*>(la[s] + 256 * c);
+          const u32x4_t av = tin[s] ? u32x4_t{a4.x, a4.y, a4.z, a4.w} : u32x4_t{0u, 0u, 0u, 0u};
+          const uint32_t as = tin[s] ? *reinterpret_cast<const uint16_t*>(lsa[s] + 32 * c) : 0u;
+          decode32_scaled(av, as, b[s]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          half8_t a[4];
+          decode32_scaled(w[r], *reinterpret_cast<const uint16_t*>(lsw[r] + 32 * c), a);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+              acc[r][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[s][q], acc[r][s], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // finish: lane l's entry l % 4 holds row 4 r + l / 16 with token (l % 16) / 4
+  // of set s over window l % 4; a quad of lanes holds the four windows of one
+  // (row, token): add them inside the quad, then its first lane stores
+  const int qrow = lane >> 4, qtok = (lane >> 2) & 3;
+  float tsc[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) tsc[s] = token_scale(p, 4 * s + qtok < M ? 4 * s + qtok : 0);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      float v = acc[r][s][lane & 3];
+      v += __uint_as_float(__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0xB1, 0xF, 0xF, false));
+      v += __uint_as_float(__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x4E, 0xF, 0xF, false));
+      const int t = 4 * s + qtok, row = wrow0 + 4 * r + qrow;
+      if ((lane & 3) == 0 && t < M && row < rows) p.y[(int64_t)t * N + tile0 + row] = v * tsc[s];
+    }
+}
+
 // (b) FP4 form, M = 1, K % 512 == 0.  The weight codes go into
 // v_mfma_scale_f32_16x16x128_f8f6f4 as they are (E2M1 x E2M1 products are
 // exact, its E8M0 scales stay 1), so no weight element is decoded.  NVFP4's
@@ -2413,7 +2532,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
 
 enum Kind {
   VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8, STREAM = 9,
-  FSTREAM = 10, GEMM = 11
+  FSTREAM = 10, GEMM = 11, WSTREAM = 12
 };
 
 struct Variant {
@@ -2490,6 +2609,14 @@ struct Variant {
         gemv_fstream_kernel<R, NW, U, false>, gemv_fstream_kernel<R, NW, U, true>           \
   }
 
+// the wave-owned streaming kernel has no LM-head form either (its epilogue
+// slot repeats the plain kernel and is never chosen)
+#define WSTREAM_V(MT, R, NW, U)                                                                      \
+  Variant {                                                                                        \
+    "wstream_m" #MT "_r" #R "_w" #NW "_u" #U, WSTREAM, MT, 16, R, NW, U,                               \
+        gemv_wstream_kernel<MT, R, NW, U>, gemv_wstream_kernel<MT, R, NW, U>                        \
+  }
+
 // the tiled GEMM has no LM-head form: its epilogue slot repeats the plain
 // kernel and is never chosen (fits() refuses GEMM with the epilogue)
 #define GEMM_V(MT)                                                                    \
@@ -2511,7 +2638,7 @@ const Variant kVariants[] = {
     FMMA_V(4, 2, 4, 3), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 1),
     // 9..128 tokens
     LMFMA_V(16, 2, 8, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(32, 2, 8, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(64, 2, 8, 1),
-    LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1), GEMM_V(32), GEMM_V(64), GEMM_V(128),
+    LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1), GEMM_V(32), GEMM_V(64), GEMM_V(128), WSTREAM_V(4, 3, 4, 2),
     // fallbacks
     DIRECT_V(2, 64, 1, 4, 1), MFMA_V(4, 2, 8, 1), MFMA_V(8, 2, 8, 1), LMFMA_V(16, 1, 4, 1), LMFMA_V(32, 1, 4, 1),
     LMFMA_V(64, 1, 4, 1), LMFMA_V(128, 1, 4, 1),
@@ -2563,6 +2690,7 @@ int64_t epi_tile_rows(const Variant& v) {
   switch (v.kind) {
     case STREAM:
     case FSTREAM: return 4 * v.r;
+    case WSTREAM: return 4 * v.r * v.nw;
     case VALU:
     case DIRECT:
     case STAGED: return (int64_t)v.r * v.nw * (64 / v.g);
@@ -2625,11 +2753,21 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
     if (stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
       return i;
   }
+  // 2..4 tokens on qkv-like shapes (8192 <= N < 16384, K < 8192) and 3..4
+  // tokens on many-row shapes (N >= 16384): the wave-owned streaming kernel
+  if (!epi && K % kStreamChunk == 0 && M <= 4 && N >= 8192 &&
+      ((N < 16384 && K < 8192 && M >= 2) || (N >= 16384 && M >= 3))) {
+    const int i = VARIANT("wstream_m4_r3_w4_u2");
+    if (stream_lds_bytes(4, K, 4 * kVariants[i].r * kVariants[i].nw) <= kLdsBytes) return i;
+  }
   if (M <= 1) {
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
     return VARIANT("direct_m1_g32_r1_w4_p1_nt");
   }
+  // 2 tokens on small shapes (N, K < 8192: the 4096 x 4096 and Qwen3-8B
+  // qkv / o): the register-staged MFMA kernel beats the staged VALU one
+  if (M == 2 && N < 8192 && K < 8192) return VARIANT("lmfma_m8_r1_w4_p1");
   if (M <= 2 && k256)
     return K >= 12288 ? fmma_sa(VARIANT("fmma_m2_r1_w4_d3_sa"), VARIANT("staged_m2_g64_r1_w4_p2"))
            : K >= 8192 && N < 16384 ? VARIANT("staged_m2_g64_r1_w4_p1")
@@ -2672,6 +2810,9 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     if ((kd == DMA || kd == DMASA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
     if ((kd == STREAM || kd == FSTREAM) && K % kStreamChunk != 0) return false;
     if (kd == GEMM && (K % kGemmStageK != 0 || epi)) return false;
+    if (kd == WSTREAM && (K % kStreamChunk != 0 || epi ||
+                          stream_lds_bytes(v.mt, K, 4 * v.r * v.nw) > kLdsBytes))
+      return false;
     // the LM-head instantiations also hold the static softmax slots
     // [MT][tile rows] of their partials
     const int64_t slot = epi ? (int64_t)4 * v.mt * epi_tile_rows(v) : 0;
@@ -2680,7 +2821,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
       return false;
     if (kd == STAGED && staged_lds_bytes(v, K) > 65536) return false;
     return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != FSTREAM &&
-            kd != GEMM) ||
+            kd != GEMM && kd != WSTREAM) ||
            (int64_t)16 * v.r * (K / 2) < (1ll << 31);
   };
   // tuning override, used when the forced variant's compiled token count
@@ -2711,6 +2852,11 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.rows_per_wg = kGemmRows;
     c.grid = (N + kGemmRows - 1) / kGemmRows;
     c.lds_bytes = 2 * (int64_t)gemm_stage_bytes(v.mt);
+  } else if (v.kind == WSTREAM) {
+    c.kp = (int)K;
+    c.rows_per_wg = 4 * v.r * v.nw;
+    c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
+    c.lds_bytes = stream_lds_bytes(v.mt, K, c.rows_per_wg);
   } else if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA ||
       v.kind == STREAM || v.kind == FSTREAM) {
     c.kp = (int)K;

@@ -61,6 +61,22 @@ def test_gemm_default_full_compare(M, N, K):
     assert_gemv_close(y, y_ref, ref_abs, what=f"gemm M={M} N={N} K={K}")
 
 
+# the wave-owned streaming kernel as the launch table picks it: 2..4 tokens on
+# qkv-like shapes and 3..4 tokens on many-row shapes, with a ragged last
+# 48-row workgroup and a ragged last 12-row wave block
+WSTREAM_DEFAULT = [(2, 8200, 5120), (4, 10241, 1024), (3, 16500, 4608), (4, 16389, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", WSTREAM_DEFAULT)
+def test_wstream_default_full_compare(M, N, K):
+    assert F.nvfp4_gemv_variant(M, N, K).startswith("wstream_m")
+    w = W.small_random_weights(N * 5 + K + M, N, K)
+    xb = W.small_random_bf16(M * 19 + K, M, K)
+    wq, aq, y = _run(M, N, K, w, xb, F.nvfp4_gemv_variant(M, N, K))
+    y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+    assert_gemv_close(y, y_ref, ref_abs, what=f"wstream M={M} N={N} K={K}")
+
+
 def _full_size(case, Ms):
     w = W.weights(case.w_seed, case.N, case.K, case.w_outlier_rows)
     wt = f32_dev(w)
