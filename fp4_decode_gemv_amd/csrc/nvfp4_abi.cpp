@@ -241,7 +241,7 @@ namespace {
 int gemv_entry(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_t* a_scales,
                const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales, const float* w_gscale,
                float* y, const nvfp4_lmhead_epilogue_t* epi, void* ws, size_t ws_bytes, void* stream,
-               bool per_token) {
+               bool per_token, int64_t ws_cap = kNoWsCap) {
   if (!shape_ok(M, N, K)) return NVFP4_ERR_SHAPE;
   if (!a_codes || !a_scales || !a_gscale || !w_codes || !w_scales || !w_gscale || !y) return NVFP4_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
@@ -254,7 +254,7 @@ int gemv_entry(int M, int64_t N, int64_t K, const uint8_t* a_codes, const uint8_
   if (overlaps(y, yb, a_codes, acb) || overlaps(y, yb, a_scales, asb) || overlaps(y, yb, a_gscale, agb) ||
       overlaps(y, yb, w_codes, wcb) || overlaps(y, yb, w_scales, wsb) || overlaps(y, yb, w_gscale, 4))
     return NVFP4_ERR_ARG;
-  const GemvConfig cfg = choose_gemv_config(M, N, K, epi != nullptr);
+  const GemvConfig cfg = choose_gemv_config(M, N, K, epi != nullptr, ws_cap);
   // the epilogue's merge addresses its partials (grid x mt x 16 bytes) with
   // 32-bit buffer offsets
   if (epi && cfg.ws_bytes > (int64_t)0x7FFFFF00) return NVFP4_ERR_SHAPE;
@@ -319,7 +319,8 @@ int nvfp4_gemv_smallm_noalloc(int M, int64_t N, int64_t K, const uint8_t* a_code
                               const float* w_gscale, float* y, const nvfp4_lmhead_epilogue_t* epi, void* stream) {
   // host checks first: shape, then the scratch this shape needs
   if (!shape_ok(M, N, K)) return NVFP4_ERR_SHAPE;
-  if (gemv_workspace_bytes(M, N, K, epi != nullptr) > kNoAllocScratchBytes) return NVFP4_ERR_WORKSPACE;
+  if (gemv_workspace_bytes(M, N, K, epi != nullptr, kNoAllocScratchBytes) > kNoAllocScratchBytes)
+    return NVFP4_ERR_WORKSPACE;
   const int d = check_device();
   if (d != NVFP4_OK) return d;
   int dev = -1;
@@ -327,7 +328,7 @@ int nvfp4_gemv_smallm_noalloc(int M, int64_t N, int64_t K, const uint8_t* a_code
   void* ws = scratch_for(dev);
   if (!ws) return NVFP4_ERR_HIP;
   return gemv_entry(M, N, K, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, y, epi, ws,
-                    kNoAllocScratchBytes, stream, false);
+                    kNoAllocScratchBytes, stream, false, kNoAllocScratchBytes);
 }
 
 size_t nvfp4_gemv_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }

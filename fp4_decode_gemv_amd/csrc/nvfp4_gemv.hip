@@ -101,6 +101,7 @@ struct GemvParams {
   EpilogueArgs epi;
   float* partials;         // epilogue: [row tiles][MT][4] = {max, S, T, -}
   uint32_t* tickets;       // epilogue: [kMaxTokens] per-token counters, zero at rest
+  int ksplit;              // tiled GEMM: K splits (1 = none); partials then hold [split][tile][M][128] sums
   size_t state_bytes;      // bytes per ReSET state
   // weight rows per workgroup of the MFMA kernels (<= 16 R): workgroup b
   // owns rows [b * tile_rows, (b + 1) * tile_rows); rows of its 16 R-row
@@ -2457,13 +2458,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
   const int wr = wave % WR, wc = wave / WR;
   const int64_t N = p.N, K = p.K;
   const int M = p.M;
-  const int64_t tile0 = (int64_t)blockIdx.x * kGemmRows;
+  // workgroup b: row tile b % ntiles, K split b / ntiles (stages st0 .. st1 - 1)
+  const int ntiles = (int)((N + kGemmRows - 1) / kGemmRows);
+  const int tile = (int)blockIdx.x % ntiles, ks = (int)blockIdx.x / ntiles;
+  const int64_t tile0 = (int64_t)tile * kGemmRows;
   const int rows = N - tile0 < kGemmRows ? (int)(N - tile0) : kGemmRows;
   const i32x4_t wcr = raw_rsrc(p.w_codes + tile0 * (K / 2), (int64_t)rows * (K / 2));
   const i32x4_t wsr = raw_rsrc(p.w_scales + tile0 * (K / 16), (int64_t)rows * (K / 16));
   const i32x4_t acr = raw_rsrc(p.a_codes, (int64_t)M * (K / 2));
   const i32x4_t asr = raw_rsrc(p.a_scales, (int64_t)M * (K / 16));
-  const int nst = (int)(K / kGemmStageK);
+  const int nst_all = (int)(K / kGemmStageK);
+  const int st0 = (int)((int64_t)nst_all * ks / p.ksplit), st1 = (int)((int64_t)nst_all * (ks + 1) / p.ksplit);
 
   float4_t acc[RT][CT];
 #pragma unroll
@@ -2472,11 +2477,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
     for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const GemmCopyPlan<MT> plan = gemm_copy_plan<MT>(K, rows, M, wave, lane);
-  gemm_stage_copy<MT>(plan, wcr, wsr, acr, asr, l0, 0, wave);
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+  if (st0 < st1) gemm_stage_copy<MT>(plan, wcr, wsr, acr, asr, l0, st0, wave);  // (splits never exceed the stages)
+  for (int st = st0; st < st1; ++st) {
+    const int buf = (st - st0) & 1;
     int ahead = 0;
-    if (st + 1 < nst) {
+    if (st + 1 < st1) {
       gemm_stage_copy<MT>(plan, wcr, wsr, acr, asr, l0 + (uint32_t)((buf ^ 1) * STAGE), st + 1, wave);
       ahead = plan.n;
     }
@@ -2506,6 +2511,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
   }
   // lane (j, g) holds D[4 g + i][j]: weight rows 4 g .. 4 g + 3 of the tile
   // for token j of the token tile
+  if (p.ksplit > 1) {  // unscaled partial sums; the reduction launch adds the splits in order
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int t = wc * (MT / WC) + 16 * ct + j;
+      if (t >= M) continue;
+      float* part = p.partials + ((int64_t)(ks * ntiles + tile) * M + t) * kGemmRows;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        *reinterpret_cast<float4_t*>(part + wr * (kGemmRows / WR) + 16 * rt + 4 * g) = acc[rt][ct];
+    }
+    return;
+  }
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int t = wc * (MT / WC) + 16 * ct + j;
@@ -2524,6 +2541,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
       }
     }
   }
+}
+
+// Second launch of a split-K GEMM: y[t][n] = (sum over the splits, in split
+// order, of the partial sums) * the global scales; one thread per output.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemvParams p) {
+  const int64_t N = p.N;
+  const int M = p.M;
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= (int64_t)M * N) return;
+  const int t = (int)(o / N);
+  const int64_t n = o - (int64_t)t * N;
+  const int ntiles = (int)((N + kGemmRows - 1) / kGemmRows);
+  const int tile = (int)(n / kGemmRows), r = (int)(n - (int64_t)tile * kGemmRows);
+  float sum = 0.0f;
+  for (int ks = 0; ks < p.ksplit; ++ks) sum += p.partials[((int64_t)(ks * ntiles + tile) * M + t) * kGemmRows + r];
+  p.y[o] = sum * token_scale(p, t);
 }
 
 // ----------------------------------------------------------------------------
@@ -2717,6 +2750,26 @@ int64_t sa_lds_bytes(const Variant& v, int64_t K) {
   return index_;                                \
 }())
 
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// K splits of the tiled GEMM: enough workgroups (tiles x splits, about 400)
+// to fill the CUs when the row tiles alone do not, each split at least 4
+// stages long, and only while the partial sums fit the caller's workspace.
+int64_t gemm_split_ws_bytes(int M, int64_t N, int ksplit) {
+  const int64_t tiles = (N + kGemmRows - 1) / kGemmRows;
+  return align256((int64_t)ksplit * tiles * M * kGemmRows * 4);
+}
+
+int gemm_ksplit(int M, int64_t N, int64_t K, int64_t ws_cap) {
+  const int64_t tiles = (N + kGemmRows - 1) / kGemmRows;
+  const int64_t nst = K / kGemmStageK;
+  int64_t s = (400 + tiles / 2) / tiles;
+  if (s > nst / 4) s = nst / 4;
+  if (s < 1) s = 1;
+  while (s > 1 && gemm_split_ws_bytes(M, N, (int)s) > ws_cap) --s;
+  return (int)s;
+}
+
 // Default variant per (M, N, K): the fastest variant of MI355X sweeps over
 // the Qwen3-32B projection and LM-head shapes (graph-replayed back-to-back
 // launches, each projection's weights rotated over >= 576 MB of copies so
@@ -2725,8 +2778,7 @@ int64_t sa_lds_bytes(const Variant& v, int64_t K) {
 // the CUs where whole tiles would leave some idle (tile_rows_for).  The
 // LDS-copy kernels need K % 256 == 0; other K use the register-staged
 // kernels.
-int default_variant(int M, int64_t N, int64_t K, bool epi) {
-  (void)epi;
+int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
   auto fmma_sa = [&](int i, int otherwise) {
@@ -2739,6 +2791,13 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   // exist; the epilogue keeps the GEMV kernels)
   if (M > 16 && !epi && N >= 16384 && K % kGemmStageK == 0)
     return M > 64 ? VARIANT("gemm_m128") : M > 32 ? VARIANT("gemm_m64") : VARIANT("gemm_m32");
+  // 65..128 tokens on long rows of few output rows (down_proj, K >= 16384):
+  // the tiled GEMM split along K, when the caller's workspace holds the
+  // partial sums of the full split (fewer splits leave CUs idle)
+  if (M > 64 && !epi && K >= 16384 && K % kGemmStageK == 0) {
+    const int s = gemm_ksplit(M, N, K, kNoWsCap);
+    if (s == 1 || gemm_split_ws_bytes(M, N, s) <= ws_cap) return VARIANT("gemm_m128");
+  }
   // 65..128 tokens: eight 16-token column tiles; 33..64: four; 17..32: two;
   // 9..16: all 16 token columns of one tile (the register-staged MFMA kernel)
   if (M > 64) return VARIANT("lmfma_m128_r2_w4_p1");
@@ -2784,7 +2843,6 @@ int default_variant(int M, int64_t N, int64_t K, bool epi) {
   return VARIANT("lmfma_m8_r1_w4_p1");
 }
 
-int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
 // LDS of the staged kernel: activation codes and scales for MT tokens and
 // the block scales of the workgroup's rows, each padded to whole KB
@@ -2800,7 +2858,7 @@ size_t reset_state_bytes(int window) {
   return (b + 15) & ~(size_t)15;
 }
 
-GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
+GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   int vi = -1;
   // the LDS-staged kernel addresses a row tile and the activation with
   // 32-bit buffer offsets
@@ -2828,7 +2886,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // covers M and it fits the shape
   const int forced = g_forced_variant.load(std::memory_order_relaxed);
   if (forced >= 0 && forced < kNumVariants && kVariants[forced].mt >= M && fits(forced)) vi = forced;
-  if (vi < 0) vi = default_variant(M, N, K, epi);
+  if (vi < 0) vi = default_variant(M, N, K, epi, ws_cap);
   if (!fits(vi))
     vi = mt_of(M) <= 2   ? VARIANT("direct_m2_g64_r1_w4_p1")
          : mt_of(M) <= 4 ? VARIANT("mfma_m4_r2_w8_p1")
@@ -2847,10 +2905,13 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
   // f16 activation elements a workgroup may stage in LDS: 64 KiB, or 48 KiB
   // when the epilogue's reduction buffers share the LDS
   const int64_t budget = epi ? 24576 : 32768;
+  c.ksplit = 1;
   if (v.kind == GEMM) {
     c.kp = (int)K;
     c.rows_per_wg = kGemmRows;
-    c.grid = (N + kGemmRows - 1) / kGemmRows;
+    const int64_t tiles = (N + kGemmRows - 1) / kGemmRows;
+    c.ksplit = gemm_ksplit(M, N, K, ws_cap);
+    c.grid = tiles * c.ksplit;
     c.lds_bytes = 2 * (int64_t)gemm_stage_bytes(v.mt);
   } else if (v.kind == WSTREAM) {
     c.kp = (int)K;
@@ -2895,10 +2956,12 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi) {
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = v.kind == STAGED ? staged_lds_bytes(v, K) : 0;
   }
-  // workspace (epilogue only): the per-token tickets, per-workgroup softmax
-  // partials, then the slice partials
+  // workspace: with the epilogue, the per-token tickets, per-workgroup
+  // softmax partials, then the slice partials; for a split-K GEMM its
+  // partial sums
   c.ws_bytes =
       epi ? align256(kEpiTicketBytes + merge_slices_offset(c.grid, c.mt) + (int64_t)c.mt * kMergeGroups * 16) : 0;
+  if (c.ksplit > 1) c.ws_bytes = gemm_split_ws_bytes(M, N, c.ksplit);
   return c;
 }
 
@@ -2916,8 +2979,8 @@ int set_gemv_tuning(const char* variant, int balance) {
 const char* gemv_variant_name(int vi) { return vi >= 0 && vi < kNumVariants ? kVariants[vi].name : "?"; }
 const char* gemv_variant_by_index(int i) { return i >= 0 && i < kNumVariants ? kVariants[i].name : nullptr; }
 
-size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi) {
-  return (size_t)choose_gemv_config(M, N, K, epi).ws_bytes;
+size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
+  return (size_t)choose_gemv_config(M, N, K, epi, ws_cap).ws_bytes;
 }
 
 hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const uint8_t* a_codes,
@@ -2949,7 +3012,14 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   const Variant& v = kVariants[cfg.variant];
   void (*fn)(GemvParams) = epi ? v.epi : v.plain;
   if (v.plain_k64 && K % 64 == 0) fn = epi ? v.epi_k64 : v.plain_k64;
+  p.ksplit = cfg.ksplit;
+  if (cfg.ksplit > 1) p.partials = reinterpret_cast<float*>(wsb);
   hipLaunchKernelGGL(fn, dim3((unsigned)cfg.grid), dim3(v.nw * 64), (size_t)cfg.lds_bytes, stream, p);
+  if (cfg.ksplit > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)(((int64_t)M * N + 255) / 256)), dim3(256), 0, stream, p);
+  }
   if (epi) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

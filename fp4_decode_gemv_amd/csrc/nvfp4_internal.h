@@ -72,9 +72,13 @@ struct GemvConfig {
   // workspace layout (byte offset of the epilogue partials) and total size
   // (0 = none needed)
   int64_t ws_bytes;
+  int ksplit;  // tiled GEMM: K splits summed by a second launch (1 = none)
 };
 
-GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi);
+// ws_cap: the largest workspace the caller can offer (a split-K choice that
+// needs more falls back to kernels that need none)
+constexpr int64_t kNoWsCap = INT64_MAX;
+GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap = kNoWsCap);
 const char* gemv_variant_name(int variant);
 // Tuning override: force a variant by name (NULL or "" = none) and choose
 // the MFMA kernels' row mapping (balance 1 = even deal, 0 = whole tiles).
@@ -84,7 +88,7 @@ const char* gemv_variant_by_index(int index);  // NULL past the end
 
 // Workspace bytes the GEMV needs for this shape (with or without the
 // LM-head epilogue); 0 = none.
-size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi);
+size_t gemv_workspace_bytes(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap = kNoWsCap);
 size_t reset_state_bytes(int window);
 constexpr int kResetMaxWindow = 1024;
 

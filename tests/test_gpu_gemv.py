@@ -61,6 +61,22 @@ def test_gemm_default_full_compare(M, N, K):
     assert_gemv_close(y, y_ref, ref_abs, what=f"gemm M={M} N={N} K={K}")
 
 
+# the tiled GEMM split along K (65..128 tokens, K >= 16384, few row tiles):
+# partial sums in the workspace, then the in-order reduce; ragged last tile
+SPLIT_DEFAULT = [(65, 1000, 16384), (128, 777, 16640), (100, 5120, 16384)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_DEFAULT)
+def test_gemm_split_default_full_compare(M, N, K):
+    assert F.nvfp4_gemv_variant(M, N, K) == "gemm_m128"
+    assert F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, N, K) > 0
+    w = W.small_random_weights(N * 7 + K + M, N, K)
+    xb = W.small_random_bf16(M * 23 + K, M, K)
+    wq, aq, y = _run(M, N, K, w, xb, F.nvfp4_gemv_variant(M, N, K))
+    y_ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+    assert_gemv_close(y, y_ref, ref_abs, what=f"split gemm M={M} N={N} K={K}")
+
+
 # the wave-owned streaming kernel as the launch table picks it: 2..4 tokens on
 # qkv-like shapes and 3..4 tokens on many-row shapes, with a ragged last
 # 48-row workgroup and a ragged last 12-row wave block

@@ -65,6 +65,47 @@ def test_noalloc_matches_workspace_entry_point(with_epilogue):
             assert np.all(np.abs(H - R.entropy_rows(yg.astype(np.float64))) <= 1e-4)
 
 
+def _noalloc(aq, wq, M, N, K):
+    y = torch.full((M, N), float("nan"), device="cuda:0")
+    st = F.lib().nvfp4_gemv_smallm_noalloc(M, N, K, _ptr(aq.codes), _ptr(aq.scales), _ptr(aq.gscale),
+                                           _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.gscale), _ptr(y), None,
+                                           int(torch.cuda.current_stream().cuda_stream) or None)
+    assert st == F.NVFP4_OK, F.status_str(st)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def test_noalloc_split_gemm_partials_in_scratch():
+    """65..128 tokens on long K: the K-split GEMM keeps its partial sums in
+    the scratch array; the same kernels as with a caller workspace, so the
+    outputs are identical.  The second, smaller call reuses the scratch."""
+    for (M, N, K, seed) in ((128, 1000, 16384, 71), (65, 777, 16640, 72)):
+        print(f"[noalloc split] M={M} N={N} K={K}", flush=True)
+        assert F.nvfp4_gemv_variant(M, N, K) == "gemm_m128"
+        ws = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, N, K)
+        assert 0 < ws <= F.lib().nvfp4_gemv_noalloc_scratch_bytes()
+        w, xb, wq, aq = _case(M, N, K, seed)
+        y_ref = F.nvfp4_gemv_smallm(aq, wq).cpu().numpy()
+        yg = _noalloc(aq, wq, M, N, K)
+        assert np.array_equal(yg, y_ref)
+        ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+        assert_gemv_close(yg, ref, ref_abs, what=f"noalloc split M={M} N={N} K={K}")
+
+
+def test_noalloc_without_room_for_the_split_uses_another_kernel():
+    """A shape whose full K split would not fit the scratch array is not
+    refused: the launch table picks a kernel without partial sums there."""
+    M, N, K = 128, 2560, 16384
+    assert F.nvfp4_gemv_variant(M, N, K) == "gemm_m128"
+    assert F.nvfp4_workspace_size(F.NVFP4_OP_GEMV, M, N, K) > F.lib().nvfp4_gemv_noalloc_scratch_bytes()
+    print(f"[noalloc no-split] M={M} N={N} K={K}", flush=True)
+    w, xb, wq, aq = _case(M, N, K, 73)
+    yg = _noalloc(aq, wq, M, N, K)
+    ref, ref_abs = O.gemv_ref(O.quantize_act_bf16(xb), O.quantize_nvfp4(w))
+    assert_gemv_close(yg, ref, ref_abs, what=f"noalloc fallback M={M} N={N} K={K}")
+    assert_gemv_close(F.nvfp4_gemv_smallm(aq, wq).cpu().numpy(), ref, ref_abs, what="workspace entry")
+
+
 def test_noalloc_rejects_workspace_beyond_scratch():
     """A shape whose LM-head workspace exceeds the scratch array is refused
     before any launch; the output is untouched."""
