@@ -326,7 +326,7 @@ def nvfp4_quantize_act(x, gscale=None, ws=None, out: NvFp4Tensor | None = None, 
         raise ValueError("a static gscale must be out.gscale")
     need = 0 if per_token else nvfp4_workspace_size(NVFP4_OP_QUANT, M, 0, K)
     if need and ws is None:
-        ws = new_workspace(need, dev, stream)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _require_ws(ws, need, dev)
     _check(lib().nvfp4_quantize_act(_ptr(x), M, K, _ptr(out.codes), _ptr(out.scales), _ptr(out.gscale),
                                     flags, _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)),
@@ -360,7 +360,7 @@ def nvfp4_quantize_act_rotated(x, rot: int = 16, gscale=None, ws=None, out: NvFp
         raise ValueError("a static gscale must be out.gscale")
     need = nvfp4_workspace_size(NVFP4_OP_QUANT_ROTATED, M, rot, K) if gscale is None else 0
     if need and ws is None:
-        ws = new_workspace(need, dev, stream)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _require_ws(ws, need, dev)
     _check(lib().nvfp4_quantize_act_rotated(_ptr(x), M, K, int(rot), _ptr(out.codes), _ptr(out.scales),
                                             _ptr(out.gscale), flags, _ptr(ws), 0 if ws is None else ws.numel(),
@@ -483,7 +483,7 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
     dev = w.codes.device
     need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD if epi is not None else NVFP4_OP_GEMV, M, N, K)
     if need and ws is None:
-        ws = new_workspace(need, dev, stream)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _require_ws(ws, need, dev)
     ws_bytes = 0 if ws is None else ws.numel()
     fn = lib().nvfp4_gemv_smallm_token_scales if per_token else lib().nvfp4_gemv_smallm

@@ -10,12 +10,20 @@
 //   token  = the first token of the order whose cumulative mass exceeds
 //            u * (mass of the first n tokens), u in [0, 1) given per row.
 //
-// Four launches, no sort of the row.  Masses are 2^-40 fixed point
-// relative to the row maximum: e_i = exp2((z_i - z_max) * log2(e) / T) in
-// float32, m_i = floor(e_i * 2^40).  Integer sums are associative, so the
-// result does not depend on the order of the atomic adds and repeated calls
-// give the same token.
-//   1. (G workgroups per row) chunk maxima; the row's histogram is cleared.
+// Four launches (for a peaked row, in effect two), no sort of the row.
+// Masses are 2^-40 fixed point relative to the row maximum:
+// e_i = exp2((z_i - z_max) * log2(e) / T) in float32, m_i = floor(e_i 2^40).
+// Integer sums are associative, so the result does not depend on the order
+// of the atomic adds, and the one floating-point sum (the row mass of the
+// listed path) runs in a fixed order: repeated calls give the same token.
+//   1. (G workgroups of 1024 threads per row) chunk maxima; the row's
+//      histogram is cleared.
+//      Also each chunk's mass relative to its own maximum and a short list
+//      of its elements near that maximum.
+//   2. (first) every workgroup puts the row mass together from those
+//      records; when the listed elements (a prefix of the order) hold the
+//      nucleus, the cuts are found among them, workgroup 0 writes the token,
+//      the row is marked resolved and launches 2 to 4 end for it.
 //   2. (G workgroups per row) every element's bucket b_i of
 //      a_i = (z_max - z_i) log2(e) / T, 1/64 wide over 2048 buckets (the
 //      last holds a_i >= 31.98, masses below 2^-31.98), is stored as 16 bits
@@ -65,6 +73,11 @@ constexpr int kSub = 1 << kSubBits;     // == kThreads: one sub-bucket per threa
 constexpr int kCap = 256;               // candidates ranked directly
 constexpr int kList = 1024;             // per row: elements of the buckets the cuts can fall in
 constexpr int kBatch = 4;               // 16-byte loads per thread in flight
+constexpr int kSpec = 32;               // launch 1: elements a chunk lists for the listed path
+constexpr float kSpecSpan = 20.0f;      // ... those within 2^-20 of the chunk maximum's mass
+constexpr int kSpecMaxChunks = 256;     // longer rows (N > 1M) always take the histogram path
+constexpr int kSpecPre = 8;             // listed slots per thread loaded with the chunk records
+constexpr uint32_t kSpecOverflow = 0xFFFFFFFFu;
 constexpr int kBufferWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 static_assert(kSub == kThreads, "one refinement bucket per thread");
@@ -91,6 +104,10 @@ struct SampleArgs {
   uint64_t* lkey;             // [M][kList] key << 32 | index
   uint64_t* lmass;            // [M][kList]
   uint32_t* lbkt;             // [M][kList] bucket
+  uint64_t* csum;             // [M][G] chunk mass relative to the chunk maximum
+  uint32_t* ccnt;             // [M][G] elements the chunk listed, kSpecOverflow past kSpec
+  uint64_t* cand;             // [M][G][kSpec] listed elements: logit bits << 32 | index
+  uint32_t* resolved;         // [M] 1: launch 2 drew the row's token from the lists
 };
 
 // Ascending in sampling order: larger z first; -0 and +0 are one value.
@@ -117,13 +134,13 @@ __device__ __forceinline__ uint64_t fixed_mass(float a) {
 
 // log2(e) / T, or false when T is not positive and finite.  A denormal T
 // overflows the quotient; it is clamped (the greedy limit).
-__device__ __forceinline__ bool row_scale(const SampleArgs& a, int m, float& c) {
-  const float T = a.temperature[m];
+__device__ __forceinline__ bool scale_of(float T, float& c) {
   if (!(T > 0.0f) || !(T <= 3.4028234663852886e38f)) return false;
   c = 1.44269504088896340736f / T;
   c = c <= 3.4028234663852886e38f ? c : 3.4028234663852886e38f;
   return true;
 }
+__device__ __forceinline__ bool row_scale(const SampleArgs& a, int m, float& c) { return scale_of(a.temperature[m], c); }
 
 __device__ __forceinline__ float clamp_uniform(float u) {
   u = u >= 0.0f ? u : 0.0f;                         // NaN -> 0
@@ -253,27 +270,196 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const SampleArgs& a, 
                                            (int)(a.N * 4), kBufferWord3);
 }
 
-// ---- launch 1: chunk maxima; the row's histogram is cleared ----
+// ---- launch 1: chunk maxima, masses and short lists ----
+//
+// Each workgroup also sums its chunk's masses relative to the chunk maximum
+// z_g (2^-40 fixed point, exact) and lists the elements with
+// z >= z_g - kSpecSpan T / log2(e) (mass >= 2^-kSpecSpan of z_g's), up to
+// kSpec of them (more: the chunk overflows).
 template <bool VEC>
-__global__ __launch_bounds__(kWide) void sample_max_kernel(SampleArgs a) {
-  __shared__ float red[kWide / 64];
+__global__ __launch_bounds__(kThreads) void sample_first_kernel(SampleArgs a) {
+  static_assert(kSampleChunk == kThreads * 4, "one 16-byte group of the chunk per thread");
+  __shared__ float red[kWaves];
+  __shared__ uint64_t red64[kWaves];
+  __shared__ uint64_t list[kSpec];
+  __shared__ uint32_t nlist;
   const int g = blockIdx.x, m = blockIdx.y;
-  for (int e = g * kWide + (int)threadIdx.x; e < kBuckets; e += a.G * kWide) {
+  const int tid = threadIdx.x;
+  for (int e = g * kThreads + tid; e < kBuckets; e += a.G * kThreads) {
     a.hist[(int64_t)m * kBuckets + e] = 0;
     a.hcnt[(int64_t)m * kBuckets + e] = 0;
   }
-  if (g == 0 && threadIdx.x == 0) a.lcount[m] = 0;
-  u32x4_t v[4];
-  load_chunk<VEC>(row_rsrc(a, m), a.N, g, v);
+  const float T = a.temperature[m];  // issued with the chunk's loads
+  if (g == 0 && tid == 0) a.lcount[m] = 0;
+  if (tid == 0) nlist = 0;
+  // elements i0 .. i0 + 3 of the row
+  const int64_t i0 = (int64_t)g * kSampleChunk + (int64_t)tid * 4;
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(a, m);
+  u32x4_t v;
+  if constexpr (VEC) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(i0 < a.N ? (uint32_t)(i0 * 4) : kOutOfRange), 0, 0);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(i0 + q < a.N ? (uint32_t)((i0 + q) * 4) : kOutOfRange),
+                                                  0, 0);
+  }
   float zm = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t i0 = (int64_t)g * kSampleChunk + (int64_t)(j * kWide + threadIdx.x) * 4;
+  for (int q = 0; q < 4; ++q) zm = i0 + q < a.N ? fmaxf(zm, __uint_as_float(v[q])) : zm;
+  zm = wg_max<kThreads>(zm, red);  // barrier: nlist is set
+  const int64_t cg = (int64_t)m * a.G + g;
+  if (tid == 0) a.maxp[cg] = zm;
+  float c;
+  if (!scale_of(T, c) || a.G > kSpecMaxChunks) return;
+  const float thr = zm - kSpecSpan / c;
+  uint64_t s = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) zm = i0 + q < a.N ? fmaxf(zm, __uint_as_float(v[j][q])) : zm;
+  for (int q = 0; q < 4; ++q) {
+    const int64_t i = i0 + q;
+    const bool valid = i < a.N;
+    const float z = __uint_as_float(v[q]);
+    s += valid ? fixed_mass((zm - z) * c) : 0;
+    const bool want = valid && z >= thr;
+    const uint64_t mask = __ballot(want);
+    if (mask == 0) continue;
+    const int lane = tid & 63;
+    const int lead = __ffsll((unsigned long long)mask) - 1;
+    uint32_t slot0 = 0;
+    if (lane == lead) slot0 = atomicAdd(&nlist, (uint32_t)__popcll(mask));
+    slot0 = __shfl(slot0, lead, 64);
+    const uint32_t slot = slot0 + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+    if (want && slot < (uint32_t)kSpec) list[slot] = ((uint64_t)v[q] << 32) | (uint64_t)(uint32_t)i;
   }
-  zm = wg_max<kWide>(zm, red);
-  if (threadIdx.x == 0) a.maxp[(int64_t)m * a.G + g] = zm;
+  uint64_t tot;
+  (void)wg_excl_scan<kThreads>(s, tot, red64);  // barrier: every append has landed
+  const uint32_t n = nlist;
+  if (tid < kSpec && (uint32_t)tid < n) a.cand[cg * kSpec + tid] = list[tid];
+  if (tid == 0) {
+    a.csum[cg] = tot;
+    a.ccnt[cg] = n > (uint32_t)kSpec ? kSpecOverflow : n;
+  }
+}
+
+// ---- the listed path, at the start of launch 2 ----
+//
+// Every element at or above z_g - kSpecSpan T / log2(e) of a chunk that did
+// not overflow is listed, so with theta the largest of
+// (overflowed ? z_g : z_g - kSpecSpan T / log2(e)) over the chunks, the
+// lists hold every element of the row above theta: a prefix of the order.
+// With the row mass S = sum_g S_g 2^((z_g - z_max) log2(e) / T) (a fixed
+// summation order), when that prefix's mass reaches the nucleus threshold
+// both cuts lie in it and are found by ranking it.  Every workgroup of the
+// row computes the same result from launch 1's records; workgroup 0 writes
+// the token.  Returns whether the row was drawn, and the row maximum.
+__device__ __forceinline__ bool resolve_listed(const SampleArgs& a, int m, bool valid, float c, float u, bool writer,
+                                               float& zmax) {
+  __shared__ float szg[kSpecMaxChunks], sth[kSpecMaxChunks];
+  __shared__ uint32_t sn[kSpecMaxChunks];
+  __shared__ double sterm[kSpecMaxChunks];
+  __shared__ uint64_t ck[kCap], cm[kCap];
+  __shared__ uint32_t ncand;
+  __shared__ uint64_t cut_cum;
+  __shared__ int64_t cut_rank, cut_index;
+  static_assert(kCap == kWide && kSpecMaxChunks == kWide, "one chunk record and one listed element per thread");
+  const int tid = threadIdx.x;
+  const int G = a.G;
+  const int64_t row0 = (int64_t)m * G;
+  // one round trip: the chunk records (thread g holds chunk g) and the
+  // first listed slots
+  const bool has = tid < G;
+  const float zg = has ? a.maxp[row0 + tid] : -INFINITY;
+  const uint64_t sg = has ? a.csum[row0 + tid] : 0;
+  const uint32_t ng = has ? a.ccnt[row0 + tid] : 0u;
+  const int64_t nslots = (int64_t)G * kSpec;
+  uint64_t pre[kSpecPre];
+#pragma unroll
+  for (int k = 0; k < kSpecPre; ++k) {
+    const int64_t sl = tid + (int64_t)k * kWide;
+    pre[k] = sl < nslots ? a.cand[row0 * kSpec + sl] : 0;
+  }
+  if (has) {
+    szg[tid] = zg;
+    sn[tid] = ng;
+  }
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  // every thread reads the G records in chunk order: the row maximum, then
+  // each chunk's mass rescaled to it and its listing level; the sum and the
+  // level theta are taken in chunk order, so every thread (and every
+  // workgroup of the row) gets the same values
+  float zmx = -INFINITY;
+  for (int g = 0; g < G; ++g) zmx = fmaxf(zmx, szg[g]);
+  zmax = zmx;
+  if (!valid) return false;  // no usable temperature: launch 1 listed nothing
+  const float span = kSpecSpan / c;
+  if (has) {
+    sterm[tid] = (double)sg * (double)exp2f(-((zmx - zg) * c));
+    sth[tid] = ng == kSpecOverflow ? zg : zg - span;
+  }
+  __syncthreads();
+  double S = 0.0;
+  float th = -INFINITY;
+  for (int g = 0; g < G; ++g) {
+    S += sterm[g];
+    th = fmaxf(th, sth[g]);
+  }
+  // the listed elements above theta, with their masses relative to z_max
+  auto take = [&](int64_t sl, uint64_t e) {
+    const int g = (int)(sl / kSpec), j = (int)(sl % kSpec);
+    const uint32_t n = sl < nslots ? sn[g] : 0u;
+    const float z = __uint_as_float((uint32_t)(e >> 32));
+    const bool want = (uint32_t)j < (n < (uint32_t)kSpec ? n : (uint32_t)kSpec) && z > th;
+    const uint64_t mask = __ballot(want);
+    if (mask == 0) return;
+    const int lane = tid & 63;
+    const int lead = __ffsll((unsigned long long)mask) - 1;
+    uint32_t slot0 = 0;
+    if (lane == lead) slot0 = atomicAdd(&ncand, (uint32_t)__popcll(mask));
+    slot0 = __shfl(slot0, lead, 64);
+    const uint32_t slot = slot0 + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+    if (want && slot < (uint32_t)kCap) {
+      ck[slot] = ((uint64_t)order_key(z) << 32) | (e & 0xFFFFFFFFull);
+      cm[slot] = fixed_mass((zmx - z) * c);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kSpecPre; ++k) take(tid + (int64_t)k * kWide, pre[k]);
+  for (int64_t base = (int64_t)kSpecPre * kWide; base < nslots; base += kWide) {  // G > 64 only
+    const int64_t sl = base + tid;
+    take(sl, sl < nslots ? a.cand[row0 * kSpec + sl] : 0);
+  }
+  __syncthreads();
+  const uint32_t cnt = ncand;
+  if (cnt > (uint32_t)kCap || !(S >= 1.0)) return false;
+  // each thread ranks its element against all of them (and sums them all)
+  const bool mine = tid < (int)cnt;
+  const uint64_t key = mine ? ck[tid] : ~0ull, mm = mine ? cm[tid] : 0;
+  uint64_t pre_m = 0, nbf = 0, total = 0;
+  for (uint32_t j = 0; j < cnt; ++j) {
+    const uint64_t kj = ck[j], mj = cm[j];
+    const bool earlier = kj < key;
+    pre_m += earlier ? mj : 0;
+    nbf += earlier;
+    total += mj;
+  }
+  const uint64_t S64 = S < 1.8446744073709552e19 ? (uint64_t)S : ~0ull;
+  const uint64_t t1 = nucleus_threshold(a.top_p, S64);
+  if (total < t1) return false;
+  if (mine && pre_m < t1 && pre_m + mm >= t1) {
+    cut_cum = pre_m + mm;
+    cut_rank = (int64_t)nbf;
+  }
+  __syncthreads();
+  const uint64_t t2 = draw_threshold(u, cut_cum);
+  if (mine && pre_m < t2 && pre_m + mm >= t2) cut_index = (int64_t)(uint32_t)key;
+  __syncthreads();
+  if (writer && tid == 0) {
+    a.tokens[m] = (int32_t)cut_index;
+    if (a.nucleus) a.nucleus[m] = (int32_t)(cut_rank + 1);
+    a.resolved[m] = 1u;
+  }
+  return true;
 }
 
 // ---- launch 2: bucket of every element, mass histogram ----
@@ -284,11 +470,21 @@ __global__ __launch_bounds__(kWide) void sample_hist_kernel(SampleArgs a) {
   __shared__ float redf[kWide / 64];
   __shared__ uint64_t red64[kWide / 64];
   const int g = blockIdx.x, m = blockIdx.y;
-  float c;
-  if (!row_scale(a, m, c)) return;
+  // every load the row needs is issued before the first branch on them
+  const float T = a.temperature[m];
+  const float u = clamp_uniform(a.uniforms[m]);
   u32x4_t v[4];
   load_chunk<VEC>(row_rsrc(a, m), a.N, g, v);
-  const float zm = row_max<kWide>(a, m, redf);
+  float c;
+  const bool valid = scale_of(T, c);
+  float zm;
+  if (a.G <= kSpecMaxChunks) {
+    if (resolve_listed(a, m, valid, c, u, g == 0, zm)) return;
+  } else {
+    zm = row_max<kWide>(a, m, redf);
+  }
+  if (g == 0 && threadIdx.x == 0) a.resolved[m] = 0u;
+  if (!valid) return;
   for (int e = threadIdx.x; e < kBuckets; e += kWide) {
     lh[e] = 0;
     lc[e] = 0;
@@ -343,7 +539,7 @@ __global__ __launch_bounds__(kWide) void sample_collect_kernel(SampleArgs a) {
   __shared__ int slot[2];
   const int g = blockIdx.x, m = blockIdx.y;
   float c;
-  if (!row_scale(a, m, c)) return;
+  if (a.resolved[m] || !row_scale(a, m, c)) return;
   u32x4_t v[4];
   load_chunk<VEC>(row_rsrc(a, m), a.N, g, v);
   u16x4_t ids[4];
@@ -617,6 +813,7 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
   __shared__ Smem sm;
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
+  if (a.resolved[m]) return;
   // every input of the row is loaded up front (one round trip): the
   // histograms, this thread's list entry and the chunk maxima
   const uint64_t x0 = a.hist[(int64_t)m * kBuckets + 2 * tid], x1 = a.hist[(int64_t)m * kBuckets + 2 * tid + 1];
@@ -702,7 +899,8 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
 }
 
 struct SampleLayout {
-  int64_t G, bstride, maxp_off, hist_off, hcnt_off, bid_off, lcount_off, lkey_off, lmass_off, lbkt_off, bytes;
+  int64_t G, bstride, maxp_off, hist_off, hcnt_off, bid_off, lcount_off, lkey_off, lmass_off, lbkt_off, csum_off,
+      ccnt_off, cand_off, resolved_off, bytes;
 };
 
 SampleLayout sample_layout(int M, int64_t N) {
@@ -718,7 +916,11 @@ SampleLayout sample_layout(int M, int64_t N) {
   L.lkey_off = L.lcount_off + al((int64_t)M * 4);
   L.lmass_off = L.lkey_off + al((int64_t)M * kList * 8);
   L.lbkt_off = L.lmass_off + al((int64_t)M * kList * 8);
-  L.bytes = L.lbkt_off + al((int64_t)M * kList * 4);
+  L.csum_off = L.lbkt_off + al((int64_t)M * kList * 4);
+  L.ccnt_off = L.csum_off + al((int64_t)M * L.G * 8);
+  L.cand_off = L.ccnt_off + al((int64_t)M * L.G * 4);
+  L.resolved_off = L.cand_off + al((int64_t)M * L.G * kSpec * 8);
+  L.bytes = L.resolved_off + al((int64_t)M * 4);
   return L;
 }
 
@@ -735,15 +937,17 @@ hipError_t launch_sample_top_p(int M, int64_t N, const float* logits, const floa
                      reinterpret_cast<float*>(w + L.maxp_off), reinterpret_cast<unsigned long long*>(w + L.hist_off),
                      reinterpret_cast<uint32_t*>(w + L.hcnt_off), reinterpret_cast<uint16_t*>(w + L.bid_off),
                      reinterpret_cast<uint32_t*>(w + L.lcount_off), reinterpret_cast<uint64_t*>(w + L.lkey_off),
-                     reinterpret_cast<uint64_t*>(w + L.lmass_off), reinterpret_cast<uint32_t*>(w + L.lbkt_off)};
+                     reinterpret_cast<uint64_t*>(w + L.lmass_off), reinterpret_cast<uint32_t*>(w + L.lbkt_off),
+                     reinterpret_cast<uint64_t*>(w + L.csum_off), reinterpret_cast<uint32_t*>(w + L.ccnt_off),
+                     reinterpret_cast<uint64_t*>(w + L.cand_off), reinterpret_cast<uint32_t*>(w + L.resolved_off)};
   const bool vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
   const dim3 wide((unsigned)L.G, (unsigned)M);
   if (vec) {
-    hipLaunchKernelGGL(sample_max_kernel<true>, wide, dim3(kWide), 0, stream, a);
+    hipLaunchKernelGGL(sample_first_kernel<true>, wide, dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(sample_hist_kernel<true>, wide, dim3(kWide), 0, stream, a);
     hipLaunchKernelGGL(sample_collect_kernel<true>, wide, dim3(kWide), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(sample_max_kernel<false>, wide, dim3(kWide), 0, stream, a);
+    hipLaunchKernelGGL(sample_first_kernel<false>, wide, dim3(kThreads), 0, stream, a);
     hipLaunchKernelGGL(sample_hist_kernel<false>, wide, dim3(kWide), 0, stream, a);
     hipLaunchKernelGGL(sample_collect_kernel<false>, wide, dim3(kWide), 0, stream, a);
   }

@@ -285,7 +285,10 @@ const char* nvfp4_gemv_variant(int M, int64_t N, int64_t K, int lmhead);
  * aligned) of nvfp4_workspace_size(NVFP4_OP_SAMPLE, M, N, 0) bytes; it
  * needs no zero-fill (every call clears what it accumulates into) and holds
  * nothing between calls.  Outputs and ws must not overlap inputs or each
- * other.  Four launches on `stream`.
+ * other.  Four launches on `stream`; a row whose nucleus lies among its
+ * elements within 2^-20 of a chunk maximum's probability (a peaked
+ * distribution) is drawn at the start of the second, and the rest of the
+ * work is skipped for it.
  * Errors: NVFP4_ERR_SHAPE (M outside [1, 65535], N outside [1, 2^24 - 1]),
  * NVFP4_ERR_NULL, NVFP4_ERR_ALIGN, NVFP4_ERR_WORKSPACE, NVFP4_ERR_ARG
  * (top_p outside (0, 1], overlap), NVFP4_ERR_DEVICE, NVFP4_ERR_HIP.

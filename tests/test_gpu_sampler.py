@@ -83,6 +83,90 @@ def test_random_logits(N, top_p):
         assert np.all(tok == np.argmax(z, axis=1)) and np.all(nuc == 1)
 
 
+def _run_flags(z, T, top_p, u):
+    """Draws plus the per-row flag of the listed path (1: the token was
+    drawn from launch 1's short lists), read from the sampler's workspace,
+    whose layout ends with that [M] int32 array padded to 256 bytes.  The
+    workspace starts out filled with 0xFF bytes: it needs no zero-fill."""
+    M, N = z.shape
+    dev = torch.device("cuda:0")
+    need = F.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, M, N, 0)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    tok, nuc = F.nvfp4_sample_top_p(f32_dev(z), f32_dev(T), top_p, f32_dev(u), ws=ws)
+    torch.cuda.synchronize()
+    off = need - (M * 4 + 255) // 256 * 256
+    flags = ws[off:off + 4 * M].view(torch.int32).cpu().numpy()
+    return tok.cpu().numpy(), nuc.cpu().numpy(), flags
+
+
+def _peaked_rows(N, seed):
+    """Eight rows over an N(0, 2) bulk: k spikes in [35, 60] spread evenly
+    over the row, k = 1, 3 (three equal maxima), 8, 40, 120, 250, then 300
+    spikes in [59, 60], and bulk only.  The first launch lists a chunk's
+    elements within 20 log2(e)-units (13.9 T) of its maximum, at most 32:
+    on the 4096-element chunks of the long rows a spike chunk holds at most 7
+    spikes, so every spike within 13.9 T of the row maximum is listed and the
+    rest of the row is below 1e-5 of its mass; rows 0 to 5 are drawn by the
+    listed path for any top_p < 1.  Row 6 lists more elements than the
+    path ranks (256) and row 7's chunks all overflow: both take the
+    histogram path.  On short rows (one or two chunks) the spikes of rows 4
+    and 5 overflow their chunk as well."""
+    rng = np.random.default_rng(seed)
+    z = (2.0 * rng.standard_normal((8, N))).astype(np.float32)
+    for m, k in enumerate((1, 3, 8, 40, 120, 250, 300, 0)):
+        if k == 0:
+            continue
+        idx = np.unique(np.linspace(0, N - 1, min(k, N)).astype(np.int64))
+        lo = 59.0 if m == 6 else 35.0
+        z[m, idx] = rng.uniform(lo, 60.0, idx.size).astype(np.float32)
+        if k == 3:
+            z[m, idx] = np.float32(50.0)
+    T = np.array([0.6, 1.0, 1.7, 0.6, 1.0, 1.7, 1.0, 1.0], dtype=np.float32)
+    return z, T
+
+
+@pytest.mark.parametrize("N", [151936, 151937, 4099, 1000])
+@pytest.mark.parametrize("top_p", [0.95, 0.5, 1e-6, 1.0])
+def test_peaked_rows_one_launch_path(N, top_p):
+    """Rows whose nucleus lies among a few high logits are drawn from the
+    first launch's short lists (flag read back from the workspace), mixed in
+    one call with rows that need the histogram path; all against the oracle.  N = 151937
+    takes the scalar loads, 4099 a 3-element last chunk, 1000 one chunk."""
+    print(f"[sampler peaked] N={N} top_p={top_p}", flush=True)
+    z, T = _peaked_rows(N, 40 + N % 97)
+    u = np.random.default_rng(N + 3).random(8).astype(np.float32)
+    tok, nuc, flags = _run_flags(z, T, top_p, u)
+    for m in range(8):
+        _check_row(z[m], float(T[m]), top_p, float(u[m]), int(tok[m]), int(nuc[m]))
+    assert set(np.unique(flags)) <= {0, 1}, flags
+    if top_p < 1.0:
+        if N > 100000:
+            assert np.all(flags[:6] == 1), flags
+        else:
+            assert np.all(flags[:4] == 1) and np.all(flags[4:6] == 0), flags
+    assert flags[6] == 0 and flags[7] == 0, flags
+    if top_p == 1e-6:
+        assert np.all(tok == np.argmax(z, axis=1)) and np.all(nuc == 1)
+    # the three equal maxima are drawn in index order
+    if top_p < 1.0:
+        top3 = np.flatnonzero(z[1] == np.float32(50.0))
+        assert tok[1] in top3
+
+
+def test_peaked_rows_past_the_listed_path_length():
+    """Rows of more than 256 chunks of 4096 (N > 1M) always take the
+    histogram path, peaked or not."""
+    N = 1_100_000
+    print(f"[sampler long] N={N}", flush=True)
+    z, T = _peaked_rows(N, 41)
+    z, T = z[[0, 3]], T[[0, 3]]
+    u = np.array([0.3, 0.8], dtype=np.float32)
+    tok, nuc, flags = _run_flags(z, T, 0.95, u)
+    assert np.all(flags == 0), flags
+    for m in range(2):
+        _check_row(z[m], float(T[m]), 0.95, float(u[m]), int(tok[m]), int(nuc[m]))
+
+
 def test_equal_logits_take_index_order():
     """All logits equal: every element lands in one bucket and shares one key,
     so the cut points come from the tie walk; the closed form is exact."""
@@ -161,29 +245,37 @@ def test_invalid_temperature_and_clamped_uniforms():
     assert tok[5] == int(np.argmax(z[5]))         # u < 0 draws the top token
 
 
-def test_repeatable_and_graph_replays_match_eager():
+@pytest.mark.parametrize("peaked", [False, True])
+def test_repeatable_and_graph_replays_match_eager(peaked):
+    """Repeated calls and graph replays on one workspace (never cleared
+    between calls): identical draws."""
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(14)
     M, N = 8, 151936
-    z = f32_dev((rng.standard_normal((M, N)) * 3.0).astype(np.float32))
-    T = f32_dev(np.full(M, 0.6, dtype=np.float32))
+    if peaked:
+        zh, Th = _peaked_rows(N, 17)
+        z, T = f32_dev(zh), f32_dev(Th)
+    else:
+        z = f32_dev((rng.standard_normal((M, N)) * 3.0).astype(np.float32))
+        T = f32_dev(np.full(M, 0.6, dtype=np.float32))
     u = f32_dev(rng.random(M).astype(np.float32))
-    tok, nuc = F.nvfp4_sample_top_p(z, T, 0.95, u)
+    ws = torch.full((F.nvfp4_workspace_size(F.NVFP4_OP_SAMPLE, M, N, 0),), 0xFF, dtype=torch.uint8, device=dev)
+    tok, nuc = F.nvfp4_sample_top_p(z, T, 0.95, u, ws=ws)
     torch.cuda.synchronize()
     ref = (tok.cpu().numpy().copy(), nuc.cpu().numpy().copy())
     for _ in range(3):
-        t2, n2 = F.nvfp4_sample_top_p(z, T, 0.95, u)
+        t2, n2 = F.nvfp4_sample_top_p(z, T, 0.95, u, ws=ws)
         torch.cuda.synchronize()
         assert np.array_equal(t2.cpu().numpy(), ref[0]) and np.array_equal(n2.cpu().numpy(), ref[1])
     s = torch.cuda.Stream()
     tg = torch.empty(M, dtype=torch.int32, device=dev)
     ng = torch.empty(M, dtype=torch.int32, device=dev)
     with torch.cuda.stream(s):
-        F.nvfp4_sample_top_p(z, T, 0.95, u, tokens=tg, nucleus=ng, stream=s)
+        F.nvfp4_sample_top_p(z, T, 0.95, u, tokens=tg, nucleus=ng, ws=ws, stream=s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        F.nvfp4_sample_top_p(z, T, 0.95, u, tokens=tg, nucleus=ng, stream=s)
+        F.nvfp4_sample_top_p(z, T, 0.95, u, tokens=tg, nucleus=ng, ws=ws, stream=s)
     for _ in range(4):
         tg.fill_(-7)
         ng.fill_(-7)
