@@ -479,11 +479,13 @@ def nvfp4_gemv_smallm(a: NvFp4Tensor, w: NvFp4Tensor, y=None, epi: Epilogue | No
     when needed and not given).  ``M`` (default: a's rows) may use only the
     first rows of ``a``.  An activation with one global scale per row goes
     to the per-token entry point."""
+    import torch
+
     M, N, K, y, per_token, ce = _gemv_args(a, w, y, epi, M)
     dev = w.codes.device
     need = nvfp4_workspace_size(NVFP4_OP_GEMV_LMHEAD if epi is not None else NVFP4_OP_GEMV, M, N, K)
     if need and ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = new_workspace(need, dev, stream)  # zero-filled: the epilogue's tickets start at zero
     _require_ws(ws, need, dev)
     ws_bytes = 0 if ws is None else ws.numel()
     fn = lib().nvfp4_gemv_smallm_token_scales if per_token else lib().nvfp4_gemv_smallm

@@ -279,28 +279,49 @@ __device__ __forceinline__ void lmhead_partials(const GemvParams& p, const float
 // past the per-XCD L2s), and the ticket is taken only after the write has
 // completed, so no release fence is needed (on gfx950 a release writes back
 // the whole L2).
-// Workspace: kEpiTicketBytes of tickets [kMaxTokens] (zero at rest), the
+// Workspace: kEpiTicketBytes of tickets [kMaxTokens] spaced kTicketStride
+// apart (zero at rest), the
 // row-tile partials [ntiles][MT], then the slice partials [MT][kMergeGroups],
 // all float4 {max, S, T, -}.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeGroups = 64;
 constexpr int kMergeLoads = 4;  // partials per thread and round, all loads in flight at once
-constexpr int64_t kEpiTicketBytes = 512;
-static_assert(kEpiTicketBytes >= 4 * kMaxTokens, "one ticket per token");
+// uint32 slots between two tokens' tickets: one 128-byte line each, so the
+// tokens' device-scope ticket atomics do not contend for one line (with
+// eight tokens packed into one line the merge took about 5 us longer)
+constexpr int kTicketStride = 32;
+constexpr int64_t kEpiTicketBytes = (4 * kTicketStride * kMaxTokens + 255) / 256 * 256;
+static_assert(kMergeGroups <= 64, "one slice partial per lane of a wave");
 
 // offset of the slice partials from the row-tile partials
 __host__ __device__ constexpr int64_t merge_slices_offset(int64_t ntiles, int mt) {
   return (ntiles * mt * 16 + 255) / 256 * 256;
 }
 
-// merge the (m, S, T) of the lane `x` places above into this lane's
-__device__ __forceinline__ void merge_from_lane(float& m, float& S, float& T, int x) {
-  const float mb = __shfl_xor(m, x, 64), Sb = __shfl_xor(S, x, 64), Tb = __shfl_xor(T, x, 64);
-  merge_partial(m, S, T, mb, Sb, Tb);
+// The merged (m, S, T) of a wave's 64 partials, in every lane: DPP moves
+// within each row of 16 lanes (rotations by 8 and 4, then the quad
+// permutations), then the four rows in index order through readlane.  The
+// order is fixed, so the result is reproducible.
+__device__ __forceinline__ void wave_merge(float& m, float& S, float& T) {
+  merge_partial(m, S, T, dpp<0x128>(m), dpp<0x128>(S), dpp<0x128>(T));  // row_ror:8
+  merge_partial(m, S, T, dpp<0x124>(m), dpp<0x124>(S), dpp<0x124>(T));  // row_ror:4
+  merge_partial(m, S, T, dpp<0xB1>(m), dpp<0xB1>(S), dpp<0xB1>(T));     // quad_perm [1,0,3,2]
+  merge_partial(m, S, T, dpp<0x4E>(m), dpp<0x4E>(S), dpp<0x4E>(T));     // quad_perm [2,3,0,1]
+  auto lane_f = [](float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+  };
+  float gm = lane_f(m, 0), gS = lane_f(S, 0), gT = lane_f(T, 0);
+  merge_partial(gm, gS, gT, lane_f(m, 16), lane_f(S, 16), lane_f(T, 16));
+  merge_partial(gm, gS, gT, lane_f(m, 32), lane_f(S, 32), lane_f(T, 32));
+  merge_partial(gm, gS, gT, lane_f(m, 48), lane_f(S, 48), lane_f(T, 48));
+  m = gm;
+  S = gS;
+  T = gT;
 }
 
 __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams p, int mt, int ntiles) {
   __shared__ float wm[kMergeThreads / 64], wS[kMergeThreads / 64], wt[kMergeThreads / 64];
+  __shared__ float sring[kResetMaxWindow];
   __shared__ uint32_t is_last;
   const int m = blockIdx.x / kMergeGroups, grp = blockIdx.x % kMergeGroups;
   if (m >= p.M) return;
@@ -328,9 +349,8 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams 
       merge_partial(gm, Sm, Tm, in ? q[j][0] : -INFINITY, q[j][1], q[j][2]);
     }
   }
-  // across the wave (xor butterfly), then across the waves through LDS
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) merge_from_lane(gm, Sm, Tm, x);
+  // across the wave, then across the waves through LDS in index order
+  wave_merge(gm, Sm, Tm);
   if (lane == 0) {
     wm[wave] = gm;
     wS[wave] = Sm;
@@ -344,53 +364,76 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams 
     __hip_atomic_store(sp + 1, Sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(sp + 2, Tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the slice partial has landed
-    const uint32_t done = __hip_atomic_fetch_add(&p.tickets[m], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* ticket = p.tickets + (int64_t)m * kTicketStride;
+    const uint32_t done = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = done == kMergeGroups - 1 ? 1u : 0u;
-    if (done == kMergeGroups - 1) __hip_atomic_store(&p.tickets[m], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == kMergeGroups - 1) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (is_last == 0 || wave != 0) return;
-  // the token's last slice workgroup, wave 0: lane g takes slice g, then the
-  // butterfly in a fixed order (the result does not depend on which
-  // workgroup came last)
-  const float* sp = slices + ((int64_t)m * kMergeGroups + lane) * 4;
+  // the token's last slice workgroup, wave 0.  One round trip: lane g loads
+  // slice partial g, every lane the sequence state, and the lanes the ring
+  // of the last entropies (the state block holds p.epi.window of them)
+  ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
+  const float* ring = reinterpret_cast<const float*>(st + 1);
+  const float* sp = slices + ((int64_t)m * kMergeGroups + (lane < kMergeGroups ? lane : 0)) * 4;
   gm = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   Sm = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   Tm = __hip_atomic_load(sp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  static_assert(kMergeGroups == 64, "one slice partial per lane of a wave");
+  if (lane >= kMergeGroups) {  // no slice: the empty partial
+    gm = -INFINITY;
+    Sm = Tm = 0.0f;
+  }
+  const int64_t count0 = st->count;
+  const int32_t st_window = st->window, len0 = st->step_len;
+  const double sum_all0 = st->sum_all, step_sum0 = st->step_sum;
+  const bool new_step = p.epi.step_start[m] != 0;
+  const int wcap = p.epi.window < kResetMaxWindow ? p.epi.window : kResetMaxWindow;
+  float rv[kResetMaxWindow / 64];
 #pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) merge_from_lane(gm, Sm, Tm, x);
-  if (lane != 0) return;
+  for (int k = 0; k < kResetMaxWindow / 64; ++k) {
+    const int i = lane + 64 * k;
+    rv[k] = i < wcap ? ring[i] : 0.0f;
+  }
+  wave_merge(gm, Sm, Tm);
   const double Sd = Sm, Td = Tm;
   const float H = (float)(log(Sd) - Td / Sd);
-  p.epi.entropy[m] = H;
   // ---- ReSET update: update with H first, then decide ----
-  ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
-  float* ring = reinterpret_cast<float*>(st + 1);
   // the ring holds the window the state was initialised with; never index
   // past the smaller of that and the caller's window
-  int w = st->window < p.epi.window ? st->window : p.epi.window;
+  int w = st_window < p.epi.window ? st_window : p.epi.window;
   if (w < 1) w = 1;
-  const double h = (double)H;
-  if (st->count == 0 || p.epi.step_start[m]) {
-    st->step_sum = 0.0;
-    st->step_len = 0;
+  const int slot = (int)(count0 % w);
+#pragma unroll
+  for (int k = 0; k < kResetMaxWindow / 64; ++k) {
+    const int i = lane + 64 * k;
+    if (i < wcap) sring[i] = i == slot ? H : rv[k];
   }
-  ring[st->count % w] = H;
-  st->count += 1;
-  st->sum_all += h;
-  st->step_sum += h;
-  st->step_len += 1;
-  const int64_t nwin = st->count < w ? st->count : w;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the wave's LDS writes before its reads
+  if (lane != 0) return;
+  const double h = (double)H;
+  const bool reset = count0 == 0 || new_step;
+  const int64_t count = count0 + 1;
+  const double sum_all = sum_all0 + h;
+  const double step_sum = (reset ? 0.0 : step_sum0) + h;
+  const int32_t step_len = (reset ? 0 : len0) + 1;
+  const int64_t nwin = count < w ? count : w;
   double wsum = 0.0;
-  for (int64_t i = st->count - nwin; i < st->count; ++i) wsum += (double)ring[i % w];
-  const double hbar = st->sum_all / (double)st->count;
-  const double hstep = st->step_len <= w ? wsum / (double)nwin : st->step_sum / (double)st->step_len;
+  for (int64_t i = count - nwin; i < count; ++i) wsum += (double)sring[i % w];
+  const double hbar = sum_all / (double)count;
+  const double hstep = step_len <= w ? wsum / (double)nwin : step_sum / (double)step_len;
   const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
   float T_t;
   if (p.epi.mode == 1) T_t = p.epi.t_base;                                   // BASE
   else if (p.epi.mode == 2) T_t = h < (double)p.epi.tau0 ? p.epi.t_low : p.epi.t_high;  // fixed threshold
   else T_t = h < tau ? p.epi.t_low : p.epi.t_high;                           // ReSET
+  float* ring_w = reinterpret_cast<float*>(st + 1);
+  ring_w[slot] = H;
+  st->count = count;
+  st->sum_all = sum_all;
+  st->step_sum = step_sum;
+  st->step_len = step_len;
+  p.epi.entropy[m] = H;
   p.epi.temperature[m] = T_t;
 }
 

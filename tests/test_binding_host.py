@@ -79,3 +79,22 @@ def test_quantize_rejects_bad_inputs():
         F.nvfp4_quantize_act(x, gscale=torch.ones(2), per_token=True)
     with pytest.raises(ValueError, match="out.codes"):
         F.nvfp4_quantize_act(x, out=nv(2, 64))
+
+
+def test_every_wrapper_that_uses_torch_imports_it():
+    """The binding imports torch inside each function (the module loads
+    without it); a wrapper that forgot would fail only on the path that
+    first touches torch, e.g. allocating a workspace the caller did not
+    pass."""
+    import ast
+    import inspect
+
+    tree = ast.parse(inspect.getsource(F))
+    missing = []
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef):
+            uses = any(isinstance(n, ast.Name) and n.id == "torch" for n in ast.walk(fn))
+            imports = any(isinstance(n, ast.Import) and any(a.name == "torch" for a in n.names) for n in ast.walk(fn))
+            if uses and not imports:
+                missing.append(fn.name)
+    assert not missing, missing

@@ -204,3 +204,30 @@ def test_epilogue_graph_replays_match_eager(M):
         assert np.array_equal(tmp.cpu().numpy(), ref_T[r]), (r, tmp.cpu().numpy(), ref_T[r])
         y.zero_()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_epilogue_workspace_allocated_by_the_binding_starts_at_zero():
+    """Without a caller workspace the binding allocates one; its ticket
+    counters must start at zero even where the allocator hands back memory
+    that held other data (a freed block of the same size filled with 0xFF
+    is reused by the caching allocator)."""
+    dev = torch.device("cuda:0")
+    M, N, K = 4, 5000, 512
+    w = W.small_random_weights(91, N, K, scale=0.2)
+    xb = W.small_random_bf16(92, M, K)
+    wq, aq = F.nvfp4_pack_weights(f32_dev(w)), F.nvfp4_quantize_act(bf16_dev(xb))
+    need = F.nvfp4_workspace_size(F.NVFP4_OP_GEMV_LMHEAD, M, N, K)
+    for _ in range(2):
+        junk = torch.full((max(16, (need + 15) // 16 * 16),), 0xFF, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        del junk
+        ent = torch.full((M,), float("nan"), device=dev)
+        tmp = torch.full((M,), float("nan"), device=dev)
+        epi = F.Epilogue(step_start=torch.ones(M, dtype=torch.uint8, device=dev), state=F.new_reset_state(M, 8, dev),
+                         entropy=ent, temperature=tmp, window=8)
+        y = F.nvfp4_gemv_smallm(aq, wq, epi=epi)
+        torch.cuda.synchronize()
+        H = ent.cpu().numpy()
+        assert np.all(np.isfinite(H)) and np.all(np.isfinite(tmp.cpu().numpy())), (H, tmp)
+        assert np.all(np.abs(H - R.entropy_rows(y.cpu().numpy().astype(np.float64))) <= 1e-4)
+
