@@ -104,8 +104,8 @@ struct SampleArgs {
   uint64_t* lkey;             // [M][kList] key << 32 | index
   uint64_t* lmass;            // [M][kList]
   uint32_t* lbkt;             // [M][kList] bucket
-  uint64_t* csum;             // [M][G] chunk mass relative to the chunk maximum
-  uint32_t* ccnt;             // [M][G] elements the chunk listed, kSpecOverflow past kSpec
+  u32x4_t* crec;              // [M][G] chunk record: maximum (float bits), elements listed
+                              // (kSpecOverflow past kSpec), mass relative to the maximum (u64)
   uint64_t* cand;             // [M][G][kSpec] listed elements: logit bits << 32 | index
   uint32_t* resolved;         // [M] 1: launch 2 drew the row's token from the lists
 };
@@ -335,10 +335,9 @@ __global__ __launch_bounds__(kThreads) void sample_first_kernel(SampleArgs a) {
   (void)wg_excl_scan<kThreads>(s, tot, red64);  // barrier: every append has landed
   const uint32_t n = nlist;
   if (tid < kSpec && (uint32_t)tid < n) a.cand[cg * kSpec + tid] = list[tid];
-  if (tid == 0) {
-    a.csum[cg] = tot;
-    a.ccnt[cg] = n > (uint32_t)kSpec ? kSpecOverflow : n;
-  }
+  if (tid == 0)
+    a.crec[cg] = u32x4_t{__float_as_uint(zm), n > (uint32_t)kSpec ? kSpecOverflow : n, (uint32_t)tot,
+                         (uint32_t)(tot >> 32)};
 }
 
 // ---- the listed path, at the start of launch 2 ----
@@ -368,9 +367,10 @@ __device__ __forceinline__ bool resolve_listed(const SampleArgs& a, int m, bool 
   // one round trip: the chunk records (thread g holds chunk g) and the
   // first listed slots
   const bool has = tid < G;
-  const float zg = has ? a.maxp[row0 + tid] : -INFINITY;
-  const uint64_t sg = has ? a.csum[row0 + tid] : 0;
-  const uint32_t ng = has ? a.ccnt[row0 + tid] : 0u;
+  const u32x4_t rec = has ? a.crec[row0 + tid] : u32x4_t{0xFF800000u, 0u, 0u, 0u};
+  const float zg = __uint_as_float(rec[0]);
+  const uint32_t ng = rec[1];
+  const uint64_t sg = ((uint64_t)rec[3] << 32) | rec[2];
   const int64_t nslots = (int64_t)G * kSpec;
   uint64_t pre[kSpecPre];
 #pragma unroll
@@ -389,6 +389,7 @@ __device__ __forceinline__ bool resolve_listed(const SampleArgs& a, int m, bool 
   // level theta are taken in chunk order, so every thread (and every
   // workgroup of the row) gets the same values
   float zmx = -INFINITY;
+#pragma unroll 8
   for (int g = 0; g < G; ++g) zmx = fmaxf(zmx, szg[g]);
   zmax = zmx;
   if (!valid) return false;  // no usable temperature: launch 1 listed nothing
@@ -400,6 +401,7 @@ __device__ __forceinline__ bool resolve_listed(const SampleArgs& a, int m, bool 
   __syncthreads();
   double S = 0.0;
   float th = -INFINITY;
+#pragma unroll 8
   for (int g = 0; g < G; ++g) {
     S += sterm[g];
     th = fmaxf(th, sth[g]);
@@ -436,6 +438,7 @@ __device__ __forceinline__ bool resolve_listed(const SampleArgs& a, int m, bool 
   const bool mine = tid < (int)cnt;
   const uint64_t key = mine ? ck[tid] : ~0ull, mm = mine ? cm[tid] : 0;
   uint64_t pre_m = 0, nbf = 0, total = 0;
+#pragma unroll 8
   for (uint32_t j = 0; j < cnt; ++j) {
     const uint64_t kj = ck[j], mj = cm[j];
     const bool earlier = kj < key;
@@ -899,8 +902,8 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
 }
 
 struct SampleLayout {
-  int64_t G, bstride, maxp_off, hist_off, hcnt_off, bid_off, lcount_off, lkey_off, lmass_off, lbkt_off, csum_off,
-      ccnt_off, cand_off, resolved_off, bytes;
+  int64_t G, bstride, maxp_off, hist_off, hcnt_off, bid_off, lcount_off, lkey_off, lmass_off, lbkt_off, crec_off,
+      cand_off, resolved_off, bytes;
 };
 
 SampleLayout sample_layout(int M, int64_t N) {
@@ -916,9 +919,8 @@ SampleLayout sample_layout(int M, int64_t N) {
   L.lkey_off = L.lcount_off + al((int64_t)M * 4);
   L.lmass_off = L.lkey_off + al((int64_t)M * kList * 8);
   L.lbkt_off = L.lmass_off + al((int64_t)M * kList * 8);
-  L.csum_off = L.lbkt_off + al((int64_t)M * kList * 4);
-  L.ccnt_off = L.csum_off + al((int64_t)M * L.G * 8);
-  L.cand_off = L.ccnt_off + al((int64_t)M * L.G * 4);
+  L.crec_off = L.lbkt_off + al((int64_t)M * kList * 4);
+  L.cand_off = L.crec_off + al((int64_t)M * L.G * 16);
   L.resolved_off = L.cand_off + al((int64_t)M * L.G * kSpec * 8);
   L.bytes = L.resolved_off + al((int64_t)M * 4);
   return L;
@@ -938,7 +940,7 @@ hipError_t launch_sample_top_p(int M, int64_t N, const float* logits, const floa
                      reinterpret_cast<uint32_t*>(w + L.hcnt_off), reinterpret_cast<uint16_t*>(w + L.bid_off),
                      reinterpret_cast<uint32_t*>(w + L.lcount_off), reinterpret_cast<uint64_t*>(w + L.lkey_off),
                      reinterpret_cast<uint64_t*>(w + L.lmass_off), reinterpret_cast<uint32_t*>(w + L.lbkt_off),
-                     reinterpret_cast<uint64_t*>(w + L.csum_off), reinterpret_cast<uint32_t*>(w + L.ccnt_off),
+                     reinterpret_cast<u32x4_t*>(w + L.crec_off),
                      reinterpret_cast<uint64_t*>(w + L.cand_off), reinterpret_cast<uint32_t*>(w + L.resolved_off)};
   const bool vec = N % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
   const dim3 wide((unsigned)L.G, (unsigned)M);
