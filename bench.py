@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "31c81731c74038de17b1a237560e118a8c4d9648b3ab6eb53563b25e4bf8955e",
-    "bytes_per_step": 1115895930,
+    "sha256": "e873141063fae891fef7ab8974ac52f7f27d7d672469a6d9a342fc5a67bba886",
+    "bytes_per_step": 1124449032,
 }
 
 
