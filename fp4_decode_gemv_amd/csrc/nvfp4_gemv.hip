@@ -2487,18 +2487,25 @@ __device__ __forceinline__ void gemm_load_decode(const char* codes, const char* 
 
 template <int MT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
-  constexpr int WR = MT >= 128 ? 2 : 4;  // wave grid: WR row groups x WC token groups
-  constexpr int WC = 4 / WR;
+  // wave grid: KH halves of each stage's K x WR row groups x WC token groups.
+  // At 128 tokens the two 128-element halves of a stage go to different
+  // waves (KH = 2), each over all 128 rows and 64 tokens: every token is
+  // decoded once per stage instead of twice, at the price of adding the two
+  // halves' accumulators at the end
+  constexpr int KH = MT >= 128 ? 2 : 1;
+  constexpr int WR = MT >= 128 ? 1 : 4;
+  constexpr int WC = 4 / WR / KH;
   constexpr int RT = kGemmRows / WR / 16;  // 16-row tiles per wave
   constexpr int CT = MT / WC / 16;         // 16-token tiles per wave
   constexpr int STAGE = gemm_stage_bytes(MT);
+  static_assert(KH * WR * WC == kGemmThreads / 64, "one wave per (K half, row group, token group)");
   extern __shared__ uint4 lds4[];
   char* lds = reinterpret_cast<char*>(lds4);
   const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g = lane >> 4;
-  const int wr = wave % WR, wc = wave / WR;
+  const int kh = wave % KH, wr = (wave / KH) % WR, wc = wave / KH / WR;
   const int64_t N = p.N, K = p.K;
   const int M = p.M;
   // workgroup b: row tile b % ntiles, K split b / ntiles (stages st0 .. st1 - 1)
@@ -2535,7 +2542,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
     const char* acodes = wscales + 2048;
     const char* ascales = acodes + (MT * 128 < 1024 ? 1024 : MT * 128);
 #pragma unroll
-    for (int seg = 0; seg < 2; ++seg) {
+    for (int sg = 0; sg < 2 / KH; ++sg) {
+      const int seg = KH == 2 ? kh : sg;  // the stage's 128-element half
       half8_t a[CT][4];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) gemm_load_decode(acodes, ascales, wc * (MT / WC) + 16 * ct + j, seg, g, a[ct]);
@@ -2551,6 +2559,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
       }
     }
     __syncthreads();  // the buffer is refilled two stages on
+  }
+  if constexpr (KH == 2) {
+    // the second half's accumulators through LDS (the stage buffers are
+    // free: the loop ended on a barrier); the first half's waves add them
+    // and finish
+    float4_t* red = reinterpret_cast<float4_t*>(lds);
+    static_assert(WC * RT * CT * 64 * 16 <= 2 * STAGE, "the exchange fits the stage buffers");
+    if (kh == 1) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) red[((wc * RT + rt) * CT + ct) * 64 + lane] = acc[rt][ct];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[rt][ct] += red[((wc * RT + rt) * CT + ct) * 64 + lane];
   }
   // lane (j, g) holds D[4 g + i][j]: weight rows 4 g .. 4 g + 3 of the tile
   // for token j of the token tile
