@@ -233,13 +233,17 @@ int nvfp4_gemv_smallm_token_scales(int M, int64_t N, int64_t K,
  * nvfp4_gemv_smallm for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same operation, kernels, arguments and errors, without a
- * workspace argument.  The workspace (the LM-head epilogue's partials; a
- * plain projection needs none) lives in a static device array of
+ * workspace argument.  The workspace (the LM-head epilogue's partials, or
+ * the partial sums of a projection whose K is split over workgroups; other
+ * plain projections need none) lives in a static device array of
  * nvfp4_gemv_noalloc_scratch_bytes() = 16 MiB that each GPU the library runs
  * on holds until the process ends; nothing is allocated or freed by the
  * call.  Shapes whose workspace would exceed it (the LM-head epilogue at
  * about N * M > 10^7, e.g. M = 128 with N > 130000) return
- * NVFP4_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * NVFP4_ERR_WORKSPACE before any HIP call; a plain projection whose K split
+ * would not fit is served by a kernel that needs no workspace (its outputs
+ * may then differ from nvfp4_gemv_smallm's in rounding, within the same
+ * tolerance).  Every call on one GPU shares
  * that GPU's array: calls that can overlap on one GPU (different streams
  * without ordering, or threads) race and give undefined results; calls on
  * one stream are ordered.  The array keeps the last call's contents; no
