@@ -37,18 +37,21 @@
 //      depends on the mass through the first cut, which lies within the
 //      first bucket, so it lies in a bucket range the histogram also gives.
 //      The elements of these buckets (key = order-preserving bits of z, then
-//      index; mass; bucket) are appended to a per-row list.
-//   4. (one workgroup of 1024 threads per row) each cut takes the candidates
-//      of its bucket from the list (the number of elements before the bucket
-//      comes from the count prefix).  If the list overflowed or the bucket is
-//      large, one pass over the bucket ids (a packed compare skips each group
-//      of eight without the bucket) collects that bucket's elements, reading
-//      only their logits.  With at most 256 candidates each one sums the
-//      masses of the candidates before it and the one whose interval holds t
-//      is the cut; with more, the pass also histogrammed them by the next 10
-//      bits of the key and the search narrows to one sub-bucket and repeats
-//      (at most four times; then all candidates share one logit and, having
-//      equal masses, the cut is found by counting them in index order).
+//      index; mass; bucket) are gathered per workgroup in LDS and appended to
+//      a per-row list of 4096 with one atomic per workgroup.
+//   4. (one workgroup of 1024 threads per row) the list is copied into LDS;
+//      each cut takes the elements of its bucket from it (the number of
+//      elements before the bucket comes from the count prefix).  With at most
+//      256 of them each one sums the masses of those before it and the one
+//      whose interval holds t is the cut; with more, they are histogrammed
+//      in LDS by the next 10 bits of the unique key (order key, index) and
+//      the search narrows to one sub-bucket until at most 256 remain.  If
+//      the list overflowed, passes over the bucket ids (a packed compare
+//      skips each group of eight without the bucket) collect the bucket's
+//      elements, reading only their logits, narrowing the same way by the
+//      order key (at most four times; then all candidates share one logit
+//      and, having equal masses, the cut is found by counting them in index
+//      order).
 //
 // Logits must be finite; T must be positive and finite (otherwise the row's
 // token is -1 and its nucleus size 0).  u outside [0, 1) is clamped into it.
@@ -71,7 +74,9 @@ constexpr int kBuckets = 2048;          // level-0 buckets, 1/64 of a unit of a_
 constexpr int kSubBits = 10;            // key bits per refinement level
 constexpr int kSub = 1 << kSubBits;     // == kThreads: one sub-bucket per thread
 constexpr int kCap = 256;               // candidates ranked directly
-constexpr int kList = 1024;             // per row: elements of the buckets the cuts can fall in
+constexpr int kList = 4096;             // per row: elements of the buckets the cuts can fall in
+constexpr int kListPer = kList / kThreads;  // list entries per selection thread
+constexpr int kWGList = 1024;           // launch 3: elements a workgroup gathers before publishing
 constexpr int kBatch = 4;               // 16-byte loads per thread in flight
 constexpr int kSpec = 32;               // launch 1: elements a chunk lists for the listed path
 constexpr float kSpecSpan = 20.0f;      // ... those within 2^-20 of the chunk maximum's mass
@@ -537,12 +542,19 @@ __global__ __launch_bounds__(kWide) void sample_hist_kernel(SampleArgs a) {
 template <bool VEC>
 __global__ __launch_bounds__(kWide) void sample_collect_kernel(SampleArgs a) {
   __shared__ uint64_t h[kBuckets];
+  // this workgroup's elements of the planned buckets, gathered in LDS and
+  // published with one device-scope atomic (one per wave step contended on
+  // the row's counter across the XCDs)
+  __shared__ uint64_t gkey[kWGList], gmass[kWGList];
+  __shared__ uint32_t gbkt[kWGList];
+  __shared__ uint32_t gn, gbase;
   __shared__ float redf[kWide / 64];
   __shared__ uint64_t red64[kWide / 64];
   __shared__ int slot[2];
   const int g = blockIdx.x, m = blockIdx.y;
   float c;
   if (a.resolved[m] || !row_scale(a, m, c)) return;
+  if (threadIdx.x == 0) gn = 0;  // ordered before its first use by the scans' barriers
   u32x4_t v[4];
   load_chunk<VEC>(row_rsrc(a, m), a.N, g, v);
   u16x4_t ids[4];
@@ -583,16 +595,32 @@ __global__ __launch_bounds__(kWide) void sample_collect_kernel(SampleArgs a) {
       const int lane = threadIdx.x & 63;
       const int lead = __ffsll((unsigned long long)mask) - 1;
       uint32_t slot0 = 0;
-      if (lane == lead) slot0 = atomicAdd(&a.lcount[m], (uint32_t)__popcll(mask));
+      if (lane == lead) slot0 = atomicAdd(&gn, (uint32_t)__popcll(mask));
       slot0 = __shfl(slot0, lead, 64);
       const uint32_t slot = slot0 + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-      if (want && slot < (uint32_t)kList) {
+      if (want && slot < (uint32_t)kWGList) {
         const float z = __uint_as_float(v[j][q]);
-        const int64_t o = (int64_t)m * kList + slot;
-        a.lkey[o] = ((uint64_t)order_key(z) << 32) | (uint64_t)(uint32_t)i;
-        a.lmass[o] = fixed_mass((zm - z) * c);
-        a.lbkt[o] = (uint32_t)b;
+        gkey[slot] = ((uint64_t)order_key(z) << 32) | (uint64_t)(uint32_t)i;
+        gmass[slot] = fixed_mass((zm - z) * c);
+        gbkt[slot] = (uint32_t)b;
       }
+    }
+  }
+  __syncthreads();
+  const uint32_t n = gn;
+  if (n == 0) return;
+  // more than this workgroup could gather: push the row's count past the
+  // list so that the selection takes the passes over the row
+  if (threadIdx.x == 0) gbase = atomicAdd(&a.lcount[m], n <= (uint32_t)kWGList ? n : (uint32_t)kList + 1u);
+  __syncthreads();
+  if (n > (uint32_t)kWGList) return;
+  for (uint32_t e = threadIdx.x; e < n; e += kWide) {
+    const uint32_t slot = gbase + e;
+    if (slot < (uint32_t)kList) {
+      const int64_t o = (int64_t)m * kList + slot;
+      a.lkey[o] = gkey[e];
+      a.lmass[o] = gmass[e];
+      a.lbkt[o] = gbkt[e];
     }
   }
 }
@@ -605,12 +633,16 @@ struct Smem {
   uint32_t cs[kSub];      // refinement: count per sub-bucket
   uint64_t ckey[kCap];    // candidates: key << 32 | index
   uint64_t cmass[kCap];
+  uint64_t lk[kList];     // launch 3's list (keys, masses), copied once
+  uint64_t lm[kList];
+  uint32_t sel[kList];    // a cut's bucket: positions of its elements in the list
   uint64_t red64[kWaves];
   float redf[kWaves];
   uint32_t ncand;
   int slot[2];
   int pick;
   uint64_t pick_before;
+  uint32_t pick_nb, pick_cnt;
   int64_t sel_index, sel_rank;
   uint64_t sel_cum;
 };
@@ -668,6 +700,70 @@ __device__ __forceinline__ Cut rank_candidates(uint64_t t, uint64_t before, uint
   }
   __syncthreads();
   return Cut{sm.sel_index, sm.sel_rank, sm.sel_cum};
+}
+
+// The cut among the cnt elements of one bucket, list entries sm.sel[0..cnt)
+// of sm.lk / sm.lm (all of the bucket's elements, ordered after nb elements
+// of mass `before`).
+// The composite keys (order key << 32 | index) are unique, so narrowing by
+// 10 key bits at a time (mass and count per sub-bucket, the sub-bucket
+// whose interval holds t) reaches at most kCap elements after a few levels,
+// which rank_candidates ranks directly.  Everything stays in LDS.
+__device__ __forceinline__ Cut rank_listed(uint64_t t, uint64_t before, uint64_t nb, uint32_t cnt, Smem& sm) {
+  const int tid = threadIdx.x;
+  static_assert(kSub == kThreads, "one sub-bucket per thread");
+  uint64_t prefix = 0;  // the active elements' key >> sh
+  int sh = 64;
+  uint32_t act = cnt;
+  while (act > (uint32_t)kCap) {
+    const int w = sh < kSubBits ? sh : kSubBits;
+    const int top = 64 - sh;  // key bits already fixed
+    sh -= w;
+    __syncthreads();
+    sm.hs[tid] = 0;
+    sm.cs[tid] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < cnt; i += kThreads) {
+      const uint32_t e = sm.sel[i];
+      const uint64_t k = sm.lk[e];
+      if (top == 0 || (k >> (sh + w)) == prefix) {
+        const int sub = (int)((k >> sh) & (uint64_t)((1u << w) - 1u));
+        atomicAdd((unsigned long long*)&sm.hs[sub], (unsigned long long)sm.lm[e]);
+        atomicAdd(&sm.cs[sub], 1u);
+      }
+    }
+    __syncthreads();
+    uint64_t tot, totn;
+    const uint64_t hm = sm.hs[tid], hc = sm.cs[tid];
+    const uint64_t ex = wg_excl_scan<kThreads>(hm, tot, sm.red64);
+    const uint64_t exn = wg_excl_scan<kThreads>(hc, totn, sm.red64);
+    if (before + ex < t && before + ex + hm >= t) {
+      sm.pick = tid;
+      sm.pick_before = before + ex;
+      sm.pick_nb = (uint32_t)exn;
+      sm.pick_cnt = (uint32_t)hc;
+    }
+    __syncthreads();
+    prefix = (prefix << w) | (uint64_t)sm.pick;
+    before = sm.pick_before;
+    nb += sm.pick_nb;
+    act = sm.pick_cnt;
+  }
+  // the active elements (at most kCap) into the directly ranked set
+  __syncthreads();
+  if (tid == 0) sm.ncand = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < cnt; i += kThreads) {
+    const uint32_t e = sm.sel[i];
+    const uint64_t k = sm.lk[e];
+    if (sh == 64 || (k >> sh) == prefix) {
+      const uint32_t slot = atomicAdd(&sm.ncand, 1u);
+      sm.ckey[slot] = k;  // slot < act <= kCap
+      sm.cmass[slot] = sm.lm[e];
+    }
+  }
+  __syncthreads();
+  return rank_candidates(t, before, nb, act, sm);
 }
 
 // Visit the row's bucket ids eight at a time: f(base, v) for the 16-byte
@@ -822,10 +918,18 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
   const uint64_t x0 = a.hist[(int64_t)m * kBuckets + 2 * tid], x1 = a.hist[(int64_t)m * kBuckets + 2 * tid + 1];
   const uint32_t n0 = a.hcnt[(int64_t)m * kBuckets + 2 * tid], n1 = a.hcnt[(int64_t)m * kBuckets + 2 * tid + 1];
   const uint32_t listed = a.lcount[m];
-  static_assert(kList == kThreads, "one list entry per thread");
-  const uint32_t my_bkt = a.lbkt[(int64_t)m * kList + tid];
-  const uint64_t my_key = a.lkey[(int64_t)m * kList + tid];
-  const uint64_t my_mass = a.lmass[(int64_t)m * kList + tid];
+  static_assert(kList % kThreads == 0, "whole list entries per thread");
+  // the list: buckets stay in registers, keys and masses go to LDS (written
+  // below, once the loads have landed).  The first kThreads entries come
+  // with the other loads; the rest only when the list is that long
+  uint32_t my_bkt[kListPer];
+  uint64_t my_key[kListPer], my_mass[kListPer];
+  {
+    const int64_t o = (int64_t)m * kList + tid;
+    my_bkt[0] = a.lbkt[o];
+    my_key[0] = a.lkey[o];
+    my_mass[0] = a.lmass[o];
+  }
   float c;
   const float u = clamp_uniform(a.uniforms[m]);
   const float zm = row_max<kThreads>(a, m, sm.redf);
@@ -845,6 +949,19 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
     sm.c0[2 * tid] = (uint32_t)(exn + n0);
     sm.c0[2 * tid + 1] = (uint32_t)(exn + n0 + n1);
   }
+  sm.lk[tid] = my_key[0];
+  sm.lm[tid] = my_mass[0];
+  const int nlist = listed < (uint32_t)kList ? (int)listed : kList;
+#pragma unroll
+  for (int e = 1; e < kListPer; ++e) {
+    my_bkt[e] = 0xFFFFFFFFu;  // no bucket
+    if (e * kThreads < nlist) {  // uniform
+      const int64_t o = (int64_t)m * kList + tid + e * kThreads;
+      my_bkt[e] = a.lbkt[o];
+      sm.lk[tid + e * kThreads] = a.lkey[o];
+      sm.lm[tid + e * kThreads] = a.lmass[o];
+    }
+  }
   __syncthreads();
   const uint64_t S = sm.h0[kBuckets - 1];
   if (S == 0) {  // no finite maximum
@@ -860,9 +977,8 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
   // cut 0, the nucleus: the first element whose cumulative mass reaches
   // top_p * S; cut 1, the draw: the first element whose cumulative mass
   // exceeds u * (nucleus mass).  A cut in a bucket that launch 3 collected
-  // whole ranks that list; any other (list overflow, a bucket of more than
-  // kCap) takes the passes over the row.  One loop, so each path is
-  // inlined once.
+  // whole is found among that list in LDS; any other (the list overflowed)
+  // takes the passes over the row.  One loop, so each path is inlined once.
   const Plan pl = plan_cuts<kThreads>(sm.h0, a.top_p, u, sm.slot);
   uint64_t t = pl.t1;
   int64_t nucleus_size = 0;
@@ -875,18 +991,18 @@ __global__ __launch_bounds__(kThreads) void sample_select_kernel(SampleArgs a) {
       __syncthreads();
       if (tid == 0) sm.ncand = 0;
       __syncthreads();
-      if ((uint32_t)tid < listed && my_bkt == (uint32_t)b) {
-        const uint32_t slot = atomicAdd(&sm.ncand, 1u);
-        if (slot < (uint32_t)kCap) {
-          sm.ckey[slot] = my_key;
-          sm.cmass[slot] = my_mass;
+#pragma unroll
+      for (int e = 0; e < kListPer; ++e) {
+        if ((uint32_t)(tid + e * kThreads) < listed && my_bkt[e] == (uint32_t)b) {
+          const uint32_t slot = atomicAdd(&sm.ncand, 1u);  // < listed <= kList
+          sm.sel[slot] = (uint32_t)(tid + e * kThreads);
         }
       }
       __syncthreads();
       const uint32_t cnt = sm.ncand;
       const uint32_t in_b = sm.c0[b] - (b ? sm.c0[b - 1] : 0u);
-      if (cnt == in_b && cnt <= (uint32_t)kCap) {
-        cut = rank_candidates(t, b ? sm.h0[b - 1] : 0, b ? sm.c0[b - 1] : 0, cnt, sm);
+      if (cnt == in_b) {  // the whole bucket is in the list
+        cut = rank_listed(t, b ? sm.h0[b - 1] : 0, b ? sm.c0[b - 1] : 0, cnt, sm);
         ranked = true;
       }
     }

@@ -196,7 +196,8 @@ def test_near_flat_logits_refine_by_key_bits():
 def test_large_bucket_inside_the_collected_list():
     """600 near-equal logits (one bucket) hold most of the mass: the list of
     collected elements does not overflow, but the cut's bucket is larger than
-    the directly ranked set, so the cut takes the passes over the row."""
+    the directly ranked set, so the selection narrows it in LDS by key bits
+    before ranking."""
     rng = np.random.default_rng(16)
     M, N = 8, 20000
     z = np.full((M, N), -30.0, dtype=np.float32)
@@ -209,6 +210,39 @@ def test_large_bucket_inside_the_collected_list():
     for top_p in (0.95, 0.5):
         tok, nuc, exact = _check(z, T, top_p, u)
         assert exact >= M // 2, exact
+
+
+@pytest.mark.parametrize("layout", ["one_chunk", "spread"])
+def test_collected_list_overflow_takes_the_passes(layout):
+    """3000 near-equal logits carrying most of the mass, either inside one
+    4096-element chunk (that chunk's workgroup gathers more than it can hold
+    and marks the list incomplete) or spread over the row with 5000 of them
+    (the row's list of 4096 overflows): the selection falls back to the
+    passes over the row."""
+    rng = np.random.default_rng(21 if layout == "one_chunk" else 22)
+    M, N = 4, 60000
+    z = np.full((M, N), -40.0, dtype=np.float32)
+    for m in range(M):
+        if layout == "one_chunk":
+            idx = 8192 + rng.choice(4096, 3000, replace=False)
+        else:
+            idx = rng.choice(N, 5000, replace=False)
+        z[m, idx] = (0.004 * rng.random(idx.size)).astype(np.float32)
+    T = np.full(M, 1.0, dtype=np.float32)
+    u = rng.random(M).astype(np.float32)
+    for top_p in (0.95, 0.3):
+        _check(z, T, top_p, u)
+
+
+def test_flat_rows_on_the_full_vocabulary():
+    """Near-uniform rows of 151936 logits (the nucleus holds most of the
+    vocabulary; the cut buckets hold hundreds of elements each)."""
+    rng = np.random.default_rng(23)
+    M, N = 4, 151936
+    z = (rng.standard_normal((M, N)) * np.array([[0.3], [1.0], [2.0], [3.0]])).astype(np.float32)
+    T = np.array([1.0, 1.0, 0.8, 0.6], dtype=np.float32)
+    u = rng.random(M).astype(np.float32)
+    _check(z, T, 0.95, u)
 
 
 def test_few_distinct_values_with_many_ties():
