@@ -590,7 +590,7 @@ def bench_lm_head(args, stream):
     """LM head N=151936 K=5120 at M = 1 and 8: quantization + GEMV with the
     fused entropy / ReSET epilogue, the plain GEMV for comparison, and the
     top-p = 0.95 draw at the epilogue's temperatures (alone and as the tail
-    of the decode step)."""
+    of the decode step), and on flat synthetic rows."""
     import torch
 
     import fp4_decode_gemv_amd as F
@@ -646,14 +646,28 @@ def bench_lm_head(args, stream):
         t_plain = _graph_us(plain, args.reps, stream)
         t_tail = _graph_us(decode_tail, args.reps, stream)
         t_samp = _graph_us(sample, args.reps, stream)  # logits and temperatures of the last step
+        # a flat row (N(0, 1) logits at T = 1: the nucleus holds most of the
+        # vocabulary), which takes the histogram path of the draw
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(3600 + M)
+        z_flat = torch.randn((M, case.N), device=dev, generator=gen)
+        t_one = torch.ones(M, device=dev)
+
+        def sample_flat(i):
+            F.nvfp4_sample_top_p(z_flat, t_one, 0.95, uni, tokens=tok, nucleus=nuc, ws=sws, stream=stream)
+
+        t_flat = _graph_us(sample_flat, args.reps, stream)
+        del z_flat
         out.append({"M": M, "N": case.N, "K": case.K, "weight_bytes": wb,
                     "variant": F.nvfp4_gemv_variant(M, case.N, case.K, True),
                     "quant_gemv_epilogue_us": round(t_all, 2), "gemv_epilogue_us": round(t_epi, 2),
                     "gemv_plain_us": round(t_plain, 2), "gemv_epilogue_gbs": round(wb / t_epi / 1e3, 1),
                     "epilogue_overhead_us": round(t_epi - t_plain, 2),
-                    "sample_top_p_us": round(t_samp, 2), "quant_gemv_epilogue_sample_us": round(t_tail, 2)})
+                    "sample_top_p_us": round(t_samp, 2), "sample_top_p_flat_rows_us": round(t_flat, 2),
+                    "quant_gemv_epilogue_sample_us": round(t_tail, 2)})
         log(args, f"[lmhead] M={M} quant+gemv+epilogue {t_all:.2f} us, gemv+epilogue {t_epi:.2f} us "
-                  f"({wb / t_epi / 1e3:.0f} GB/s), plain gemv {t_plain:.2f} us, top-p draw {t_samp:.2f} us, "
+                  f"({wb / t_epi / 1e3:.0f} GB/s), plain gemv {t_plain:.2f} us, top-p draw {t_samp:.2f} us "
+                  f"(flat rows {t_flat:.2f} us), "
                   f"whole tail {t_tail:.2f} us")
     del copies, base
     torch.cuda.empty_cache()
