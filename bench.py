@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "e873141063fae891fef7ab8974ac52f7f27d7d672469a6d9a342fc5a67bba886",
-    "bytes_per_step": 1124449032,
+    "sha256": "efcb2c432691851758de04c0a9b54d4f387c807e8233ffc5ff9f0fdaed899ece",
+    "bytes_per_step": 1123840762,
 }
 
 
