@@ -643,6 +643,7 @@ struct Smem {
   int pick;
   uint64_t pick_before;
   uint32_t pick_nb, pick_cnt;
+  uint64_t kmin, kmax;
   int64_t sel_index, sel_rank;
   uint64_t sel_cum;
 };
@@ -706,28 +707,60 @@ __device__ __forceinline__ Cut rank_candidates(uint64_t t, uint64_t before, uint
 // of sm.lk / sm.lm (all of the bucket's elements, ordered after nb elements
 // of mass `before`).
 // The composite keys (order key << 32 | index) are unique, so narrowing by
-// 10 key bits at a time (mass and count per sub-bucket, the sub-bucket
-// whose interval holds t) reaches at most kCap elements after a few levels,
-// which rank_candidates ranks directly.  Everything stays in LDS.
+// up to 10 key bits at a time, just below the active keys' highest
+// differing bit (mass and count per sub-bucket, the sub-bucket whose
+// interval holds t), reaches at most kCap elements, which rank_candidates
+// ranks directly.  Everything stays in LDS.
 __device__ __forceinline__ Cut rank_listed(uint64_t t, uint64_t before, uint64_t nb, uint32_t cnt, Smem& sm) {
   const int tid = threadIdx.x;
   static_assert(kSub == kThreads, "one sub-bucket per thread");
-  uint64_t prefix = 0;  // the active elements' key >> sh
+  // the active elements: (key >> sh) == prefix (all of them while sh == 64)
+  uint64_t prefix = 0;
   int sh = 64;
   uint32_t act = cnt;
+  auto active = [&](uint64_t k) { return sh == 64 || (k >> sh) == prefix; };
   while (act > (uint32_t)kCap) {
-    const int w = sh < kSubBits ? sh : kSubBits;
-    const int top = 64 - sh;  // key bits already fixed
-    sh -= w;
+    // the active keys' range: the window starts below their highest
+    // differing bit, so every level splits the set (keys of one bucket share
+    // many leading bits)
+    uint64_t lo = ~0ull, hi = 0;
+    for (uint32_t i = tid; i < cnt; i += kThreads) {
+      const uint64_t k = sm.lk[sm.sel[i]];
+      if (active(k)) {
+        lo = k < lo ? k : lo;
+        hi = k > hi ? k : hi;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t lo2 = __shfl_xor(lo, o, 64), hi2 = __shfl_xor(hi, o, 64);
+      lo = lo2 < lo ? lo2 : lo;
+      hi = hi2 > hi ? hi2 : hi;
+    }
     __syncthreads();
+    if (tid == 0) {
+      sm.kmin = ~0ull;
+      sm.kmax = 0;
+    }
+    __syncthreads();
+    if ((tid & 63) == 0) {
+      atomicMin((unsigned long long*)&sm.kmin, (unsigned long long)lo);
+      atomicMax((unsigned long long*)&sm.kmax, (unsigned long long)hi);
+    }
+    __syncthreads();
+    const uint64_t d = sm.kmin ^ sm.kmax;  // != 0: more than one (unique) key is active
+    const int top = 63 - __clzll((long long)d);  // highest differing bit
+    const int shn = top + 1 > kSubBits ? top + 1 - kSubBits : 0;
+    const int w = top + 1 - shn;
+    const uint64_t base = top + 1 >= 64 ? 0 : sm.kmin >> (top + 1);  // bits every active key shares
     sm.hs[tid] = 0;
     sm.cs[tid] = 0;
     __syncthreads();
     for (uint32_t i = tid; i < cnt; i += kThreads) {
       const uint32_t e = sm.sel[i];
       const uint64_t k = sm.lk[e];
-      if (top == 0 || (k >> (sh + w)) == prefix) {
-        const int sub = (int)((k >> sh) & (uint64_t)((1u << w) - 1u));
+      if (active(k)) {
+        const int sub = (int)((k >> shn) & (uint64_t)((1u << w) - 1u));
         atomicAdd((unsigned long long*)&sm.hs[sub], (unsigned long long)sm.lm[e]);
         atomicAdd(&sm.cs[sub], 1u);
       }
@@ -744,7 +777,8 @@ __device__ __forceinline__ Cut rank_listed(uint64_t t, uint64_t before, uint64_t
       sm.pick_cnt = (uint32_t)hc;
     }
     __syncthreads();
-    prefix = (prefix << w) | (uint64_t)sm.pick;
+    prefix = (base << w) | (uint64_t)sm.pick;
+    sh = shn;
     before = sm.pick_before;
     nb += sm.pick_nb;
     act = sm.pick_cnt;
@@ -756,7 +790,7 @@ __device__ __forceinline__ Cut rank_listed(uint64_t t, uint64_t before, uint64_t
   for (uint32_t i = tid; i < cnt; i += kThreads) {
     const uint32_t e = sm.sel[i];
     const uint64_t k = sm.lk[e];
-    if (sh == 64 || (k >> sh) == prefix) {
+    if (active(k)) {
       const uint32_t slot = atomicAdd(&sm.ncand, 1u);
       sm.ckey[slot] = k;  // slot < act <= kCap
       sm.cmass[slot] = sm.lm[e];
