@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "efcb2c432691851758de04c0a9b54d4f387c807e8233ffc5ff9f0fdaed899ece",
-    "bytes_per_step": 1123840762,
+    "sha256": "3041804089d0a96740ee892f58c676d5596270e2b43e214494fdbd1503f664ef",
+    "bytes_per_step": 1122793558,
 }
 
 

@@ -1937,6 +1937,11 @@ __device__ __forceinline__ void stream_stage(const GemvParams& p, int T, int64_t
 // decoded to exact f16 values E2M1 * E4M3 (at most 6 significant bits) and
 // v_mfma_f32_16x16x32_f16 adds the products: D[4 wr + w][4 t + w] is row wr
 // with token t over window w.  Tokens >= M read as zeros.
+// Each chunk's activation codes and scales (256 contiguous bytes per token,
+// which every workgroup reads, so they stay in L2) come from global memory
+// into the register ring beside the weights'; only the tile's block scales
+// are copied into LDS.  Staging the whole activation in LDS instead held
+// every wave at a barrier until up to 115 KB had landed, and measured slower.
 template <int MT, int R, int NW, int U, bool EPI>
 __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
   static_assert(MT == 4 || MT == 8, "token sets of 4");
@@ -1953,10 +1958,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
   const int nchunks = (int)(K / kStreamChunk);
   const int n = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;  // chunks wave, wave + NW, ...
 
-  int64_t acb, asb;
-  stream_stage<NW>(p, MT, rows, tile0, wave, lane, acb, asb);
+  const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+  stage_to_lds<NW>(raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16)), l0, rows * (K / 16), wave, lane);
   const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t acr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_codes), (short)0,
+                                                                      (int)(M * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t asr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_scales), (short)0,
+                                                                      (int)(M * (K / 16)), kBufferWord3);
   const int b0 = 64 * kg + 16 * jw;  // byte of this lane within a row's chunk
   uint32_t vw[R];
   const char* lds = reinterpret_cast<const char*>(lds4);
@@ -1965,17 +1974,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
   for (int r = 0; r < R; ++r) {
     const int row = 4 * r + jr;
     vw[r] = row < rows ? (uint32_t)(row * (int)(K / 2) + b0) : kOffOut;
-    lsw[r] = lds + acb + asb + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;
+    lsw[r] = lds + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;
   }
-  bool tin[S];
-  const char* la[S];
-  const char* lsa[S];
+  uint32_t va[S], vsa[S];  // buffer offsets of the token's codes (+ 256 c) and scales (+ 32 c); past M: zeros
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int t = 4 * s + jr;
-    tin[s] = t < M;
-    la[s] = lds + (t < M ? t : 0) * (K / 2) + b0;                   // + 256 c
-    lsa[s] = lds + acb + (t < M ? t : 0) * (K / 16) + b0 / 8;       // + 32 c
+    va[s] = t < M ? (uint32_t)(t * (int)(K / 2) + b0) : kOffOut;
+    vsa[s] = t < M ? (uint32_t)(t * (int)(K / 16) + b0 / 8) : kOffOut;
   }
 
   float4_t acc[R][S];
@@ -1985,11 +1991,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
     for (int s = 0; s < S; ++s) acc[r][s] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   u32x4_t ring[U][R];
+  u32x4_t aring[U][S];
+  uint32_t sring[U][S];
   auto load = [&](int u, int i) {  // the wave's i-th chunk into slot u; past the last, the last again (never used)
     const int c = wave + (i < n ? i : n - 1) * NW;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], c * 256, 0);
+      sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], c * 32, 0);
+    }
   };
   if (n > 0) {
 #pragma unroll
@@ -1998,7 +2011,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  wait_vmcnt<(U * R < 63 ? U * R : 63)>();  // this wave's staging copies (issued first) have landed ...
+  constexpr int kRingLoads = U * (R + 2 * S);
+  wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();  // this wave's staging copies (issued first) have landed ...
   asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
   if (n > 0) {
     for (int i0 = 0; i0 < n; i0 += U) {
@@ -2009,17 +2023,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
         u32x4_t w[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) w[r] = ring[u][r];
+        u32x4_t ga[S];
+        uint32_t gs[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          ga[s] = aring[u][s];
+          gs[s] = sring[u][s];
+        }
         load(u, i + U);
         __builtin_amdgcn_sched_barrier(0);
         if (i < n) {
           half8_t b[S][4];
 #pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const uint4 a4 = *reinterpret_cast<const uint4*>(la[s] + 256 * c);
-            const u32x4_t av = tin[s] ? u32x4_t{a4.x, a4.y, a4.z, a4.w} : u32x4_t{0u, 0u, 0u, 0u};
-            const uint32_t as = tin[s] ? *reinterpret_cast<const uint16_t*>(lsa[s] + 32 * c) : 0u;
-            decode32_scaled(av, as, b[s]);
-          }
+          for (int s = 0; s < S; ++s) decode32_scaled(ga[s], gs[s], b[s]);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             half8_t a[4];
@@ -2087,7 +2103,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
 // workgroup stages the activation (and its rows' block scales) once for
 // NW x 4 R rows, and no partial sums cross waves: a row's four windows are
 // added inside the lane quad that holds them (DPP), then stored.
-template <int MT, int R, int NW, int U>
+template <int MT, int R, int NW, int U, bool AG = false>
 __global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
   static_assert(MT == 4 || MT == 8, "token sets of 4");
   constexpr int S = MT / 4;  // token sets
@@ -2104,9 +2120,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
   const int wrow0 = wave * 4 * R;  // first row of this wave within the tile
 
   int64_t acb, asb;
-  stream_stage<NW>(p, MT, rows, tile0, wave, lane, acb, asb);
+  if constexpr (AG) {
+    acb = asb = 0;
+    const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+    stage_to_lds<NW>(raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16)), l0, rows * (K / 16), wave, lane);
+  } else {
+    stream_stage<NW>(p, MT, rows, tile0, wave, lane, acb, asb);
+  }
   const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t acr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_codes), (short)0,
+                                                                      (int)(M * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t asr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_scales), (short)0,
+                                                                      (int)(M * (K / 16)), kBufferWord3);
   const int b0 = 64 * kg + 16 * jw;  // byte of this lane within a row's chunk
   uint32_t vw[R];
   const char* lds = reinterpret_cast<const char*>(lds4);
@@ -2120,12 +2146,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
   bool tin[S];
   const char* la[S];
   const char* lsa[S];
+  uint32_t va[S], vsa[S];  // AG: buffer offsets of the token's codes (+ 256 c) and scales (+ 32 c)
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int t = 4 * s + jr;
     tin[s] = t < M;
     la[s] = lds + (t < M ? t : 0) * (K / 2) + b0;               // + 256 c
     lsa[s] = lds + acb + (t < M ? t : 0) * (K / 16) + b0 / 8;   // + 32 c
+    va[s] = t < M ? (uint32_t)(t * (int)(K / 2) + b0) : kOffOut;
+    vsa[s] = t < M ? (uint32_t)(t * (int)(K / 16) + b0 / 8) : kOffOut;
   }
 
   float4_t acc[R][S];
@@ -2135,18 +2164,28 @@ __global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
     for (int s = 0; s < S; ++s) acc[r][s] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   u32x4_t ring[U][R];
+  u32x4_t aring[U][AG ? S : 1];
+  uint32_t sring[U][AG ? S : 1];
   auto load = [&](int u, int i) {  // chunk i into slot u; past the last, the last again (never used)
     const int c = i < n ? i : n - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+    if constexpr (AG) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], c * 256, 0);
+        sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], c * 32, 0);
+      }
+    }
   };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     load(u, u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  wait_vmcnt<(U * R < 63 ? U * R : 63)>();  // this wave's staging copies (issued first) have landed ...
+  constexpr int kRingLoads = U * (R + (AG ? 2 * S : 0));
+  wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();  // this wave's staging copies (issued first) have landed ...
   asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
   for (int i0 = 0; i0 < n; i0 += U) {
 #pragma unroll
@@ -2156,16 +2195,29 @@ __global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
       u32x4_t w[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) w[r] = ring[u][r];
+      u32x4_t ga[AG ? S : 1];
+      uint32_t gs[AG ? S : 1];
+      if constexpr (AG) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          ga[s] = aring[u][s];
+          gs[s] = sring[u][s];
+        }
+      }
       load(u, i + U);
       __builtin_amdgcn_sched_barrier(0);
       if (i < n) {
         half8_t b[S][4];
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const uint4 a4 = *reinterpret_cast<const uint4*>(la[s] + 256 * c);
-          const u32x4_t av = tin[s] ? u32x4_t{a4.x, a4.y, a4.z, a4.w} : u32x4_t{0u, 0u, 0u, 0u};
-          const uint32_t as = tin[s] ? *reinterpret_cast<const uint16_t*>(lsa[s] + 32 * c) : 0u;
-          decode32_scaled(av, as, b[s]);
+          if constexpr (AG) {
+            decode32_scaled(ga[s], gs[s], b[s]);  // tokens >= M loaded zeros
+          } else {
+            const uint4 a4 = *reinterpret_cast<const uint4*>(la[s] + 256 * c);
+            const u32x4_t av = tin[s] ? u32x4_t{a4.x, a4.y, a4.z, a4.w} : u32x4_t{0u, 0u, 0u, 0u};
+            const uint32_t as = tin[s] ? *reinterpret_cast<const uint16_t*>(lsa[s] + 32 * c) : 0u;
+            decode32_scaled(av, as, b[s]);
+          }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -2635,7 +2687,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemvParams p) {
 
 enum Kind {
   VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8, STREAM = 9,
-  FSTREAM = 10, GEMM = 11, WSTREAM = 12
+  FSTREAM = 10, GEMM = 11, WSTREAM = 12, WSTREAMAG = 13
 };
 
 struct Variant {
@@ -2722,6 +2774,12 @@ struct Variant {
 
 // the tiled GEMM has no LM-head form: its epilogue slot repeats the plain
 // kernel and is never chosen (fits() refuses GEMM with the epilogue)
+#define WSTREAM_AG_V(MT, R, NW, U)                                                                     \
+  Variant {                                                                                          \
+    "wstream_m" #MT "_r" #R "_w" #NW "_u" #U "_ag", WSTREAMAG, MT, 16, R, NW, U,                      \
+        gemv_wstream_kernel<MT, R, NW, U, true>, gemv_wstream_kernel<MT, R, NW, U, true>              \
+  }
+
 #define GEMM_V(MT)                                                                    \
   Variant {                                                                         \
     "gemm_m" #MT, GEMM, MT, 16, kGemmRows / 16, kGemmThreads / 64, 0, gemm_kernel<MT>, gemm_kernel<MT> \
@@ -2742,6 +2800,7 @@ const Variant kVariants[] = {
     // 9..128 tokens
     LMFMA_V(16, 2, 8, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(32, 2, 8, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(64, 2, 8, 1),
     LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1), GEMM_V(32), GEMM_V(64), GEMM_V(128), WSTREAM_V(4, 3, 4, 2),
+    WSTREAM_AG_V(4, 3, 4, 2),
     // fallbacks
     DIRECT_V(2, 64, 1, 4, 1), MFMA_V(4, 2, 8, 1), MFMA_V(8, 2, 8, 1), LMFMA_V(16, 1, 4, 1), LMFMA_V(32, 1, 4, 1),
     LMFMA_V(64, 1, 4, 1), LMFMA_V(128, 1, 4, 1),
@@ -2793,7 +2852,8 @@ int64_t epi_tile_rows(const Variant& v) {
   switch (v.kind) {
     case STREAM:
     case FSTREAM: return 4 * v.r;
-    case WSTREAM: return 4 * v.r * v.nw;
+    case WSTREAM:
+    case WSTREAMAG: return 4 * v.r * v.nw;
     case VALU:
     case DIRECT:
     case STAGED: return (int64_t)v.r * v.nw * (64 / v.g);
@@ -2801,10 +2861,11 @@ int64_t epi_tile_rows(const Variant& v) {
   }
 }
 
-// LDS a streaming kernel stages: activation and block scales (the FP4 form
-// for its 1 or 2 tokens, the f16 form for 8)
+// LDS a streaming kernel stages: the tile's block scales (the f16 form), and
+// the activation codes and scales of its one token beside them (the FP4 form)
 int64_t stream_kernel_lds(const Variant& v, int64_t K, int64_t tile_rows) {
-  return stream_lds_bytes(v.kind == FSTREAM ? 1 : v.mt, K, tile_rows);
+  if (v.kind == STREAM) return pad1k(tile_rows * (K / 16));
+  return stream_lds_bytes(1, K, tile_rows);
 }
 
 // LDS of the direct-to-LDS kernels with staged activation (f16 and FP4
@@ -2875,17 +2936,22 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
   // 2..8 tokens on long rows of few output rows (o_proj, down_proj): the
-  // streaming MFMA kernel, when its staged activation and scales fit
+  // streaming MFMA kernel, when its staged block scales fit
   if (M >= 2 && N < 16384 && K >= 8192 && K % kStreamChunk == 0) {
     const int i = M <= 4 ? VARIANT("stream_m4_r5_w4_u2") : VARIANT("stream_m8_r5_w4_u2");
     const Variant& v = kVariants[i];
     if (stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
       return i;
   }
-  // 2..4 tokens on qkv-like shapes (8192 <= N < 16384, K < 8192) and 3..4
-  // tokens on many-row shapes (N >= 16384): the wave-owned streaming kernel
-  if (!epi && K % kStreamChunk == 0 && M <= 4 && N >= 8192 &&
-      ((N < 16384 && K < 8192 && M >= 2) || (N >= 16384 && M >= 3))) {
+  // 2..4 tokens on qkv-like shapes (8192 <= N < 16384, K < 8192): the
+  // wave-owned streaming kernel with the activation read from L2; 3..4
+  // tokens on many-row shapes (N >= 16384): the same kernel with the
+  // activation staged in LDS (there it measured a little faster)
+  if (!epi && K % kStreamChunk == 0 && M >= 2 && M <= 4 && N >= 8192 && N < 16384 && K < 8192) {
+    const int i = VARIANT("wstream_m4_r3_w4_u2_ag");
+    if (pad1k(4 * kVariants[i].r * kVariants[i].nw * (K / 16)) <= kLdsBytes) return i;
+  }
+  if (!epi && K % kStreamChunk == 0 && M >= 3 && M <= 4 && N >= 16384) {
     const int i = VARIANT("wstream_m4_r3_w4_u2");
     if (stream_lds_bytes(4, K, 4 * kVariants[i].r * kVariants[i].nw) <= kLdsBytes) return i;
   }
@@ -2941,6 +3007,8 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
     if (kd == WSTREAM && (K % kStreamChunk != 0 || epi ||
                           stream_lds_bytes(v.mt, K, 4 * v.r * v.nw) > kLdsBytes))
       return false;
+    if (kd == WSTREAMAG && (K % kStreamChunk != 0 || epi || pad1k(4 * v.r * v.nw * (K / 16)) > kLdsBytes))
+      return false;
     // the LM-head instantiations also hold the static softmax slots
     // [MT][tile rows] of their partials
     const int64_t slot = epi ? (int64_t)4 * v.mt * epi_tile_rows(v) : 0;
@@ -2949,7 +3017,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
       return false;
     if (kd == STAGED && staged_lds_bytes(v, K) > 65536) return false;
     return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != FSTREAM &&
-            kd != GEMM && kd != WSTREAM) ||
+            kd != GEMM && kd != WSTREAM && kd != WSTREAMAG) ||
            (int64_t)16 * v.r * (K / 2) < (1ll << 31);
   };
   // tuning override, used when the forced variant's compiled token count
@@ -2983,11 +3051,11 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
     c.ksplit = gemm_ksplit(M, N, K, ws_cap);
     c.grid = tiles * c.ksplit;
     c.lds_bytes = 2 * (int64_t)gemm_stage_bytes(v.mt);
-  } else if (v.kind == WSTREAM) {
+  } else if (v.kind == WSTREAM || v.kind == WSTREAMAG) {
     c.kp = (int)K;
     c.rows_per_wg = 4 * v.r * v.nw;
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
-    c.lds_bytes = stream_lds_bytes(v.mt, K, c.rows_per_wg);
+    c.lds_bytes = v.kind == WSTREAM ? stream_lds_bytes(v.mt, K, c.rows_per_wg) : pad1k(c.rows_per_wg * (K / 16));
   } else if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA ||
       v.kind == STREAM || v.kind == FSTREAM) {
     c.kp = (int)K;

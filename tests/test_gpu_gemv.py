@@ -78,14 +78,16 @@ def test_gemm_split_default_full_compare(M, N, K):
 
 
 # the wave-owned streaming kernel as the launch table picks it: 2..4 tokens on
-# qkv-like shapes and 3..4 tokens on many-row shapes, with a ragged last
-# 48-row workgroup and a ragged last 12-row wave block
-WSTREAM_DEFAULT = [(2, 8200, 5120), (4, 10241, 1024), (3, 16500, 4608), (4, 16389, 512)]
+# qkv-like shapes (activation read from L2) and 3..4 tokens on many-row shapes
+# (activation staged in LDS), with a ragged last 48-row workgroup and a ragged
+# last 12-row wave block
+WSTREAM_DEFAULT = [(2, 8200, 5120, "wstream_m4_r3_w4_u2_ag"), (4, 10241, 1024, "wstream_m4_r3_w4_u2_ag"),
+                   (3, 16500, 4608, "wstream_m4_r3_w4_u2"), (4, 16389, 512, "wstream_m4_r3_w4_u2")]
 
 
-@pytest.mark.parametrize("M,N,K", WSTREAM_DEFAULT)
-def test_wstream_default_full_compare(M, N, K):
-    assert F.nvfp4_gemv_variant(M, N, K).startswith("wstream_m")
+@pytest.mark.parametrize("M,N,K,variant", WSTREAM_DEFAULT)
+def test_wstream_default_full_compare(M, N, K, variant):
+    assert F.nvfp4_gemv_variant(M, N, K) == variant
     w = W.small_random_weights(N * 5 + K + M, N, K)
     xb = W.small_random_bf16(M * 19 + K, M, K)
     wq, aq, y = _run(M, N, K, w, xb, F.nvfp4_gemv_variant(M, N, K))
