@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "3041804089d0a96740ee892f58c676d5596270e2b43e214494fdbd1503f664ef",
-    "bytes_per_step": 1122793558,
+    "sha256": "afd06f8ae7476f29338f427962fcc152220d0a30af2f99f61c9ec3612b3546f2",
+    "bytes_per_step": 1106075549,
 }
 
 

@@ -1893,6 +1893,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
 // (not range-checked), which only ever addresses bytes inside the rows.
 constexpr int kStreamChunk = 512;          // K elements per chunk and row
 constexpr uint32_t kOffOut = 0x80000000u;  // beyond any buffer resource used here
+// A scalar offset that moves every lane's offset (kOffOut included, without
+// wrapping) past the end of any buffer under 1 GiB: such a load reads zeros
+// and makes no memory request (a larger buffer gets an in-bounds read)
+constexpr int kPastEnd = 0x40000000;
 
 // 32 codes (one 16-byte word) times two block scales (16 elements each) ->
 // four f16 operands of 8 elements
@@ -1993,15 +1997,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
   u32x4_t ring[U][R];
   u32x4_t aring[U][S];
   uint32_t sring[U][S];
-  auto load = [&](int u, int i) {  // the wave's i-th chunk into slot u; past the last, the last again (never used)
-    const int c = wave + (i < n ? i : n - 1) * NW;
+  auto load = [&](int u, int i) {  // the wave's i-th chunk into slot u; past the last, zeros (never used)
+    const int c = wave + i * NW;
+    const int co = i < n ? c * 256 : kPastEnd, so = i < n ? c * 32 : kPastEnd;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], co, 2 /* non-temporal */);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], c * 256, 0);
-      sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], c * 32, 0);
+      aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], co, 0);
+      sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], so, 0);
     }
   };
   if (n > 0) {
@@ -2166,16 +2171,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_wstream_kernel(GemvParams p) {
   u32x4_t ring[U][R];
   u32x4_t aring[U][AG ? S : 1];
   uint32_t sring[U][AG ? S : 1];
-  auto load = [&](int u, int i) {  // chunk i into slot u; past the last, the last again (never used)
-    const int c = i < n ? i : n - 1;
+  auto load = [&](int u, int i) {  // chunk i into slot u; past the last, zeros (never used)
+    const int co = i < n ? i * 256 : kPastEnd, so = i < n ? i * 32 : kPastEnd;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], c * 256, 2 /* non-temporal */);
+      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], co, 2 /* non-temporal */);
     if constexpr (AG) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], c * 256, 0);
-        sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], c * 32, 0);
+        aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], co, 0);
+        sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], so, 0);
       }
     }
   };
