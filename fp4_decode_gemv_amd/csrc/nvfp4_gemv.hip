@@ -2948,11 +2948,12 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
     if (stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
       return i;
   }
-  // 2..4 tokens on qkv-like shapes (8192 <= N < 16384, K < 8192): the
-  // wave-owned streaming kernel with the activation read from L2; 3..4
-  // tokens on many-row shapes (N >= 16384): the same kernel with the
-  // activation staged in LDS (there it measured a little faster)
-  if (!epi && K % kStreamChunk == 0 && M >= 2 && M <= 4 && N >= 8192 && N < 16384 && K < 8192) {
+  // 2..4 tokens on qkv-like shapes (8192 <= N < 16384, K < 8192) and 2
+  // tokens on many-row shapes (N >= 16384, K < 8192): the wave-owned
+  // streaming kernel with the activation read from L2; 3..4 tokens on
+  // many-row shapes: the same kernel with the activation staged in LDS
+  // (there the two forms measured within 1%)
+  if (!epi && K % kStreamChunk == 0 && M >= 2 && M <= 4 && N >= 8192 && K < 8192 && (N < 16384 || M == 2)) {
     const int i = VARIANT("wstream_m4_r3_w4_u2_ag");
     if (pad1k(4 * kVariants[i].r * kVariants[i].nw * (K / 16)) <= kLdsBytes) return i;
   }

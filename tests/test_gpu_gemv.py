@@ -78,10 +78,11 @@ def test_gemm_split_default_full_compare(M, N, K):
 
 
 # the wave-owned streaming kernel as the launch table picks it: 2..4 tokens on
-# qkv-like shapes (activation read from L2) and 3..4 tokens on many-row shapes
-# (activation staged in LDS), with a ragged last 48-row workgroup and a ragged
-# last 12-row wave block
+# qkv-like shapes and 2 tokens on many-row shapes (activation read from L2),
+# 3..4 tokens on many-row shapes (activation staged in LDS), with a ragged
+# last 48-row workgroup and a ragged last 12-row wave block
 WSTREAM_DEFAULT = [(2, 8200, 5120, "wstream_m4_r3_w4_u2_ag"), (4, 10241, 1024, "wstream_m4_r3_w4_u2_ag"),
+                   (2, 16500, 4608, "wstream_m4_r3_w4_u2_ag"),
                    (3, 16500, 4608, "wstream_m4_r3_w4_u2"), (4, 16389, 512, "wstream_m4_r3_w4_u2")]
 
 
