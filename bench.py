@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "c588606b1b5e228f9f28b7dc05e3c9dbb3748f9d50d0ae98f090f0be3b1ae01e",
-    "bytes_per_step": 1106076416,
+    "sha256": "249a679279748d2ec14424af0cc9d28ce8e59aa511cbb296c0fb72bf9ebd497a",
+    "bytes_per_step": 1105834967,
 }
 
 

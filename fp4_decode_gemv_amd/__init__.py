@@ -392,9 +392,12 @@ def variant_tokens(name: str) -> int:
 
 def variant_k_multiple(name: str) -> int:
     """K granularity a variant needs: the streaming kernels (``stream_*``,
-    ``fstream_*``) stream whole 512-element chunks, the direct-to-LDS kernels
+    ``fstream_*``, ``wstream_*``) stream whole 512-element chunks (the
+    eight-token ``stream8_*`` 256-element ones), the direct-to-LDS kernels
     (``dma_*``, ``staged_*``, ``fmma_*``) and the tiled GEMM (``gemm_*``)
     copy whole 256-element steps, every other kernel 32-element chunks."""
+    if name.startswith("stream8_"):
+        return 256
     if name.startswith(("stream_", "fstream_", "wstream_")):
         return 512
     return 256 if name.startswith(("dma_", "staged_", "fmma_", "gemm_")) else 32

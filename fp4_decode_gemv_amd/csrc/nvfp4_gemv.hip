@@ -1892,6 +1892,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_fmma_kernel(GemvParams p) {
 // outside the buffer and read as zeros; the chunk offset is a scalar operand
 // (not range-checked), which only ever addresses bytes inside the rows.
 constexpr int kStreamChunk = 512;          // K elements per chunk and row
+constexpr int kStream8Chunk = 256;         // K elements per chunk and row of the eight-token form
 constexpr uint32_t kOffOut = 0x80000000u;  // beyond any buffer resource used here
 // A scalar offset that moves every lane's offset (kOffOut included, without
 // wrapping) past the end of any buffer under 1 GiB: such a load reads zeros
@@ -2100,6 +2101,153 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
     }
   }
   if constexpr (EPI) lmhead_partials<MT, 4 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
+}
+
+// (a2) Eight-token f16 form, M <= 8, K % 256 == 0.  The operand layout of
+// form (a) with two windows instead of four: lane (j, kg) holds row (or
+// token) j / 2 and window j % 2, the 16 bytes at byte 32 kg + 16 (j % 2) of
+// the row's 128-byte chunk, so a wave instruction reads 8 rows x 128 B (a
+// whole cache line per row).  The token side holds all 8 tokens, and
+// D[2 wr + w][2 t + w] is row wr with token t over window w: half of each
+// MFMA's results are used, against a quarter for form (a) with two sets of
+// 4 tokens, which halves the MFMA work at M = 5..8.  The activation of each
+// chunk comes from L2 into the register ring beside the weights; only the
+// tile's block scales are staged in LDS.  Tokens >= M read as zeros.
+template <int R, int NW, int U, bool EPI>
+__global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
+  constexpr int MT = 8;
+  extern __shared__ uint4 lds4[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, kg = lane >> 4;
+  const int jr = j >> 1, jw = j & 1;  // row (weight side) / token (token side), window
+  const int64_t N = p.N, K = p.K;
+  const int M = p.M;
+  const int64_t tile0 = (int64_t)blockIdx.x * p.tile_rows;
+  const int64_t rows = N - tile0 < p.tile_rows ? N - tile0 : p.tile_rows;
+  const int nchunks = (int)(K / kStream8Chunk);
+  const int n = wave < nchunks ? (nchunks - wave + NW - 1) / NW : 0;  // chunks wave, wave + NW, ...
+
+  const uint32_t l0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds4));
+  stage_to_lds<NW>(raw_rsrc(p.w_scales + tile0 * (K / 16), rows * (K / 16)), l0, rows * (K / 16), wave, lane);
+  const __amdgpu_buffer_rsrc_t wcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.w_codes + tile0 * (K / 2)), (short)0, (int)(rows * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t acr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_codes), (short)0,
+                                                                      (int)(M * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t asr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a_scales), (short)0,
+                                                                      (int)(M * (K / 16)), kBufferWord3);
+  const int b0 = 32 * kg + 16 * jw;  // byte of this lane within a row's chunk
+  uint32_t vw[R];
+  const char* lds = reinterpret_cast<const char*>(lds4);
+  const char* lsw[R];  // block scales of each row group's row (+ 16 c); rows past the tile read the last row's
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = 8 * r + jr;
+    vw[r] = row < rows ? (uint32_t)(row * (int)(K / 2) + b0) : kOffOut;
+    lsw[r] = lds + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;
+  }
+  // the token's codes (+ 128 c) and scales (+ 16 c); past M: zeros
+  const uint32_t va = jr < M ? (uint32_t)(jr * (int)(K / 2) + b0) : kOffOut;
+  const uint32_t vsa = jr < M ? (uint32_t)(jr * (int)(K / 16) + b0 / 8) : kOffOut;
+
+  float4_t acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  u32x4_t ring[U][R];
+  u32x4_t aring[U];
+  uint32_t sring[U];
+  auto load = [&](int u, int i) {  // the wave's i-th chunk into slot u; past the last, zeros (never used)
+    const int c = wave + i * NW;
+    const int co = i < n ? c * 128 : kPastEnd, so = i < n ? c * 16 : kPastEnd;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], co, 2 /* non-temporal */);
+    aring[u] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va, co, 0);
+    sring[u] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa, so, 0);
+  };
+  if (n > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  constexpr int kRingLoads = U * (R + 2);
+  wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();  // this wave's staging copies (issued first) have landed ...
+  asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
+  if (n > 0) {
+    for (int i0 = 0; i0 < n; i0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u;
+        const int c = wave + (i < n ? i : n - 1) * NW;
+        u32x4_t w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[r] = ring[u][r];
+        const u32x4_t ga = aring[u];
+        const uint32_t gs = sring[u];
+        load(u, i + U);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < n) {
+          half8_t b[4];
+          decode32_scaled(ga, gs, b);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            half8_t a[4];
+            decode32_scaled(w[r], *reinterpret_cast<const uint16_t*>(lsw[r] + 16 * c), a);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], acc[r], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // finish: lane l = 16 g + i holds, in entry e = (i % 2) + 2 h, row
+  // 8 r + 2 g + h with token i / 2 over window i % 2; output (t, row) = the
+  // sum over waves and the two windows (lanes 16 g + 2 t + w)
+  __syncthreads();  // every wave is done with the staged scales before the reduction reuses the LDS
+  float* red = reinterpret_cast<float*>(lds4);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) red[((wave * R + r) * 2 + h) * 64 + lane] = acc[r][(lane & 1) + 2 * h];
+  __syncthreads();
+  constexpr int OUTS = 8 * R * MT;
+  constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);
+  float tsc[NV];  // global scales, all loaded before the first store
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int t = ((int)threadIdx.x + u * NW * 64) / (8 * R);
+    tsc[u] = token_scale(p, t < M ? t : 0);
+  }
+  float out[NV];
+  int tok[NV], rowt[NV];
+  bool ok[NV], own[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int o = (int)threadIdx.x + u * NW * 64;
+    out[u] = 0.0f;
+    tok[u] = 0;
+    rowt[u] = 0;
+    ok[u] = own[u] = false;
+    if (o < OUTS) {
+      const int rt = o % (8 * R), t = o / (8 * R);  // consecutive threads: consecutive rows
+      const int r = rt >> 3, g = (rt & 7) >> 1, h = rt & 1;
+      float sum = 0.0f;
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int ww = 0; ww < 2; ++ww) sum += red[((w * R + r) * 2 + h) * 64 + 16 * g + 2 * t + ww];
+      out[u] = sum * tsc[u];
+      tok[u] = t;
+      rowt[u] = rt;
+      own[u] = t < M;
+      ok[u] = t < M && rt < rows;
+      if (ok[u]) p.y[(int64_t)t * N + tile0 + rt] = out[u];
+    }
+  }
+  if constexpr (EPI) lmhead_partials<MT, 8 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
 }
 
 // (c) Wave-owned rows, for many-row projections at M = 2..8 (K % 512 == 0):
@@ -2692,7 +2840,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemvParams p) {
 
 enum Kind {
   VALU = 0, DIRECT = 1, MFMA = 2, LMFMA = 3, DMA = 4, STAGED = 5, FMMA = 6, FMMASA = 7, DMASA = 8, STREAM = 9,
-  FSTREAM = 10, GEMM = 11, WSTREAM = 12, WSTREAMAG = 13
+  FSTREAM = 10, GEMM = 11, WSTREAM = 12, WSTREAMAG = 13, STREAM8 = 14
 };
 
 struct Variant {
@@ -2763,6 +2911,11 @@ struct Variant {
     "stream_m" #MT "_r" #R "_w" #NW "_u" #U, STREAM, MT, 16, R, NW, U,                       \
         gemv_stream_kernel<MT, R, NW, U, false>, gemv_stream_kernel<MT, R, NW, U, true>     \
   }
+#define STREAM8_V(R, NW, U)                                                               \
+  Variant {                                                                             \
+    "stream8_m8_r" #R "_w" #NW "_u" #U, STREAM8, 8, 16, R, NW, U,                            \
+        gemv_stream8_kernel<R, NW, U, false>, gemv_stream8_kernel<R, NW, U, true>           \
+  }
 #define FSTREAM_V(R, NW, U)                                                                 \
   Variant {                                                                               \
     "fstream_m1_r" #R "_w" #NW "_u" #U, FSTREAM, 1, 16, R, NW, U,                            \
@@ -2800,12 +2953,13 @@ const Variant kVariants[] = {
     // two tokens
     FMMA_SA_V(2, 1, 4, 3), STAGED_V(2, 64, 1, 4, 2), STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
     // 3..8 tokens
-    STREAM_V(4, 5, 4, 2), STREAM_V(8, 5, 4, 2), DMA_V(4, 2, 4, 3), DMA_SA_V(8, 2, 4, 2), DMA_V(8, 2, 4, 3),
+    STREAM_V(4, 5, 4, 2), DMA_V(4, 2, 4, 3), DMA_V(8, 2, 4, 3),
     FMMA_V(4, 2, 4, 3), LMFMA_V(8, 2, 8, 1), LMFMA_V(8, 1, 4, 1),
     // 9..128 tokens
     LMFMA_V(16, 2, 8, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(32, 2, 8, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(64, 2, 8, 1),
     LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1), GEMM_V(32), GEMM_V(64), GEMM_V(128), WSTREAM_V(4, 3, 4, 2),
-    WSTREAM_AG_V(4, 3, 4, 2),
+    WSTREAM_AG_V(4, 3, 4, 2), STREAM8_V(2, 4, 2), STREAM8_V(3, 4, 2), STREAM8_V(4, 4, 2), STREAM8_V(5, 4, 2),
+    STREAM8_V(2, 8, 2), STREAM8_V(3, 8, 2),
     // fallbacks
     DIRECT_V(2, 64, 1, 4, 1), MFMA_V(4, 2, 8, 1), MFMA_V(8, 2, 8, 1), LMFMA_V(16, 1, 4, 1), LMFMA_V(32, 1, 4, 1),
     LMFMA_V(64, 1, 4, 1), LMFMA_V(128, 1, 4, 1),
@@ -2857,6 +3011,7 @@ int64_t epi_tile_rows(const Variant& v) {
   switch (v.kind) {
     case STREAM:
     case FSTREAM: return 4 * v.r;
+    case STREAM8: return 8 * v.r;
     case WSTREAM:
     case WSTREAMAG: return 4 * v.r * v.nw;
     case VALU:
@@ -2869,7 +3024,7 @@ int64_t epi_tile_rows(const Variant& v) {
 // LDS a streaming kernel stages: the tile's block scales (the f16 form), and
 // the activation codes and scales of its one token beside them (the FP4 form)
 int64_t stream_kernel_lds(const Variant& v, int64_t K, int64_t tile_rows) {
-  if (v.kind == STREAM) return pad1k(tile_rows * (K / 16));
+  if (v.kind == STREAM || v.kind == STREAM8) return pad1k(tile_rows * (K / 16));
   return stream_lds_bytes(1, K, tile_rows);
 }
 
@@ -2914,6 +3069,39 @@ int gemm_ksplit(int M, int64_t N, int64_t K, int64_t ws_cap) {
 // the CUs where whole tiles would leave some idle (tile_rows_for).  The
 // LDS-copy kernels need K % 256 == 0; other K use the register-staged
 // kernels.
+// The eight-token streaming variant for N x K: the number R of 8-row groups
+// per workgroup tile, and 8 waves instead of 4 on long rows (K >= 8192) of
+// tiles of at most 24 rows.
+//   N >= 65536 (LM heads): R = 4.
+//   16384 <= N < 65536: the R in {5, 4, 3} whose workgroups take the fewest
+//     rows per CU when dealt out over the CUs (rounds of workgroups x R).
+//   N < 16384: the fewest groups that hold the rows a workgroup gets when
+//     40-row tiles are balanced over the CUs (tile_rows_for), 2 to 5.
+int stream8_variant(int64_t N, int64_t K) {
+  int r = 5;
+  if (N >= 65536) {
+    r = 4;
+  } else if (N >= 16384) {
+    int64_t best = -1;
+    for (int c = 5; c >= 3; --c) {
+      const int64_t wgs = (N + 8 * c - 1) / (8 * c);
+      const int64_t cost = (wgs + kComputeUnits - 1) / kComputeUnits * c;
+      if (best < 0 || cost < best) {
+        best = cost;
+        r = c;
+      }
+    }
+  } else {
+    const int64_t groups = (tile_rows_for(N, 40) + 7) / 8;
+    r = groups < 2 ? 2 : groups > 5 ? 5 : (int)groups;
+  }
+  if (N < 16384 && K >= 8192 && r <= 3) return r == 2 ? VARIANT("stream8_m8_r2_w8_u2") : VARIANT("stream8_m8_r3_w8_u2");
+  return r == 2 ? VARIANT("stream8_m8_r2_w4_u2")
+         : r == 3 ? VARIANT("stream8_m8_r3_w4_u2")
+         : r == 4 ? VARIANT("stream8_m8_r4_w4_u2")
+                  : VARIANT("stream8_m8_r5_w4_u2");
+}
+
 int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   const bool k256 = K % 256 == 0;
   // the FP4 MFMA kernel with the activation in LDS, when that fits
@@ -2940,10 +3128,18 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   if (M > 32) return K >= 16384 ? VARIANT("lmfma_m64_r2_w8_p1") : VARIANT("lmfma_m64_r2_w4_p1");
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
-  // 2..8 tokens on long rows of few output rows (o_proj, down_proj): the
+  // 5..8 tokens: the eight-token streaming kernel, when its staged block
+  // scales fit
+  if (M >= 5 && K % kStream8Chunk == 0) {
+    const int i = stream8_variant(N, K);
+    const Variant& v = kVariants[i];
+    if (stream_kernel_lds(v, K, tile_rows_for(N, 8 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
+      return i;
+  }
+  // 2..4 tokens on long rows of few output rows (o_proj, down_proj): the
   // streaming MFMA kernel, when its staged block scales fit
-  if (M >= 2 && N < 16384 && K >= 8192 && K % kStreamChunk == 0) {
-    const int i = M <= 4 ? VARIANT("stream_m4_r5_w4_u2") : VARIANT("stream_m8_r5_w4_u2");
+  if (M >= 2 && M <= 4 && N < 16384 && K >= 8192 && K % kStreamChunk == 0) {
+    const int i = VARIANT("stream_m4_r5_w4_u2");
     const Variant& v = kVariants[i];
     if (stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
       return i;
@@ -2973,13 +3169,9 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
     return K >= 12288 ? fmma_sa(VARIANT("fmma_m2_r1_w4_d3_sa"), VARIANT("staged_m2_g64_r1_w4_p2"))
            : K >= 8192 && N < 16384 ? VARIANT("staged_m2_g64_r1_w4_p1")
                                     : VARIANT("staged_m2_g32_r2_w4_p1");
-  // N >= 16384: the plain ring at M = 3..4; at M = 5..8 the staged-activation
-  // form when two workgroups still fit a CU's LDS (with one per CU it is
-  // slower than the plain ring)
-  if (k256 && N >= 16384)
-    return M <= 4 ? VARIANT("dma_m4_r2_w4_d3")
-           : sa_lds_bytes(kVariants[VARIANT("dma_m8_r2_w4_d2_sa")], K) <= 81920 ? VARIANT("dma_m8_r2_w4_d2_sa")
-                                                                                 : VARIANT("dma_m8_r2_w4_d3");
+  // N >= 16384: the direct-to-LDS ring (at M = 5..8 only where the
+  // eight-token streaming kernel's block scales do not fit)
+  if (k256 && N >= 16384) return M <= 4 ? VARIANT("dma_m4_r2_w4_d3") : VARIANT("dma_m8_r2_w4_d3");
   if (M <= 4 && k256 && K >= 12288) return VARIANT("fmma_m4_r2_w4_d3");
   if (K >= 8192) return VARIANT("lmfma_m8_r2_w8_p1");
   return VARIANT("lmfma_m8_r1_w4_p1");
@@ -3009,6 +3201,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
     const Kind kd = v.kind;
     if ((kd == DMA || kd == DMASA || kd == STAGED || kd == FMMA || kd == FMMASA) && K % 256 != 0) return false;
     if ((kd == STREAM || kd == FSTREAM) && K % kStreamChunk != 0) return false;
+    if (kd == STREAM8 && K % kStream8Chunk != 0) return false;
     if (kd == GEMM && (K % kGemmStageK != 0 || epi)) return false;
     if (kd == WSTREAM && (K % kStreamChunk != 0 || epi ||
                           stream_lds_bytes(v.mt, K, 4 * v.r * v.nw) > kLdsBytes))
@@ -3021,8 +3214,9 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
     if ((kd == FMMASA || kd == DMASA) && sa_lds_bytes(v, K) + slot > kLdsBytes) return false;
     if ((kd == STREAM || kd == FSTREAM) && stream_kernel_lds(v, K, tile_rows_for(N, 4 * v.r)) + slot > kLdsBytes)
       return false;
+    if (kd == STREAM8 && stream_kernel_lds(v, K, tile_rows_for(N, 8 * v.r)) + slot > kLdsBytes) return false;
     if (kd == STAGED && staged_lds_bytes(v, K) > 65536) return false;
-    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != FSTREAM &&
+    return (kd != LMFMA && kd != DMA && kd != DMASA && kd != FMMA && kd != FMMASA && kd != STREAM && kd != STREAM8 && kd != FSTREAM &&
             kd != GEMM && kd != WSTREAM && kd != WSTREAMAG) ||
            (int64_t)16 * v.r * (K / 2) < (1ll << 31);
   };
@@ -3063,9 +3257,10 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     c.lds_bytes = v.kind == WSTREAM ? stream_lds_bytes(v.mt, K, c.rows_per_wg) : pad1k(c.rows_per_wg * (K / 16));
   } else if (v.kind == MFMA || v.kind == LMFMA || v.kind == DMA || v.kind == DMASA || v.kind == FMMA || v.kind == FMMASA ||
-      v.kind == STREAM || v.kind == FSTREAM) {
+      v.kind == STREAM || v.kind == STREAM8 || v.kind == FSTREAM) {
     c.kp = (int)K;
-    const int64_t tile = (int64_t)(v.kind == STREAM || v.kind == FSTREAM ? 4 : 16) * v.r;  // rows of the kernel's tile
+    const int64_t tile =
+        (int64_t)(v.kind == STREAM || v.kind == FSTREAM ? 4 : v.kind == STREAM8 ? 8 : 16) * v.r;  // rows of the kernel's tile
     c.rows_per_wg = v.kind == MFMA ? tile : tile_rows_for(N, tile);
     c.grid = (N + c.rows_per_wg - 1) / c.rows_per_wg;
     const int ct = v.mt > 16 ? v.mt / 16 : 1;              // 16-token column tiles
@@ -3078,7 +3273,7 @@ GemvConfig choose_gemv_config(int M, int64_t N, int64_t K, bool epi, int64_t ws_
       const int64_t b = sa_lds_bytes(v, K);
       if (b > c.lds_bytes) c.lds_bytes = b;
     }
-    if (v.kind == FSTREAM || v.kind == STREAM) {
+    if (v.kind == FSTREAM || v.kind == STREAM || v.kind == STREAM8) {
       const int64_t b = stream_kernel_lds(v, K, c.rows_per_wg);
       if (b > c.lds_bytes) c.lds_bytes = b;
     }

@@ -245,9 +245,10 @@ ROW_MAP_CASES = [("lmfma_m8_r2_w8_p1", 8, 4099, 2048), ("lmfma_m8_r1_w4_p1", 5, 
                  ("lmfma_m32_r2_w8_p1", 32, 5117, 2048), ("lmfma_m32_r1_w4_p1", 20, 4099, 1312),
                  ("lmfma_m64_r2_w8_p1", 64, 5117, 2048), ("lmfma_m64_r2_w4_p1", 40, 4099, 1312),
                  ("lmfma_m128_r1_w4_p1", 128, 5117, 1024), ("lmfma_m128_r2_w4_p1", 90, 4099, 1312),
-                 ("dma_m8_r2_w4_d3", 8, 5117, 1024), ("dma_m8_r2_w4_d2_sa", 7, 4099, 2048),
+                 ("dma_m8_r2_w4_d3", 8, 5117, 1024), ("stream8_m8_r5_w4_u2", 7, 4099, 2048),
+                 ("stream8_m8_r3_w8_u2", 6, 5117, 2048), ("stream8_m8_r2_w4_u2", 5, 4099, 1280),
                  ("fmma_m4_r2_w4_d3", 4, 5117, 1024), ("fmma_m2_r1_w4_d3_sa", 2, 4099, 1024),
-                 ("stream_m8_r5_w4_u2", 8, 5117, 1024), ("stream_m4_r5_w4_u2", 3, 4099, 2048)]
+                 ("stream8_m8_r3_w4_u2", 8, 5117, 1024), ("stream_m4_r5_w4_u2", 3, 4099, 2048)]
 
 
 @pytest.mark.parametrize("balance", ["0", "1"])
