@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "249a679279748d2ec14424af0cc9d28ce8e59aa511cbb296c0fb72bf9ebd497a",
-    "bytes_per_step": 1105834967,
+    "sha256": "c055f47cf062dae93cacb628eee325b37f3921a2da3cca91cba1e4a4e57fa62b",
+    "bytes_per_step": 1105979368,
 }
 
 

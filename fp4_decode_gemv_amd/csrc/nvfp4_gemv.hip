@@ -3073,8 +3073,8 @@ int gemm_ksplit(int M, int64_t N, int64_t K, int64_t ws_cap) {
 // per workgroup tile, and 8 waves instead of 4 on long rows (K >= 8192) of
 // tiles of at most 24 rows.
 //   N >= 65536 (LM heads): R = 4.
-//   16384 <= N < 65536: the R in {5, 4, 3} whose workgroups take the fewest
-//     rows per CU when dealt out over the CUs (rounds of workgroups x R).
+//   16384 <= N < 65536: the smallest R in {3, 4, 5} whose workgroups take
+//     the fewest rows per CU when dealt out over the CUs (rounds x R).
 //   N < 16384: the fewest groups that hold the rows a workgroup gets when
 //     40-row tiles are balanced over the CUs (tile_rows_for), 2 to 5.
 int stream8_variant(int64_t N, int64_t K) {
@@ -3083,7 +3083,7 @@ int stream8_variant(int64_t N, int64_t K) {
     r = 4;
   } else if (N >= 16384) {
     int64_t best = -1;
-    for (int c = 5; c >= 3; --c) {
+    for (int c = 3; c <= 5; ++c) {
       const int64_t wgs = (N + 8 * c - 1) / (8 * c);
       const int64_t cost = (wgs + kComputeUnits - 1) / kComputeUnits * c;
       if (best < 0 || cost < best) {
@@ -3128,16 +3128,22 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   if (M > 32) return K >= 16384 ? VARIANT("lmfma_m64_r2_w8_p1") : VARIANT("lmfma_m64_r2_w4_p1");
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
-  // 5..8 tokens: the eight-token streaming kernel, when its staged block
-  // scales fit
-  if (M >= 5 && K % kStream8Chunk == 0) {
+  // The eight-token streaming kernel, when its staged block scales fit: at
+  // 5..8 tokens on every shape, at 2..4 tokens except where another kernel
+  // measured as fast or faster (o-like rows, 8192 <= K < 16384, on
+  // N < 16384: the four-window form; LM-head-sized N >= 65536 without the
+  // epilogue: the wave-owned form), and at 1 token on small shapes (N and
+  // K < 8192; elsewhere the VALU kernels are faster)
+  const bool oLike = N < 16384 && K >= 8192 && K < 16384;
+  if (K % kStream8Chunk == 0 &&
+      (M >= 5 || (M >= 2 && !oLike && !(N >= 65536 && !epi)) || (M == 1 && N < 8192 && K < 8192))) {
     const int i = stream8_variant(N, K);
     const Variant& v = kVariants[i];
     if (stream_kernel_lds(v, K, tile_rows_for(N, 8 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
       return i;
   }
-  // 2..4 tokens on long rows of few output rows (o_proj, down_proj): the
-  // streaming MFMA kernel, when its staged block scales fit
+  // 2..4 tokens on long rows of few output rows (o_proj; down_proj where
+  // the eight-token kernel does not fit): the four-window streaming kernel
   if (M >= 2 && M <= 4 && N < 16384 && K >= 8192 && K % kStreamChunk == 0) {
     const int i = VARIANT("stream_m4_r5_w4_u2");
     const Variant& v = kVariants[i];
@@ -3145,10 +3151,11 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
       return i;
   }
   // 2..4 tokens on qkv-like shapes (8192 <= N < 16384, K < 8192) and 2
-  // tokens on many-row shapes (N >= 16384, K < 8192): the wave-owned
-  // streaming kernel with the activation read from L2; 3..4 tokens on
-  // many-row shapes: the same kernel with the activation staged in LDS
-  // (there the two forms measured within 1%)
+  // tokens on many-row shapes (N >= 16384, K < 8192), where the eight-token
+  // kernel is not taken: the wave-owned streaming kernel with the
+  // activation read from L2; 3..4 tokens on many-row shapes: the same
+  // kernel with the activation staged in LDS (the two forms measured within
+  // 1% there)
   if (!epi && K % kStreamChunk == 0 && M >= 2 && M <= 4 && N >= 8192 && K < 8192 && (N < 16384 || M == 2)) {
     const int i = VARIANT("wstream_m4_r3_w4_u2_ag");
     if (pad1k(4 * kVariants[i].r * kVariants[i].nw * (K / 16)) <= kLdsBytes) return i;

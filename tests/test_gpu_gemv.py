@@ -77,13 +77,12 @@ def test_gemm_split_default_full_compare(M, N, K):
     assert_gemv_close(y, y_ref, ref_abs, what=f"split gemm M={M} N={N} K={K}")
 
 
-# the wave-owned streaming kernel as the launch table picks it: 2..4 tokens on
-# qkv-like shapes and 2 tokens on many-row shapes (activation read from L2),
-# 3..4 tokens on many-row shapes (activation staged in LDS), with a ragged
-# last 48-row workgroup and a ragged last 12-row wave block
-WSTREAM_DEFAULT = [(2, 8200, 5120, "wstream_m4_r3_w4_u2_ag"), (4, 10241, 1024, "wstream_m4_r3_w4_u2_ag"),
-                   (2, 16500, 4608, "wstream_m4_r3_w4_u2_ag"),
-                   (3, 16500, 4608, "wstream_m4_r3_w4_u2"), (4, 16389, 512, "wstream_m4_r3_w4_u2")]
+# the wave-owned streaming kernel as the launch table picks it (LM-head-sized
+# N >= 65536 without the epilogue): 2 tokens with the activation read from
+# L2, 3..4 tokens with it staged in LDS, with a ragged last 48-row workgroup
+# and a ragged last 12-row wave block
+WSTREAM_DEFAULT = [(2, 65600, 1024, "wstream_m4_r3_w4_u2_ag"), (3, 65601, 512, "wstream_m4_r3_w4_u2"),
+                   (4, 65557, 1024, "wstream_m4_r3_w4_u2")]
 
 
 @pytest.mark.parametrize("M,N,K,variant", WSTREAM_DEFAULT)
