@@ -214,6 +214,33 @@ def test_launch_table_names_real_variants(L):
                 assert K % F.variant_k_multiple(v) == 0, (M, N, K, v)
 
 
+# The launch table's measured choices on the workloads' shapes (host logic
+# only).  The eight-token kernel's row groups R follow the rule written in
+# default_variant: 40-row tiles balanced over 256 CUs below N = 16384 (qkv:
+# 40 rows -> R = 5; o, down: 20 rows -> R = 3 with 8 waves on K >= 8192;
+# 4096 rows: 16 -> R = 2), the fewest rows per CU at 16384 <= N < 65536
+# (gate_up 51200: R = 5 in 5 rounds; Qwen3-8B gate_up 24576: R = 3 and 4 tie
+# at 12, the smaller wins), R = 4 for LM heads.
+LAUNCH_CHOICES = [
+    (8, 10240, 5120, False, "stream8_m8_r5_w4_u2"), (8, 5120, 8192, False, "stream8_m8_r3_w8_u2"),
+    (8, 51200, 5120, False, "stream8_m8_r5_w4_u2"), (8, 5120, 25600, False, "stream8_m8_r3_w8_u2"),
+    (8, 24576, 4096, False, "stream8_m8_r3_w4_u2"), (8, 4096, 4096, False, "stream8_m8_r2_w4_u2"),
+    (8, 4096, 12288, False, "stream8_m8_r2_w8_u2"), (8, 151936, 5120, True, "stream8_m8_r4_w4_u2"),
+    (5, 151936, 5120, False, "stream8_m8_r4_w4_u2"), (2, 51200, 5120, False, "stream8_m8_r5_w4_u2"),
+    (4, 5120, 8192, False, "stream_m4_r5_w4_u2"), (2, 5120, 25600, False, "stream8_m8_r3_w8_u2"),
+    (2, 151936, 5120, False, "wstream_m4_r3_w4_u2_ag"), (4, 151936, 5120, False, "wstream_m4_r3_w4_u2"),
+    (1, 4096, 4096, False, "stream8_m8_r2_w4_u2"), (1, 10240, 5120, False, "direct_m1_g32_r1_w4_p1_nt"),
+    (1, 51200, 5120, False, "staged_m1_g32_r1_w4_p2"), (1, 151936, 5120, True, "staged_m1_g32_r1_w4_p2"),
+    (8, 1024, 4128, False, "lmfma_m8_r1_w4_p1"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,lm,variant", LAUNCH_CHOICES)
+def test_launch_choices_on_the_workload_shapes(L, M, N, K, lm, variant):
+    F.nvfp4_gemv_tune(None, True)
+    assert F.nvfp4_gemv_variant(M, N, K, lm) == variant
+
+
 def test_forced_variant_falls_back_when_k_does_not_fit(L):
     """A direct-to-LDS variant forced on a K that is not a multiple of 256
     is not launched; the default for that shape is used instead."""
