@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "c055f47cf062dae93cacb628eee325b37f3921a2da3cca91cba1e4a4e57fa62b",
-    "bytes_per_step": 1105979368,
+    "sha256": "e918ffb2d1976ed437334b08db38bafe7b32f09028b02bc0ee4b6b4c20aeb9fc",
+    "bytes_per_step": 1105839654,
 }
 
 

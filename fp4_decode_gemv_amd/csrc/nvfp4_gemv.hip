@@ -2112,10 +2112,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
 // MFMA's results are used, against a quarter for form (a) with two sets of
 // 4 tokens, which halves the MFMA work at M = 5..8.  The activation of each
 // chunk comes from L2 into the register ring beside the weights; only the
-// tile's block scales are staged in LDS.  Tokens >= M read as zeros.
-template <int R, int NW, int U, bool EPI>
+// tile's block scales are staged in LDS.  Tokens >= M read as zeros.  With
+// S sets of 8 tokens (MT = 8 S) each decoded weight operand meets S token
+// operands.
+template <int R, int NW, int U, bool EPI, int S = 1>
 __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
-  constexpr int MT = 8;
+  constexpr int MT = 8 * S;
   extern __shared__ uint4 lds4[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2146,25 +2148,35 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
     vw[r] = row < rows ? (uint32_t)(row * (int)(K / 2) + b0) : kOffOut;
     lsw[r] = lds + (row < rows ? row : (int)rows - 1) * (K / 16) + b0 / 8;
   }
-  // the token's codes (+ 128 c) and scales (+ 16 c); past M: zeros
-  const uint32_t va = jr < M ? (uint32_t)(jr * (int)(K / 2) + b0) : kOffOut;
-  const uint32_t vsa = jr < M ? (uint32_t)(jr * (int)(K / 16) + b0 / 8) : kOffOut;
-
-  float4_t acc[R];
+  // token 8 s + j / 2's codes (+ 128 c) and scales (+ 16 c); past M: zeros
+  uint32_t va[S], vsa[S];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < S; ++s) {
+    const int t = 8 * s + jr;
+    va[s] = t < M ? (uint32_t)(t * (int)(K / 2) + b0) : kOffOut;
+    vsa[s] = t < M ? (uint32_t)(t * (int)(K / 16) + b0 / 8) : kOffOut;
+  }
+
+  float4_t acc[R][S];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc[r][s] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   u32x4_t ring[U][R];
-  u32x4_t aring[U];
-  uint32_t sring[U];
+  u32x4_t aring[U][S];
+  uint32_t sring[U][S];
   auto load = [&](int u, int i) {  // the wave's i-th chunk into slot u; past the last, zeros (never used)
     const int c = wave + i * NW;
     const int co = i < n ? c * 128 : kPastEnd, so = i < n ? c * 16 : kPastEnd;
 #pragma unroll
     for (int r = 0; r < R; ++r)
       ring[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wcr, (int)vw[r], co, 2 /* non-temporal */);
-    aring[u] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va, co, 0);
-    sring[u] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa, so, 0);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      aring[u][s] = __builtin_amdgcn_raw_buffer_load_b128(acr, (int)va[s], co, 0);
+      sring[u][s] = __builtin_amdgcn_raw_buffer_load_b16(asr, (int)vsa[s], so, 0);
+    }
   };
   if (n > 0) {
 #pragma unroll
@@ -2173,7 +2185,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  constexpr int kRingLoads = U * (R + 2);
+  constexpr int kRingLoads = U * (R + 2 * S);
   wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();  // this wave's staging copies (issued first) have landed ...
   asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
   if (n > 0) {
@@ -2185,34 +2197,46 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
         u32x4_t w[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) w[r] = ring[u][r];
-        const u32x4_t ga = aring[u];
-        const uint32_t gs = sring[u];
+        u32x4_t ga[S];
+        uint32_t gs[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          ga[s] = aring[u][s];
+          gs[s] = sring[u][s];
+        }
         load(u, i + U);
         __builtin_amdgcn_sched_barrier(0);
         if (i < n) {
-          half8_t b[4];
-          decode32_scaled(ga, gs, b);
+          half8_t b[S][4];
+#pragma unroll
+          for (int s = 0; s < S; ++s) decode32_scaled(ga[s], gs[s], b[s]);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             half8_t a[4];
             decode32_scaled(w[r], *reinterpret_cast<const uint16_t*>(lsw[r] + 16 * c), a);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[q], acc[r], 0, 0, 0);
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int s = 0; s < S; ++s)
+                acc[r][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b[s][q], acc[r][s], 0, 0, 0);
           }
         }
       }
     }
   }
 
-  // finish: lane l = 16 g + i holds, in entry e = (i % 2) + 2 h, row
-  // 8 r + 2 g + h with token i / 2 over window i % 2; output (t, row) = the
-  // sum over waves and the two windows (lanes 16 g + 2 t + w)
+  // finish: lane l = 16 g + i holds, in entry e = (i % 2) + 2 h of set s,
+  // row 8 r + 2 g + h with token 8 s + i / 2 over window i % 2; output
+  // (t, row) = the sum over waves and the two windows (lanes 16 g + 2 t + w)
   __syncthreads();  // every wave is done with the staged scales before the reduction reuses the LDS
   float* red = reinterpret_cast<float*>(lds4);
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) red[((wave * R + r) * 2 + h) * 64 + lane] = acc[r][(lane & 1) + 2 * h];
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        red[(((wave * R + r) * S + s) * 2 + h) * 64 + lane] = acc[r][s][(lane & 1) + 2 * h];
   __syncthreads();
   constexpr int OUTS = 8 * R * MT;
   constexpr int NV = (OUTS + NW * 64 - 1) / (NW * 64);
@@ -2234,11 +2258,11 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
     ok[u] = own[u] = false;
     if (o < OUTS) {
       const int rt = o % (8 * R), t = o / (8 * R);  // consecutive threads: consecutive rows
-      const int r = rt >> 3, g = (rt & 7) >> 1, h = rt & 1;
+      const int r = rt >> 3, g = (rt & 7) >> 1, h = rt & 1, s = t >> 3, tt = t & 7;
       float sum = 0.0f;
       for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int ww = 0; ww < 2; ++ww) sum += red[((w * R + r) * 2 + h) * 64 + 16 * g + 2 * t + ww];
+        for (int ww = 0; ww < 2; ++ww) sum += red[(((w * R + r) * S + s) * 2 + h) * 64 + 16 * g + 2 * tt + ww];
       out[u] = sum * tsc[u];
       tok[u] = t;
       rowt[u] = rt;
@@ -2916,6 +2940,11 @@ struct Variant {
     "stream8_m8_r" #R "_w" #NW "_u" #U, STREAM8, 8, 16, R, NW, U,                            \
         gemv_stream8_kernel<R, NW, U, false>, gemv_stream8_kernel<R, NW, U, true>           \
   }
+#define STREAM16_V(R, NW, U)                                                                 \
+  Variant {                                                                                \
+    "stream8_m16_r" #R "_w" #NW "_u" #U, STREAM8, 16, 16, R, NW, U,                             \
+        gemv_stream8_kernel<R, NW, U, false, 2>, gemv_stream8_kernel<R, NW, U, true, 2>        \
+  }
 #define FSTREAM_V(R, NW, U)                                                                 \
   Variant {                                                                               \
     "fstream_m1_r" #R "_w" #NW "_u" #U, FSTREAM, 1, 16, R, NW, U,                            \
@@ -2959,7 +2988,7 @@ const Variant kVariants[] = {
     LMFMA_V(16, 2, 8, 1), LMFMA_V(16, 2, 4, 1), LMFMA_V(32, 2, 8, 1), LMFMA_V(32, 2, 4, 1), LMFMA_V(64, 2, 8, 1),
     LMFMA_V(64, 2, 4, 1), LMFMA_V(128, 2, 4, 1), GEMM_V(32), GEMM_V(64), GEMM_V(128), WSTREAM_V(4, 3, 4, 2),
     WSTREAM_AG_V(4, 3, 4, 2), STREAM8_V(2, 4, 2), STREAM8_V(3, 4, 2), STREAM8_V(4, 4, 2), STREAM8_V(5, 4, 2),
-    STREAM8_V(2, 8, 2), STREAM8_V(3, 8, 2),
+    STREAM8_V(2, 8, 2), STREAM8_V(3, 8, 2), STREAM16_V(4, 4, 2), STREAM16_V(5, 4, 2),
     // fallbacks
     DIRECT_V(2, 64, 1, 4, 1), MFMA_V(4, 2, 8, 1), MFMA_V(8, 2, 8, 1), LMFMA_V(16, 1, 4, 1), LMFMA_V(32, 1, 4, 1),
     LMFMA_V(64, 1, 4, 1), LMFMA_V(128, 1, 4, 1),
@@ -3069,15 +3098,14 @@ int gemm_ksplit(int M, int64_t N, int64_t K, int64_t ws_cap) {
 // the CUs where whole tiles would leave some idle (tile_rows_for).  The
 // LDS-copy kernels need K % 256 == 0; other K use the register-staged
 // kernels.
-// The eight-token streaming variant for N x K: the number R of 8-row groups
-// per workgroup tile, and 8 waves instead of 4 on long rows (K >= 8192) of
-// tiles of at most 24 rows.
+// The number R of 8-row groups per workgroup tile of the eight-token
+// streaming kernel for N rows:
 //   N >= 65536 (LM heads): R = 4.
 //   16384 <= N < 65536: the smallest R in {3, 4, 5} whose workgroups take
 //     the fewest rows per CU when dealt out over the CUs (rounds x R).
 //   N < 16384: the fewest groups that hold the rows a workgroup gets when
 //     40-row tiles are balanced over the CUs (tile_rows_for), 2 to 5.
-int stream8_variant(int64_t N, int64_t K) {
+int stream8_groups(int64_t N) {
   int r = 5;
   if (N >= 65536) {
     r = 4;
@@ -3095,6 +3123,13 @@ int stream8_variant(int64_t N, int64_t K) {
     const int64_t groups = (tile_rows_for(N, 40) + 7) / 8;
     r = groups < 2 ? 2 : groups > 5 ? 5 : (int)groups;
   }
+  return r;
+}
+
+// The eight-token streaming variant for N x K: R from stream8_groups, and 8
+// waves instead of 4 on long rows (K >= 8192) of tiles of at most 24 rows.
+int stream8_variant(int64_t N, int64_t K) {
+  const int r = stream8_groups(N);
   if (N < 16384 && K >= 8192 && r <= 3) return r == 2 ? VARIANT("stream8_m8_r2_w8_u2") : VARIANT("stream8_m8_r3_w8_u2");
   return r == 2 ? VARIANT("stream8_m8_r2_w4_u2")
          : r == 3 ? VARIANT("stream8_m8_r3_w4_u2")
@@ -3127,6 +3162,16 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   if (M > 64) return VARIANT("lmfma_m128_r2_w4_p1");
   if (M > 32) return K >= 16384 ? VARIANT("lmfma_m64_r2_w8_p1") : VARIANT("lmfma_m64_r2_w4_p1");
   if (M > 16) return K >= 8192 ? VARIANT("lmfma_m32_r2_w8_p1") : VARIANT("lmfma_m32_r2_w4_p1");
+  // 9..16 tokens: the streaming kernel with two sets of 8 tokens where its
+  // row groups come out at R >= 4 (qkv-like and many-row shapes: 7-13%
+  // faster there; with fewer rows per workgroup the register-staged kernel
+  // is as fast or faster)
+  if (M > 8 && K % kStream8Chunk == 0 && stream8_groups(N) >= 4) {
+    const int i = stream8_groups(N) == 4 ? VARIANT("stream8_m16_r4_w4_u2") : VARIANT("stream8_m16_r5_w4_u2");
+    const Variant& v = kVariants[i];
+    if (stream_kernel_lds(v, K, tile_rows_for(N, 8 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
+      return i;
+  }
   if (M > 8) return K >= 8192 ? VARIANT("lmfma_m16_r2_w8_p1") : VARIANT("lmfma_m16_r2_w4_p1");
   // The eight-token streaming kernel, when its staged block scales fit: at
   // 5..8 tokens on every shape, at 2..4 tokens except where another kernel

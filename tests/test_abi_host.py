@@ -220,7 +220,8 @@ def test_launch_table_names_real_variants(L):
 # 40 rows -> R = 5; o, down: 20 rows -> R = 3 with 8 waves on K >= 8192;
 # 4096 rows: 16 -> R = 2), the fewest rows per CU at 16384 <= N < 65536
 # (gate_up 51200: R = 5 in 5 rounds; Qwen3-8B gate_up 24576: R = 3 and 4 tie
-# at 12, the smaller wins), R = 4 for LM heads.
+# at 12, the smaller wins), R = 4 for LM heads.  At 9..16 tokens the
+# two-set form is taken only where R comes out at 4 or 5.
 LAUNCH_CHOICES = [
     (8, 10240, 5120, False, "stream8_m8_r5_w4_u2"), (8, 5120, 8192, False, "stream8_m8_r3_w8_u2"),
     (8, 51200, 5120, False, "stream8_m8_r5_w4_u2"), (8, 5120, 25600, False, "stream8_m8_r3_w8_u2"),
@@ -232,6 +233,9 @@ LAUNCH_CHOICES = [
     (1, 4096, 4096, False, "stream8_m8_r2_w4_u2"), (1, 10240, 5120, False, "direct_m1_g32_r1_w4_p1_nt"),
     (1, 51200, 5120, False, "staged_m1_g32_r1_w4_p2"), (1, 151936, 5120, True, "staged_m1_g32_r1_w4_p2"),
     (8, 1024, 4128, False, "lmfma_m8_r1_w4_p1"),
+    (16, 10240, 5120, False, "stream8_m16_r5_w4_u2"), (12, 51200, 5120, False, "stream8_m16_r5_w4_u2"),
+    (16, 151936, 5120, True, "stream8_m16_r4_w4_u2"), (16, 5120, 8192, False, "lmfma_m16_r2_w8_p1"),
+    (16, 24576, 4096, False, "lmfma_m16_r2_w4_p1"), (9, 4096, 4096, False, "lmfma_m16_r2_w4_p1"),
 ]
 
 

@@ -247,7 +247,8 @@ ROW_MAP_CASES = [("lmfma_m8_r2_w8_p1", 8, 4099, 2048), ("lmfma_m8_r1_w4_p1", 5, 
                  ("dma_m8_r2_w4_d3", 8, 5117, 1024), ("stream8_m8_r5_w4_u2", 7, 4099, 2048),
                  ("stream8_m8_r3_w8_u2", 6, 5117, 2048), ("stream8_m8_r2_w4_u2", 5, 4099, 1280),
                  ("fmma_m4_r2_w4_d3", 4, 5117, 1024), ("fmma_m2_r1_w4_d3_sa", 2, 4099, 1024),
-                 ("stream8_m8_r3_w4_u2", 8, 5117, 1024), ("stream_m4_r5_w4_u2", 3, 4099, 2048)]
+                 ("stream8_m8_r3_w4_u2", 8, 5117, 1024), ("stream_m4_r5_w4_u2", 3, 4099, 2048),
+                 ("stream8_m16_r5_w4_u2", 16, 4099, 2048), ("stream8_m16_r4_w4_u2", 11, 5117, 1024)]
 
 
 @pytest.mark.parametrize("balance", ["0", "1"])
