@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "e918ffb2d1976ed437334b08db38bafe7b32f09028b02bc0ee4b6b4c20aeb9fc",
-    "bytes_per_step": 1105839654,
+    "sha256": "50924a1910cfec2a5d9934cc1a299b96351b0749efa788c9bf230d7e46403c88",
+    "bytes_per_step": 1105839211,
 }
 
 

@@ -2103,7 +2103,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
   if constexpr (EPI) lmhead_partials<MT, 4 * R, NV>(p, out, tok, rowt, own, ok, blockIdx.x);
 }
 
-// (a2) Eight-token f16 form, M <= 8, K % 256 == 0.  The operand layout of
+// (a2) Eight-token f16 form, M <= 8 S, K % 256 == 0.  The operand layout of
 // form (a) with two windows instead of four: lane (j, kg) holds row (or
 // token) j / 2 and window j % 2, the 16 bytes at byte 32 kg + 16 (j % 2) of
 // the row's 128-byte chunk, so a wave instruction reads 8 rows x 128 B (a
@@ -2113,8 +2113,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
 // 4 tokens, which halves the MFMA work at M = 5..8.  The activation of each
 // chunk comes from L2 into the register ring beside the weights; only the
 // tile's block scales are staged in LDS.  Tokens >= M read as zeros.  With
-// S sets of 8 tokens (MT = 8 S) each decoded weight operand meets S token
-// operands.
+// S sets of 8 tokens (MT = 8 S, S = 1 or 2) each decoded weight operand
+// meets S token operands.
 template <int R, int NW, int U, bool EPI, int S = 1>
 __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
   constexpr int MT = 8 * S;
