@@ -319,6 +319,71 @@ __device__ __forceinline__ void wave_merge(float& m, float& S, float& T) {
   T = gT;
 }
 
+// The end of the LM-head epilogue for token m, run by one wave whose lanes
+// hold partials (max, S, T) of disjoint parts of the row (empty partials
+// where a lane has none): every lane loads the sequence state and a part of
+// the ring of the last entropies in the same round trip (the state block
+// holds p.epi.window of them), the lanes' partials are merged in a fixed
+// order, and lane 0 computes H = log S - T/S and runs the ReSET update.
+// sring: LDS for kResetMaxWindow floats.
+__device__ __forceinline__ void lmhead_reset_tail(const GemvParams& p, int m, float gm, float Sm, float Tm, int lane,
+                                                  float* sring) {
+  ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
+  const float* ring = reinterpret_cast<const float*>(st + 1);
+  const int64_t count0 = st->count;
+  const int32_t st_window = st->window, len0 = st->step_len;
+  const double sum_all0 = st->sum_all, step_sum0 = st->step_sum;
+  const bool new_step = p.epi.step_start[m] != 0;
+  const int wcap = p.epi.window < kResetMaxWindow ? p.epi.window : kResetMaxWindow;
+  float rv[kResetMaxWindow / 64];
+#pragma unroll
+  for (int k = 0; k < kResetMaxWindow / 64; ++k) {
+    const int i = lane + 64 * k;
+    rv[k] = i < wcap ? ring[i] : 0.0f;
+  }
+  wave_merge(gm, Sm, Tm);
+  const double Sd = Sm, Td = Tm;
+  const float H = (float)(log(Sd) - Td / Sd);
+  // ---- ReSET update: update with H first, then decide ----
+  // the ring holds the window the state was initialised with; never index
+  // past the smaller of that and the caller's window
+  int w = st_window < p.epi.window ? st_window : p.epi.window;
+  if (w < 1) w = 1;
+  const int slot = (int)(count0 % w);
+#pragma unroll
+  for (int k = 0; k < kResetMaxWindow / 64; ++k) {
+    const int i = lane + 64 * k;
+    if (i < wcap) sring[i] = i == slot ? H : rv[k];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the wave's LDS writes before its reads
+  if (lane != 0) return;
+  const double h = (double)H;
+  const bool reset = count0 == 0 || new_step;
+  const int64_t count = count0 + 1;
+  const double sum_all = sum_all0 + h;
+  const double step_sum = (reset ? 0.0 : step_sum0) + h;
+  const int32_t step_len = (reset ? 0 : len0) + 1;
+  const int64_t nwin = count < w ? count : w;
+  double wsum = 0.0;
+  for (int64_t i = count - nwin; i < count; ++i) wsum += (double)sring[i % w];
+  const double hbar = sum_all / (double)count;
+  const double hstep = step_len <= w ? wsum / (double)nwin : step_sum / (double)step_len;
+  const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
+  float T_t;
+  if (p.epi.mode == 1) T_t = p.epi.t_base;                                   // BASE
+  else if (p.epi.mode == 2) T_t = h < (double)p.epi.tau0 ? p.epi.t_low : p.epi.t_high;  // fixed threshold
+  else T_t = h < tau ? p.epi.t_low : p.epi.t_high;                           // ReSET
+  float* ring_w = reinterpret_cast<float*>(st + 1);
+  ring_w[slot] = H;
+  st->count = count;
+  st->sum_all = sum_all;
+  st->step_sum = step_sum;
+  st->step_len = step_len;
+  p.epi.entropy[m] = H;
+  p.epi.temperature[m] = T_t;
+}
+
+
 __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams p, int mt, int ntiles) {
   __shared__ float wm[kMergeThreads / 64], wS[kMergeThreads / 64], wt[kMergeThreads / 64];
   __shared__ float sring[kResetMaxWindow];
@@ -371,11 +436,7 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams 
   }
   __syncthreads();
   if (is_last == 0 || wave != 0) return;
-  // the token's last slice workgroup, wave 0.  One round trip: lane g loads
-  // slice partial g, every lane the sequence state, and the lanes the ring
-  // of the last entropies (the state block holds p.epi.window of them)
-  ResetState* st = reinterpret_cast<ResetState*>(reinterpret_cast<char*>(p.epi.state) + (size_t)m * p.state_bytes);
-  const float* ring = reinterpret_cast<const float*>(st + 1);
+  // the token's last slice workgroup, wave 0: lane g takes slice partial g
   const float* sp = slices + ((int64_t)m * kMergeGroups + (lane < kMergeGroups ? lane : 0)) * 4;
   gm = __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   Sm = __hip_atomic_load(sp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -384,57 +445,50 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams 
     gm = -INFINITY;
     Sm = Tm = 0.0f;
   }
-  const int64_t count0 = st->count;
-  const int32_t st_window = st->window, len0 = st->step_len;
-  const double sum_all0 = st->sum_all, step_sum0 = st->step_sum;
-  const bool new_step = p.epi.step_start[m] != 0;
-  const int wcap = p.epi.window < kResetMaxWindow ? p.epi.window : kResetMaxWindow;
-  float rv[kResetMaxWindow / 64];
+  lmhead_reset_tail(p, m, gm, Sm, Tm, lane, sring);
+}
+
+// LM-head epilogue, part 2 for one token with at most kOneMergeMax row-tile
+// partials (mt apart; contiguous for the one-token kernels): one workgroup
+// merges all of them (every load in flight at once), then its first wave
+// finishes as above.  No slice
+// partials and no tickets: the merge is one round trip after the launch.
+// (With several tokens the partials interleave by token, and one workgroup
+// per token measured slower than the slices.)
+constexpr int kOneThreads = 1024;
+constexpr int kOneLoads = 8;
+constexpr int kOneMergeMax = kOneThreads * kOneLoads;
+
+__global__ __launch_bounds__(kOneThreads) void lmhead_merge_one_kernel(GemvParams p, int mt, int ntiles) {
+  __shared__ float wm[kOneThreads / 64], wS[kOneThreads / 64], wt[kOneThreads / 64];
+  __shared__ float sring[kResetMaxWindow];
+  const int m = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+      p.partials, (short)0, (int)((int64_t)ntiles * mt * 16), kBufferWord3);
+  float4_t q[kOneLoads];
 #pragma unroll
-  for (int k = 0; k < kResetMaxWindow / 64; ++k) {
-    const int i = lane + 64 * k;
-    rv[k] = i < wcap ? ring[i] : 0.0f;
+  for (int j = 0; j < kOneLoads; ++j) {
+    const int idx = j * kOneThreads + (int)threadIdx.x;
+    const int off = idx < ntiles ? (int)((int64_t)idx * mt * 16) : (int)0x7FFFFFF0;
+    q[j] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+  }
+  float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kOneLoads; ++j) {
+    const bool in = j * kOneThreads + (int)threadIdx.x < ntiles;
+    merge_partial(gm, Sm, Tm, in ? q[j][0] : -INFINITY, q[j][1], q[j][2]);
   }
   wave_merge(gm, Sm, Tm);
-  const double Sd = Sm, Td = Tm;
-  const float H = (float)(log(Sd) - Td / Sd);
-  // ---- ReSET update: update with H first, then decide ----
-  // the ring holds the window the state was initialised with; never index
-  // past the smaller of that and the caller's window
-  int w = st_window < p.epi.window ? st_window : p.epi.window;
-  if (w < 1) w = 1;
-  const int slot = (int)(count0 % w);
-#pragma unroll
-  for (int k = 0; k < kResetMaxWindow / 64; ++k) {
-    const int i = lane + 64 * k;
-    if (i < wcap) sring[i] = i == slot ? H : rv[k];
+  if (lane == 0) {
+    wm[wave] = gm;
+    wS[wave] = Sm;
+    wt[wave] = Tm;
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the wave's LDS writes before its reads
-  if (lane != 0) return;
-  const double h = (double)H;
-  const bool reset = count0 == 0 || new_step;
-  const int64_t count = count0 + 1;
-  const double sum_all = sum_all0 + h;
-  const double step_sum = (reset ? 0.0 : step_sum0) + h;
-  const int32_t step_len = (reset ? 0 : len0) + 1;
-  const int64_t nwin = count < w ? count : w;
-  double wsum = 0.0;
-  for (int64_t i = count - nwin; i < count; ++i) wsum += (double)sring[i % w];
-  const double hbar = sum_all / (double)count;
-  const double hstep = step_len <= w ? wsum / (double)nwin : step_sum / (double)step_len;
-  const double tau = hstep > hbar ? hstep : (double)p.epi.tau0;
-  float T_t;
-  if (p.epi.mode == 1) T_t = p.epi.t_base;                                   // BASE
-  else if (p.epi.mode == 2) T_t = h < (double)p.epi.tau0 ? p.epi.t_low : p.epi.t_high;  // fixed threshold
-  else T_t = h < tau ? p.epi.t_low : p.epi.t_high;                           // ReSET
-  float* ring_w = reinterpret_cast<float*>(st + 1);
-  ring_w[slot] = H;
-  st->count = count;
-  st->sum_all = sum_all;
-  st->step_sum = step_sum;
-  st->step_len = step_len;
-  p.epi.entropy[m] = H;
-  p.epi.temperature[m] = T_t;
+  __syncthreads();
+  if (wave != 0) return;
+  const bool has = lane < kOneThreads / 64;
+  lmhead_reset_tail(p, m, has ? wm[lane] : -INFINITY, has ? wS[lane] : 0.0f, has ? wt[lane] : 0.0f, lane, sring);
 }
 
 // ----------------------------------------------------------------------------
@@ -2979,6 +3033,7 @@ struct Variant {
 const Variant kVariants[] = {
     // one token
     DIRECT_NT_V(1, 64, 1, 4, 1), DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), STAGED_V(1, 32, 1, 4, 2),
+    DIRECT_NT_V(1, 32, 4, 4, 1),
     // two tokens
     FMMA_SA_V(2, 1, 4, 3), STAGED_V(2, 64, 1, 4, 2), STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
     // 3..8 tokens
@@ -3210,6 +3265,10 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
     if (stream_lds_bytes(4, K, 4 * kVariants[i].r * kVariants[i].nw) <= kLdsBytes) return i;
   }
   if (M <= 1) {
+    // the LM head with the epilogue: 32-row tiles, as fast as the staged
+    // kernel's 8-row ones, leave few enough partials for a one-workgroup
+    // merge
+    if (epi && N >= 16384) return VARIANT("direct_m1_g32_r4_w4_p1_nt");
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
     return VARIANT("direct_m1_g32_r1_w4_p1_nt");
@@ -3414,8 +3473,11 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   if (epi) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_slice_kernel, dim3(M * kMergeGroups), dim3(kMergeThreads), 0, stream, p, cfg.mt,
-                       (int)cfg.grid);
+    if (M == 1 && cfg.grid <= kOneMergeMax)
+      hipLaunchKernelGGL(lmhead_merge_one_kernel, dim3(1), dim3(kOneThreads), 0, stream, p, cfg.mt, (int)cfg.grid);
+    else
+      hipLaunchKernelGGL(lmhead_slice_kernel, dim3(M * kMergeGroups), dim3(kMergeThreads), 0, stream, p, cfg.mt,
+                         (int)cfg.grid);
   }
   return hipGetLastError();
 }
