@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "50924a1910cfec2a5d9934cc1a299b96351b0749efa788c9bf230d7e46403c88",
-    "bytes_per_step": 1105839211,
+    "sha256": "335fcc5d93165f8ebeeff22ebcd31a149aa48f65358448f448031847a81a5eaa",
+    "bytes_per_step": 1105839464,
 }
 
 

@@ -448,58 +448,6 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_slice_kernel(GemvParams 
   lmhead_reset_tail(p, m, gm, Sm, Tm, lane, sring);
 }
 
-// LM-head epilogue, part 2 when the row-tile partials of all tokens number
-// at most kOneMergeMax: one workgroup merges all of them, and wave m then
-// finishes token m as above.  Thread t loads every partial of the flat
-// [ntiles][mt] array at index t + kOneThreads j (all loads in flight at
-// once); kOneThreads is a multiple of mt, so all of them belong to token
-// t % mt.  Lanes of one token merge by xor shuffles, the waves through LDS.
-// No slice partials and no tickets: the merge is one round trip after the
-// launch.  (One workgroup reading the 19 K partials of the eight-token LM
-// head from 64-row tiles measured slower than the slices: 13.9 against
-// 9.3 us of epilogue.)
-constexpr int kOneThreads = 1024;
-constexpr int kOneLoads = 8;
-constexpr int kOneMergeMax = kOneThreads * kOneLoads;
-constexpr int kOneMaxTokens = 16;
-
-__global__ __launch_bounds__(kOneThreads) void lmhead_merge_one_kernel(GemvParams p, int mt, int ntiles) {
-  constexpr int NWV = kOneThreads / 64;
-  __shared__ float wm[NWV][kOneMaxTokens], wS[NWV][kOneMaxTokens], wt[NWV][kOneMaxTokens];
-  __shared__ float sring[kOneMaxTokens][kResetMaxWindow];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int total = ntiles * mt;
-  const __amdgpu_buffer_rsrc_t pr =
-      __builtin_amdgcn_make_buffer_rsrc(p.partials, (short)0, (int)((int64_t)total * 16), kBufferWord3);
-  float4_t q[kOneLoads];
-#pragma unroll
-  for (int j = 0; j < kOneLoads; ++j) {
-    const int idx = j * kOneThreads + (int)threadIdx.x;
-    q[j] = __builtin_bit_cast(float4_t,
-                              __builtin_amdgcn_raw_buffer_load_b128(pr, idx < total ? idx * 16 : 0x7FFFFFF0, 0, 0));
-  }
-  float gm = -INFINITY, Sm = 0.0f, Tm = 0.0f;
-#pragma unroll
-  for (int j = 0; j < kOneLoads; ++j) {
-    const bool in = j * kOneThreads + (int)threadIdx.x < total;
-    merge_partial(gm, Sm, Tm, in ? q[j][0] : -INFINITY, q[j][1], q[j][2]);
-  }
-  // lanes l and l ^ s (s = mt, 2 mt, .., 32) hold the same token
-  for (int s = mt; s < 64; s <<= 1)
-    merge_partial(gm, Sm, Tm, __shfl_xor(gm, s, 64), __shfl_xor(Sm, s, 64), __shfl_xor(Tm, s, 64));
-  if (lane < mt) {
-    wm[wave][lane] = gm;
-    wS[wave][lane] = Sm;
-    wt[wave][lane] = Tm;
-  }
-  __syncthreads();
-  if (wave >= p.M) return;
-  const int m = wave;
-  const bool has = lane < NWV;
-  lmhead_reset_tail(p, m, has ? wm[lane][m] : -INFINITY, has ? wS[lane][m] : 0.0f, has ? wt[lane][m] : 0.0f, lane,
-                    sring[m]);
-}
-
 // ----------------------------------------------------------------------------
 // VALU kernel
 // ----------------------------------------------------------------------------
@@ -3042,7 +2990,6 @@ struct Variant {
 const Variant kVariants[] = {
     // one token
     DIRECT_NT_V(1, 64, 1, 4, 1), DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), STAGED_V(1, 32, 1, 4, 2),
-    DIRECT_NT_V(1, 32, 4, 4, 1),
     // two tokens
     FMMA_SA_V(2, 1, 4, 3), STAGED_V(2, 64, 1, 4, 2), STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
     // 3..8 tokens
@@ -3274,10 +3221,10 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
     if (stream_lds_bytes(4, K, 4 * kVariants[i].r * kVariants[i].nw) <= kLdsBytes) return i;
   }
   if (M <= 1) {
-    // the LM head with the epilogue: 32-row tiles, as fast as the staged
-    // kernel's 8-row ones, leave few enough partials for a one-workgroup
-    // merge
-    if (epi && N >= 16384) return VARIANT("direct_m1_g32_r4_w4_p1_nt");
+    // LM heads (N >= 65536, with or without the epilogue): the direct
+    // kernel's 16-row tiles measured faster than the staged kernel's 8-row
+    // ones (and leave a quarter of the epilogue's partials)
+    if (N >= 65536) return VARIANT("direct_m1_g32_r2_w4_p1_nt");
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
     if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
     return VARIANT("direct_m1_g32_r1_w4_p1_nt");
@@ -3482,11 +3429,8 @@ hipError_t launch_gemv(const GemvConfig& cfg, int M, int64_t N, int64_t K, const
   if (epi) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (cfg.mt <= kOneMaxTokens && kOneThreads % cfg.mt == 0 && cfg.grid * cfg.mt <= kOneMergeMax)
-      hipLaunchKernelGGL(lmhead_merge_one_kernel, dim3(1), dim3(kOneThreads), 0, stream, p, cfg.mt, (int)cfg.grid);
-    else
-      hipLaunchKernelGGL(lmhead_slice_kernel, dim3(M * kMergeGroups), dim3(kMergeThreads), 0, stream, p, cfg.mt,
-                         (int)cfg.grid);
+    hipLaunchKernelGGL(lmhead_slice_kernel, dim3(M * kMergeGroups), dim3(kMergeThreads), 0, stream, p, cfg.mt,
+                       (int)cfg.grid);
   }
   return hipGetLastError();
 }
