@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "335fcc5d93165f8ebeeff22ebcd31a149aa48f65358448f448031847a81a5eaa",
-    "bytes_per_step": 1105839464,
+    "sha256": "6084a7338fbe3ad132af237dd2574593da75d6f546bd30a668af00858768d9ac",
+    "bytes_per_step": 1105891702,
 }
 
 

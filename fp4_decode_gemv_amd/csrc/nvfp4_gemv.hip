@@ -3187,12 +3187,13 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   // The eight-token streaming kernel, when its staged block scales fit: at
   // 5..8 tokens on every shape, at 2..4 tokens except where another kernel
   // measured as fast or faster (o-like rows, 8192 <= K < 16384, on
-  // N < 16384: the four-window form; LM-head-sized N >= 65536 without the
-  // epilogue: the wave-owned form), and at 1 token on small shapes (N and
-  // K < 8192; elsewhere the VALU kernels are faster)
-  const bool oLike = N < 16384 && K >= 8192 && K < 16384;
+  // N < 16384 whose workgroups leave some of the kernel's 8-row groups
+  // empty: the four-window form; LM-head-sized N >= 65536 without the
+  // epilogue: the wave-owned form), and at 1 token on few rows (N < 8192;
+  // elsewhere the VALU kernels are faster)
+  const bool oLike = N < 16384 && K >= 8192 && K < 16384 && 8 * stream8_groups(N) > tile_rows_for(N, 40);
   if (K % kStream8Chunk == 0 &&
-      (M >= 5 || (M >= 2 && !oLike && !(N >= 65536 && !epi)) || (M == 1 && N < 8192 && K < 8192))) {
+      (M >= 5 || (M >= 2 && !oLike && !(N >= 65536 && !epi)) || (M == 1 && N < 8192))) {
     const int i = stream8_variant(N, K);
     const Variant& v = kVariants[i];
     if (stream_kernel_lds(v, K, tile_rows_for(N, 8 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
