@@ -310,7 +310,8 @@ const char* nvfp4_gemv_variant_name(int index);
  * `variant` for every M its token count covers and every shape it fits
  * (NULL or "" = the launch table's choice).  balance = 1 (the default)
  * deals the rows of small-N shapes out evenly over the CUs in the MFMA tile
- * kernels; balance = 0 keeps whole 16- or 4-row-group tiles.  Both change
+ * kernels; balance = 0 keeps whole tiles (16-, 8- or 4-row groups times the
+ * kernel's group count).  Both change
  * workspace sizes, which must be queried again.  Not for use while another
  * thread launches GEMVs.  Errors: NVFP4_ERR_ARG (unknown name, balance not
  * 0 or 1; nothing changes).
