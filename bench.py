@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "6084a7338fbe3ad132af237dd2574593da75d6f546bd30a668af00858768d9ac",
-    "bytes_per_step": 1105891702,
+    "sha256": "e4da530f628fd822bb19a32b80a8ba87852cbe3bfca5610d7253238e94e20d26",
+    "bytes_per_step": 1105972392,
 }
 
 

@@ -2989,7 +2989,7 @@ struct Variant {
 // NVFP4_GEMV_EXTRA_VARIANTS as a list of the *_V initialisers above.
 const Variant kVariants[] = {
     // one token
-    DIRECT_NT_V(1, 64, 1, 4, 1), DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), STAGED_V(1, 32, 1, 4, 2),
+    DIRECT_NT_V(1, 64, 1, 4, 1), DIRECT_NT_V(1, 32, 1, 4, 1), DIRECT_NT_V(1, 32, 2, 4, 1), STAGED_V(1, 32, 2, 4, 1),
     // two tokens
     FMMA_SA_V(2, 1, 4, 3), STAGED_V(2, 64, 1, 4, 2), STAGED_V(2, 64, 1, 4, 1), STAGED_V(2, 32, 2, 4, 1),
     // 3..8 tokens
@@ -3189,11 +3189,12 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
   // measured as fast or faster (o-like rows, 8192 <= K < 16384, on
   // N < 16384 whose workgroups leave some of the kernel's 8-row groups
   // empty: the four-window form; LM-head-sized N >= 65536 without the
-  // epilogue: the wave-owned form), and at 1 token on few rows (N < 8192;
-  // elsewhere the VALU kernels are faster)
-  const bool oLike = N < 16384 && K >= 8192 && K < 16384 && 8 * stream8_groups(N) > tile_rows_for(N, 40);
+  // epilogue: the wave-owned form), and at 1 token on few rows (N < 8192)
+  // that fill its row groups (elsewhere the VALU kernels are faster)
+  const bool gaps = N < 16384 && 8 * stream8_groups(N) > tile_rows_for(N, 40);
+  const bool oLike = K >= 8192 && K < 16384 && gaps;
   if (K % kStream8Chunk == 0 &&
-      (M >= 5 || (M >= 2 && !oLike && !(N >= 65536 && !epi)) || (M == 1 && N < 8192))) {
+      (M >= 5 || (M >= 2 && !oLike && !(N >= 65536 && !epi)) || (M == 1 && N < 8192 && !gaps))) {
     const int i = stream8_variant(N, K);
     const Variant& v = kVariants[i];
     if (stream_kernel_lds(v, K, tile_rows_for(N, 8 * v.r)) + (epi ? 4 * v.mt * epi_tile_rows(v) : 0) <= kLdsBytes)
@@ -3227,7 +3228,7 @@ int default_variant(int M, int64_t N, int64_t K, bool epi, int64_t ws_cap) {
     // ones (and leave a quarter of the epilogue's partials)
     if (N >= 65536) return VARIANT("direct_m1_g32_r2_w4_p1_nt");
     if (K >= 8192) return VARIANT("direct_m1_g64_r1_w4_p1_nt");
-    if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r1_w4_p2") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
+    if (N >= 16384) return k256 ? VARIANT("staged_m1_g32_r2_w4_p1") : VARIANT("direct_m1_g32_r2_w4_p1_nt");
     return VARIANT("direct_m1_g32_r1_w4_p1_nt");
   }
   // 2 tokens on small shapes (N, K < 8192: the 4096 x 4096 and Qwen3-8B

@@ -230,9 +230,11 @@ LAUNCH_CHOICES = [
     (5, 151936, 5120, False, "stream8_m8_r4_w4_u2"), (2, 51200, 5120, False, "stream8_m8_r5_w4_u2"),
     (4, 5120, 8192, False, "stream_m4_r5_w4_u2"), (2, 5120, 25600, False, "stream8_m8_r3_w8_u2"),
     (4, 4096, 12288, False, "stream8_m8_r2_w8_u2"), (1, 4096, 12288, False, "stream8_m8_r2_w8_u2"),
+    (1, 5120, 8192, False, "direct_m1_g64_r1_w4_p1_nt"), (1, 5120, 25600, False, "direct_m1_g64_r1_w4_p1_nt"),
+    (1, 6144, 4096, False, "stream8_m8_r3_w4_u2"),
     (2, 151936, 5120, False, "wstream_m4_r3_w4_u2_ag"), (4, 151936, 5120, False, "wstream_m4_r3_w4_u2"),
     (1, 4096, 4096, False, "stream8_m8_r2_w4_u2"), (1, 10240, 5120, False, "direct_m1_g32_r1_w4_p1_nt"),
-    (1, 51200, 5120, False, "staged_m1_g32_r1_w4_p2"), (1, 151936, 5120, True, "direct_m1_g32_r2_w4_p1_nt"),
+    (1, 51200, 5120, False, "staged_m1_g32_r2_w4_p1"), (1, 151936, 5120, True, "direct_m1_g32_r2_w4_p1_nt"),
     (1, 151936, 5120, False, "direct_m1_g32_r2_w4_p1_nt"),
     (8, 1024, 4128, False, "lmfma_m8_r1_w4_p1"),
     (16, 10240, 5120, False, "stream8_m16_r5_w4_u2"), (12, 51200, 5120, False, "stream8_m16_r5_w4_u2"),

@@ -95,7 +95,8 @@ def test_small_vocab_sequence(mode, M, N, K):
 
 def test_one_token_tile_sizes_agree():
     """One token on an LM-head-sized vocabulary: the launch table's 16-row
-    tiles (4375 partials) and the staged kernel's 8-row tiles (8750, forced)
+    tiles (4375 partials) and the 8-row tiles of another direct form (8750,
+    forced)
     give the same entropies within rounding, each within 1e-4 nats of the
     fp64 entropy of its own logits, and ReSET decisions that match the
     oracle."""
@@ -108,8 +109,8 @@ def test_one_token_tile_sizes_agree():
     wq = F.nvfp4_pack_weights(f32_dev(w))
     assert F.nvfp4_gemv_variant(M, N, K, True) == "direct_m1_g32_r2_w4_p1_nt"
     _, H1, T1, Href1 = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
-    with F.forced_variant("staged_m1_g32_r1_w4_p2"):
-        assert F.nvfp4_gemv_variant(M, N, K, True) == "staged_m1_g32_r1_w4_p2"
+    with F.forced_variant("direct_m1_g32_r1_w4_p1_nt"):
+        assert F.nvfp4_gemv_variant(M, N, K, True) == "direct_m1_g32_r1_w4_p1_nt"
         _, H2, T2, Href2 = _run_sequence(wq, xs, flags, p, M, scale_exp=u)
     assert np.all(np.abs(H1 - Href1) <= 1e-4) and np.all(np.abs(H2 - Href2) <= 1e-4)
     assert np.all(np.abs(H1 - H2) <= 1e-4)
