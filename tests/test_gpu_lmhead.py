@@ -59,7 +59,8 @@ def _run_sequence(wq, xbits_pos, flags, p: R.ResetParams, M, scale_exp=None, kee
 @pytest.mark.parametrize("mode,M,N,K", [(0, 4, 3000, 512), (1, 4, 3000, 512), (2, 4, 3000, 512), (0, 1, 2500, 1024),
                                          (0, 8, 2000, 8192), (0, 2, 4099, 256), (0, 16, 3000, 512), (2, 13, 2500, 1024),
                                          (0, 32, 3000, 512), (1, 23, 2500, 1024), (0, 64, 3000, 512),
-                                         (2, 41, 2500, 1024), (0, 128, 3000, 512), (1, 77, 2500, 1024)])
+                                         (2, 41, 2500, 1024), (0, 128, 3000, 512), (1, 77, 2500, 1024),
+                                         (0, 12, 70000, 256), (0, 6, 70000, 256)])
 def test_small_vocab_sequence(mode, M, N, K):
     P = 60
     w = W.small_random_weights(41, N, K, scale=0.2)
