@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "e4da530f628fd822bb19a32b80a8ba87852cbe3bfca5610d7253238e94e20d26",
-    "bytes_per_step": 1105972392,
+    "sha256": "78c58b625e877522628fce0d44c997aca12afcb72850accb1c1c4724bad4da93",
+    "bytes_per_step": 1105973039,
 }
 
 

@@ -2029,7 +2029,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream_kernel(GemvParams p) {
     }
   }
   constexpr int kRingLoads = U * (R + 2 * S);
-  wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();  // this wave's staging copies (issued first) have landed ...
+  // This wave's staging copies (issued before the ring loads) have landed ...
+  if (n > 0) wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();
+  else wait_vmcnt<0>();  // a wave with no chunks issued no ring loads to count past
   asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
   if (n > 0) {
     for (int i0 = 0; i0 < n; i0 += U) {
@@ -2197,7 +2199,9 @@ __global__ __launch_bounds__(NW * 64) void gemv_stream8_kernel(GemvParams p) {
     }
   }
   constexpr int kRingLoads = U * (R + 2 * S);
-  wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();  // this wave's staging copies (issued first) have landed ...
+  // This wave's staging copies (issued before the ring loads) have landed ...
+  if (n > 0) wait_vmcnt<(kRingLoads < 63 ? kRingLoads : 63)>();
+  else wait_vmcnt<0>();  // a wave with no chunks issued no ring loads to count past
   asm volatile("s_barrier" ::: "memory");   // ... and every other wave's
   if (n > 0) {
     for (int i0 = 0; i0 < n; i0 += U) {
