@@ -64,8 +64,8 @@ CPU_ROWS = 2048
 # kernel source it was measured on; reported as null once that changes.
 GEMV_TRAFFIC = {
     "source": "fp4_decode_gemv_amd/csrc/nvfp4_gemv.hip",
-    "sha256": "78c58b625e877522628fce0d44c997aca12afcb72850accb1c1c4724bad4da93",
-    "bytes_per_step": 1105973039,
+    "sha256": "058ee307d21b18473b3a3fc5a8b7955c46032ccbc7f31afb1129094d710f65d3",
+    "bytes_per_step": 1105972704,
 }
 
 

@@ -2608,7 +2608,8 @@ __global__ void reset_state_init_kernel(char* state, int M, int window, size_t s
 // [128][128 B], weight block scales [128][16 B], activation codes [MT][128 B]
 // and scales [MT][16 B]) are copied into one of two LDS buffers with
 // direct-to-LDS loads while the waves compute on the other buffer.  Waves
-// split the tile as a WR x WC grid (rows x token groups); each decodes its
+// split each stage's K in two halves and the tile as a WR x WC grid (rows x
+// token groups); each decodes its
 // weight rows and tokens from LDS to exact f16 values (E2M1 x E4M3 has at
 // most 6 significant bits) in registers and runs v_mfma_f32_16x16x32_f16 on
 // 16-row x 16-token tiles, so the products are exact and only the f32
@@ -2732,12 +2733,14 @@ __device__ __forceinline__ void gemm_load_decode(const char* codes, const char* 
 template <int MT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
   // wave grid: KH halves of each stage's K x WR row groups x WC token groups.
-  // At 128 tokens the two 128-element halves of a stage go to different
-  // waves (KH = 2), each over all 128 rows and 64 tokens: every token is
-  // decoded once per stage instead of twice, at the price of adding the two
+  // The two 128-element halves of a stage go to different waves (KH = 2),
+  // each over 64 rows and all MT tokens (MT = 32, 64) or all 128 rows and 64
+  // tokens (MT = 128): a wave decodes (rows + tokens) x 128 elements of a
+  // stage for rows x tokens x 128 products, fewer decodes per product than
+  // 4 row groups over the whole stage, at the price of adding the two
   // halves' accumulators at the end
-  constexpr int KH = MT >= 128 ? 2 : 1;
-  constexpr int WR = MT >= 128 ? 1 : 4;
+  constexpr int KH = 2;
+  constexpr int WR = MT >= 128 ? 1 : 2;
   constexpr int WC = 4 / WR / KH;
   constexpr int RT = kGemmRows / WR / 16;  // 16-row tiles per wave
   constexpr int CT = MT / WC / 16;         // 16-token tiles per wave
@@ -2809,19 +2812,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemvParams p) {
     // free: the loop ended on a barrier); the first half's waves add them
     // and finish
     float4_t* red = reinterpret_cast<float4_t*>(lds);
-    static_assert(WC * RT * CT * 64 * 16 <= 2 * STAGE, "the exchange fits the stage buffers");
+    static_assert(WR * WC * RT * CT * 64 * 16 <= 2 * STAGE, "the exchange fits the stage buffers");
+    const int wg = wr * WC + wc;  // the wave's (row group, token group)
     if (kh == 1) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) red[((wc * RT + rt) * CT + ct) * 64 + lane] = acc[rt][ct];
+        for (int ct = 0; ct < CT; ++ct) red[((wg * RT + rt) * CT + ct) * 64 + lane] = acc[rt][ct];
     }
     __syncthreads();
     if (kh == 1) return;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) acc[rt][ct] += red[((wc * RT + rt) * CT + ct) * 64 + lane];
+      for (int ct = 0; ct < CT; ++ct) acc[rt][ct] += red[((wg * RT + rt) * CT + ct) * 64 + lane];
   }
   // lane (j, g) holds D[4 g + i][j]: weight rows 4 g .. 4 g + 3 of the tile
   // for token j of the token tile
