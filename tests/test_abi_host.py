@@ -240,6 +240,15 @@ LAUNCH_CHOICES = [
     (16, 10240, 5120, False, "stream8_m16_r5_w4_u2"), (12, 51200, 5120, False, "stream8_m16_r5_w4_u2"),
     (16, 151936, 5120, True, "stream8_m16_r4_w4_u2"), (16, 5120, 8192, False, "lmfma_m16_r2_w8_p1"),
     (16, 24576, 4096, False, "lmfma_m16_r2_w4_p1"), (9, 4096, 4096, False, "lmfma_m16_r2_w4_p1"),
+    # 17..128 tokens: the tiled GEMM on gate_up (many row tiles) and, split
+    # along K, on down at 65..128; the register-staged kernel elsewhere (the
+    # split GEMM measured slower on qkv, o and down at 24..64 tokens)
+    (32, 51200, 5120, False, "gemm_m32"), (64, 51200, 5120, False, "gemm_m64"),
+    (128, 51200, 5120, False, "gemm_m128"), (128, 5120, 25600, False, "gemm_m128"),
+    (32, 10240, 5120, False, "lmfma_m32_r2_w4_p1"), (64, 10240, 5120, False, "lmfma_m64_r2_w4_p1"),
+    (128, 10240, 5120, False, "lmfma_m128_r2_w4_p1"), (32, 5120, 8192, False, "lmfma_m32_r2_w8_p1"),
+    (64, 5120, 8192, False, "lmfma_m64_r2_w4_p1"), (32, 5120, 25600, False, "lmfma_m32_r2_w8_p1"),
+    (64, 5120, 25600, False, "lmfma_m64_r2_w8_p1"),
 ]
 
 
